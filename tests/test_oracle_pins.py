@@ -1,0 +1,495 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+Each test checks an oracle function against something other than itself: a value the
+pages print, a closed form, a brute-force enumeration, a textbook special case computed
+by an independent routine, or central finite differences.
+"""
+
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prism_oracle as O
+from workloads import CANDS_16, CANDS_64
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SP = O.ShapeParams()
+
+
+def _grid_field(grid, fn, C=1):
+    """X [1, 1, N, C] with X[n, c] = fn(t, h, w, c) in token raster order."""
+    T, H, W = grid
+    t, h, w = np.meshgrid(np.arange(T), np.arange(H), np.arange(W), indexing="ij")
+    cols = [fn(t, h, w, c).ravel() for c in range(C)]
+    return np.stack(cols, axis=1)[None, None].astype(np.float64)
+
+
+def _shape_of(stats, cands=CANDS_64, zone=(4, 16, 16), dtype=np.float32):
+    sid, margin = O.assign_shapes(stats, cands, zone, SP, dtype)
+    return [cands[i] for i in sid.ravel()], margin.ravel()
+
+
+# ------------------------------------------------------------------ pages' values
+def test_table11_shape_codes_have_equal_volume_per_set():
+    sets, rows = {}, []
+    for line in open(os.path.join(GOLDEN, "table11_shape_codes.txt")):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        f = line.split()
+        if f[0] == "ROW":
+            rows.append([float(x) for x in f[2:]])
+        else:
+            sets[f[0]] = (int(f[1]), [O.parse_shape_code(c) for c in f[2:]])
+    assert O.parse_shape_code("824") == (8, 2, 4)
+    for name, (vol, shapes) in sets.items():
+        assert O.candidate_volume(shapes) == vol, name
+    # mixing two sets must be rejected
+    with pytest.raises(ValueError):
+        O.candidate_volume(sets["C_64"][1] + sets["C_128"][1])
+    for r in rows:
+        assert abs(sum(r) - 100.0) < 1e-9
+    assert O.candidate_volume(CANDS_64) == 64 and O.candidate_volume(CANDS_16) == 16
+
+
+# ------------------------------------------------------------------ zones
+def test_zone_view_tiles_every_token_once():
+    grid, zone = (5, 7, 9), (2, 4, 4)
+    N = 5 * 7 * 9
+    X = (np.arange(N, dtype=np.float64) + 1.0)[None, None, :, None]
+    Xz, mask = O.zone_view(X, grid, zone)
+    vals = Xz[0, 0, ..., 0][mask]
+    assert sorted(vals.tolist()) == list(range(1, N + 1))
+    assert (Xz[0, 0, ..., 0][~mask] == 0).all()
+    assert Xz.shape[2] == 3 * 2 * 3
+
+
+def test_semivariance_of_sinusoids_matches_closed_form():
+    # One 4x16x16 zone.  Channel 0 varies along t with period 3 (3 pairs = 1 period),
+    # channel 1 along h with period 5 (15 pairs = 3 periods), channel 2 along w with
+    # period 15; over whole periods gamma = A^2 sin^2(omega/2) on that axis, 0 elsewhere.
+    grid = zone = (4, 16, 16)
+    A = [2.0, 0.7, 1.3]
+    om = [2 * math.pi / 3, 2 * math.pi / 5, 2 * math.pi / 15]
+    ph = [0.3, 1.1, 2.0]
+
+    def fn(t, h, w, c):
+        x = (t, h, w)[c]
+        return A[c] * np.sin(om[c] * x + ph[c])
+
+    V = _grid_field(grid, fn, C=3)
+    Vz, mask = O.zone_view(V[0, 0], grid, zone)
+    g = O.directional_semivariance(Vz, mask)[0]          # [3 axes, 3 channels]
+    for c in range(3):
+        for d in range(3):
+            want = A[c] ** 2 * math.sin(om[c] / 2) ** 2 if d == c else 0.0
+            assert abs(g[d, c] - want) < 1e-12, (d, c, g[d, c], want)
+
+
+def test_video_share_of_separable_field_matches_closed_form():
+    grid = zone = (4, 16, 16)
+    w1, w2 = 2 * math.pi / 3, 2 * math.pi / 5
+    V = _grid_field(grid, lambda t, h, w, c: np.sin(w1 * t) + 0.5 * np.sin(w2 * h + 0.4), C=2)
+    a2v = np.ones_like(V)
+    st = O.zone_stats(V, a2v, grid, zone)[0, 0, 0]
+    gt, gh = math.sin(w1 / 2) ** 2, 0.25 * math.sin(w2 / 2) ** 2
+    assert abs(st[0] - gt / (gt + gh)) < 1e-9
+    assert abs(st[1] - gh / (gt + gh)) < 1e-9
+    assert abs(st[2]) < 1e-9
+    assert abs(st[0] + st[1] + st[2] - 1.0) < 1e-9
+
+
+def test_zone_stats_vectorised_equals_bruteforce_on_ragged_grid():
+    rng = np.random.default_rng(7)
+    grid, zone = (5, 6, 7), (2, 4, 4)
+    N = 5 * 6 * 7
+    V = rng.standard_normal((1, 2, N, 3))
+    A = rng.standard_normal((1, 2, N, 4))
+    a = O.zone_stats(V, A, grid, zone)
+    b = O.zone_stats_bruteforce(V, A, grid, zone)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+    assert a[..., 7].sum() == 2 * N
+
+
+def test_audio_norm_statistics_closed_form():
+    grid = zone = (4, 16, 16)
+    # a2v rows of norm 3 (all tokens): m_z = 3, increments zero.
+    A = np.zeros((1, 1, 4 * 16 * 16, 2))
+    A[..., 0] = 3.0
+    st = O.zone_stats(np.zeros_like(A), A, grid, zone)[0, 0, 0]
+    assert abs(st[6] - 3.0) < 1e-12 and np.allclose(st[3:6], 0)
+    # a norm ramp a = 2h along h: gamma_h = 1/2 * 2^2 = 2, nothing along t, w.
+    A = _grid_field(grid, lambda t, h, w, c: 2.0 * h + 0 * c, C=1)
+    st = O.zone_stats(np.zeros_like(A), A, grid, zone)[0, 0, 0]
+    assert np.allclose(st[3:6], [0.0, 2.0, 0.0], atol=1e-12)
+    assert abs(st[6] - 15.0) < 1e-12
+
+
+# ------------------------------------------------------------------ shapes
+def _stats_row(rv, ga=(0, 0, 0), m=1.0, n=1024):
+    return np.array([[[list(rv) + list(ga) + [m, n]]]], dtype=np.float64)
+
+
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_shape_special_cases(dtype):
+    # flat zone -> cube; variation along one axis only -> the block is thinnest there.
+    cases = {(0, 0, 0): (4, 4, 4), (1, 0, 0): (1, 8, 8), (0, 1, 0): (4, 2, 8), (0, 0, 1): (4, 8, 2),
+             (0, 0.5, 0.5): (4, 4, 4)}
+    for rv, want in cases.items():
+        got, _ = _shape_of(_stats_row(rv), dtype=dtype)
+        assert got[0] == want, (rv, got, want)
+
+
+def test_shape_from_fields_single_axis():
+    grid = zone = (4, 16, 16)
+    flat = np.ones((1, 1, 1024, 4))
+    fields = {
+        0: (lambda t, h, w, c: np.sin(2.1 * t + c), (1, 8, 8)),
+        1: (lambda t, h, w, c: np.sin(1.3 * h + c), (4, 2, 8)),
+        2: (lambda t, h, w, c: np.sin(1.3 * w + c), (4, 8, 2)),
+    }
+    for _, (fn, want) in fields.items():
+        V = _grid_field(grid, fn, C=4)
+        st = O.zone_stats(V, flat, grid, zone)
+        got, _ = _shape_of(st)
+        assert got[0] == want
+    st = O.zone_stats(np.full((1, 1, 1024, 4), 0.25), flat, grid, zone)
+    assert _shape_of(st)[0][0] == (4, 4, 4)
+
+
+def test_shape_is_equivariant_under_h_w_swap():
+    rng = np.random.default_rng(3)
+    grid = zone = (4, 16, 16)
+    swap = {c: (c[0], c[2], c[1]) for c in CANDS_64}
+    for trial in range(20):
+        V = rng.standard_normal((4, 16, 16, 8)).cumsum(axis=rng.integers(0, 3)) * rng.uniform(0.1, 2)
+        V = V * np.linspace(0.2, 2.0, 16)[None, None, :, None] ** rng.uniform(0, 3)
+        Vt = V.transpose(0, 2, 1, 3)
+        flat = np.ones((1, 1, 1024, 2))
+        s1 = O.zone_stats(V.reshape(1, 1, 1024, 8), flat, grid, zone)
+        s2 = O.zone_stats(Vt.reshape(1, 1, 1024, 8), flat, grid, zone)
+        (c1,), (m1,) = _shape_of(s1, dtype=np.float64)
+        (c2,), (m2,) = _shape_of(s2, dtype=np.float64)
+        if m1 > 1e-6:
+            assert swap[c1] == c2
+
+
+def test_ideal_extents_preserve_volume_and_order():
+    rng = np.random.default_rng(0)
+    g = rng.uniform(1e-3, 1.0, size=(100, 3))
+    lam = O.ideal_log_extents(g, 64, 0.5, np.float64)
+    assert np.allclose(lam.sum(axis=1), 6.0, atol=1e-12)
+    for i in range(100):
+        o = np.argsort(g[i])
+        assert lam[i, o[0]] >= lam[i, o[1]] >= lam[i, o[2]]     # faster variation -> thinner
+    # hand value: g = (1/2, 1/4, 1/4) -> log2 g = (-1, -2, -2), mean -5/3
+    lam = O.ideal_log_extents(np.array([[0.5, 0.25, 0.25]]), 64, 0.5, np.float64)[0]
+    assert np.allclose(lam, [2 - 1 / 3, 2 + 1 / 6, 2 + 1 / 6], atol=1e-12)
+
+
+def test_gate_closed_form():
+    # zones with mean norms 1, 1, 3, 1 of equal size: head mean 1.5, ratios 2/3, 2/3, 2, 2/3
+    st = np.zeros((1, 1, 4, 8))
+    st[0, 0, :, 0:3] = (0.0, 0.0, 1.0)          # video alone would pick 4x8x2
+    st[0, 0, :, 3:6] = (0.0, 5.0, 0.0)          # audio varies along h
+    st[0, 0, :, 6] = (1.0, 1.0, 3.0, 1.0)
+    st[0, 0, :, 7] = 256
+    abar, vhat, g = O.shape_guidance(st, SP, np.float64)
+    assert np.allclose(abar[0, 0], [0, 0, 1, 0])
+    assert np.allclose(vhat[0, 0, 2], [0, 1, 0], atol=1e-9)
+    got, _ = _shape_of(st)
+    assert got == [(4, 8, 2), (4, 8, 2), (4, 2, 8), (4, 8, 2)]
+    # gate halfway: ratio 1.5 -> a-bar = 0.5
+    st[0, 0, :, 6] = (1.0, 1.0, 2.0, 0.0)        # mean 1, ratios 1, 1, 2, 0
+    abar, _, _ = O.shape_guidance(st, SP, np.float64)
+    assert np.allclose(abar[0, 0], [0, 0, 1, 0])
+    st[0, 0, :, 6] = (1.0, 1.0, 1.5, 0.5)        # mean 1, ratio 1.5 -> 0.5
+    abar, _, _ = O.shape_guidance(st, SP, np.float64)
+    assert np.allclose(abar[0, 0], [0, 0, 0.5, 0])
+    # uniform norms -> gate closed everywhere
+    st[0, 0, :, 6] = 2.0
+    abar, _, _ = O.shape_guidance(st, SP, np.float64)
+    assert (abar == 0).all()
+
+
+def test_infeasible_candidate_is_never_chosen():
+    # tiny workload: zone 2x4x8 cannot hold the 4x2x2 candidate (b_T = 4 > 2)
+    assert not O.feasible((4, 2, 2), (2, 4, 8))
+    st = _stats_row((0.0, 1.0, 1.0))            # ideal is long along t
+    sid, _ = O.assign_shapes(st, CANDS_16, (2, 4, 8), SP)
+    assert CANDS_16[int(sid.ravel()[0])] != (4, 2, 2)
+
+
+# ------------------------------------------------------------------ permutation
+def test_slot_map_hand_example():
+    grid, zone = (1, 2, 3), (1, 2, 4)
+    cands = [(1, 2, 2), (1, 1, 4)]
+    tok = O.slot_map(grid, zone, cands, np.array([[[0]]]))
+    assert tok[0, 0].tolist() == [0, 1, 3, 4, 2, 5, -1, -1]
+    tok = O.slot_map(grid, zone, cands, np.array([[[1]]]))
+    assert tok[0, 0].tolist() == [0, 1, 2, -1, 3, 4, 5, -1]
+    assert O.block_valid(tok, 4).tolist() == [[[3, 3]]]
+
+
+def test_slot_map_tiles_each_zone_exactly():
+    rng = np.random.default_rng(1)
+    grid, zone = (8, 30, 52), (4, 16, 16)
+    nZ = O.num_zones(grid, zone)
+    sid = rng.integers(0, 8, size=(1, 3, nZ))
+    tok = O.slot_map(grid, zone, CANDS_64, sid)
+    N = 8 * 30 * 52
+    T, H, W = grid
+    for h in range(3):
+        t = tok[0, h]
+        v = t[t >= 0]
+        assert sorted(v.tolist()) == list(range(N))
+        for z in range(nZ):                      # each zone's slots hold exactly its tokens
+            zt_ = t[z * 1024:(z + 1) * 1024]
+            zt_ = zt_[zt_ >= 0]
+            tt, hh, ww = zt_ // (H * W), (zt_ // W) % H, zt_ % W
+            zid = ((tt // 4) * 2 + hh // 16) * 4 + ww // 16
+            assert (zid == z).all()
+            for blk in range(16):                # each block is a box of its shape
+                bt, bh, bw = CANDS_64[sid[0, h, z]]
+                s = t[z * 1024 + blk * 64: z * 1024 + blk * 64 + 64]
+                s = s[s >= 0]
+                if s.size:
+                    ext = [np.ptp(s // (H * W)) + 1, np.ptp((s // W) % H) + 1, np.ptp(s % W) + 1]
+                    assert ext[0] <= bt and ext[1] <= bh and ext[2] <= bw
+                    assert ext[0] * ext[1] * ext[2] == s.size
+        bv = O.block_valid(tok, 64)[0, h]
+        assert bv.sum() == N and bv.max() == 64
+
+
+def test_permute_unpermute_is_identity():
+    rng = np.random.default_rng(2)
+    grid, zone = (8, 30, 52), (4, 16, 16)
+    N = 8 * 30 * 52
+    x = rng.standard_normal((1, 2, N, 5)).astype(np.float32)
+    sid = rng.integers(0, 8, size=(1, 2, O.num_zones(grid, zone)))
+    tok = O.slot_map(grid, zone, CANDS_64, sid)
+    y = O.permute(x, tok)
+    assert (O.unpermute(y, tok, N) == x).all()
+    assert (y[tok < 0] == 0).all()
+
+
+def test_pooling_bruteforce():
+    rng = np.random.default_rng(4)
+    xp = rng.standard_normal((1, 2, 64, 3))
+    bv = np.array([[[16, 5, 0, 9], [1, 16, 16, 2]]], dtype=np.int32)
+    got = O.pool_blocks(xp, bv, 16)
+    for h in range(2):
+        for I in range(4):
+            n = bv[0, h, I]
+            want = np.zeros(3) if n == 0 else sum(xp[0, h, I * 16 + r] for r in range(n)) / n
+            assert np.allclose(got[0, h, I], want, atol=1e-14)
+
+
+# ------------------------------------------------------------------ selection
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_hybrid_count_hand_rows(dtype):
+    P = np.array([0.5, 0.25, 0.125, 0.125])
+    assert O.hybrid_count(P, 0.9, 1, 4, dtype)[0] == 4       # .5 .75 .875 1.0
+    assert O.hybrid_count(P, 0.75, 1, 4, dtype)[0] == 3      # strictly exceeds: .75 is not > .75
+    assert O.hybrid_count(P, 0.7, 1, 4, dtype)[0] == 2
+    assert O.hybrid_count(P, 1e-6, 1, 4, dtype)[0] == 1
+    assert O.hybrid_count(P, 1e-6, 3, 4, dtype)[0] == 3      # Top-k floor
+    assert O.hybrid_count(P, 0.9, 1, 2, dtype)[0] == 2       # Top-k ceiling
+    assert O.hybrid_count(P, 1.0, 1, 9, dtype) == (4, 4)     # nothing exceeds 1 -> all live
+    P = np.array([0.5, 0.3, 0.15, 0.05])
+    assert O.hybrid_count(P, 0.9, 1, 8, dtype)[0] == 3
+
+
+def test_top_p_is_smallest_subset_by_bruteforce():
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        n = int(rng.integers(2, 9))
+        P = rng.dirichlet(np.full(n, rng.uniform(0.2, 2.0)))
+        p = float(rng.uniform(0.05, 0.99))
+        best = n
+        for r in range(1, n + 1):
+            if any(sum(P[list(c)]) > p + 1e-12 for c in itertools.combinations(range(n), r)):
+                best = r
+                break
+        got = O.hybrid_count(np.sort(P)[::-1], p, 1, n, np.float64)[1]
+        if all(abs(sum(sorted(P, reverse=True)[:r]) - p) > 1e-9 for r in range(1, n + 1)):
+            assert got == best
+
+
+def test_select_row_topk_and_topp_against_independent_sorts():
+    rng = np.random.default_rng(6)
+    d = 16
+    for trial in range(50):
+        nb = int(rng.integers(3, 40))
+        K = rng.standard_normal((nb, d)) * rng.uniform(0.1, 3)
+        q = rng.standard_normal(d)
+        live = rng.uniform(size=nb) > 0.2
+        live[0] = True
+        J = np.nonzero(live)[0]
+        s = K[J] @ q / 4.0
+        P = np.exp(s - s.max())
+        P /= P.sum()
+        k = int(rng.integers(1, J.size + 1))
+        sel, _ = O.select_row(q, K, live, 0.25, 1.0, k, k, np.float64)
+        want = sorted(sorted(range(J.size), key=lambda i: (-P[i], J[i]))[:k])
+        assert sel.tolist() == [int(J[i]) for i in want]
+        p = float(rng.uniform(0.1, 0.95))
+        sel, near = O.select_row(q, K, live, 0.25, p, 1, J.size, np.float64)
+        order = sorted(range(J.size), key=lambda i: (-P[i], J[i]))
+        acc, n = 0.0, J.size
+        for r, i in enumerate(order):
+            acc += P[i]
+            if acc > p:
+                n = r + 1
+                break
+        if not near:
+            assert sel.tolist() == sorted(int(J[i]) for i in order[:n])
+
+
+def test_select_flags_exact_tie_at_cut():
+    K = np.array([[1.0, 0.0], [1.0, 0.0], [0.0, 0.0]])
+    sel, near = O.select_row(np.array([2.0, 0.0]), K, np.ones(3, bool), 1.0, 0.3, 1, 3, np.float64)
+    assert sel.tolist() == [0] and near          # blocks 0 and 1 tie; lower index wins
+
+
+def test_reverse_index_bruteforce():
+    rng = np.random.default_rng(8)
+    nb, kmax = 12, 5
+    sel = {}
+    for I in range(nb):
+        c = int(rng.integers(0, kmax + 1))
+        sel[(0, 0, I)] = np.sort(rng.choice(nb, size=c, replace=False)).astype(np.int32)
+    idx, cnt = O.selection_arrays(sel, 1, 1, nb, kmax)
+    rp, ri = O.reverse_index(idx, cnt)
+    for J in range(nb):
+        want = [I for I in range(nb) if J in sel[(0, 0, I)].tolist()]
+        assert ri[0, 0, rp[0, 0, J]:rp[0, 0, J + 1]].tolist() == want
+
+
+# ------------------------------------------------------------------ attention
+def _tiny_problem(seed=0, C=8):
+    rng = np.random.default_rng(seed)
+    grid, zone, cands = (4, 8, 8), (2, 4, 8), list(CANDS_16)
+    N = 256
+    q, k, v = (rng.standard_normal((1, 2, N, C)) for _ in range(3))
+    sid = rng.integers(0, 3, size=(1, 2, O.num_zones(grid, zone)))
+    tok = O.slot_map(grid, zone, cands, sid)
+    return q, k, v, tok, N
+
+
+def _all_selected(bv):
+    B, Hh, nb = bv.shape
+    return {(b, h, I): (np.nonzero(bv[b, h] > 0)[0].astype(np.int32) if bv[b, h, I] else np.zeros(0, np.int32))
+            for b in range(B) for h in range(Hh) for I in range(nb)}
+
+
+def test_all_blocks_selected_equals_textbook_dense_attention():
+    q, k, v, tok, N = _tiny_problem()
+    bv = O.block_valid(tok, 16)
+    # p = 1 with k_min = k_max = every live block selects all live key blocks
+    qp, kp, vp = O.permute(q, tok), O.permute(k, tok), O.permute(v, tok)
+    qb, kb = O.pool_blocks(qp, bv, 16), O.pool_blocks(kp, bv, 16)
+    nl = int((bv[0, 0] > 0).sum())
+    sel, _ = O.select_blocks(qb, kb, bv, 0.3, 1.0, nl, nl, dtype=np.float64)
+    op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, 0.3, 16)
+    o = O.unpermute(op, tok, N)
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.3).numpy()
+    assert np.allclose(o, want, atol=1e-12)
+    lse_want = torch.logsumexp(0.3 * tq @ tk.transpose(-1, -2), dim=-1).numpy()
+    assert np.allclose(O.unpermute(lse[..., None], tok, N)[..., 0], lse_want, atol=1e-12)
+    od, ld = O.dense_attn_fwd(q, k, v, 0.3)
+    assert np.allclose(od, want, atol=1e-12) and np.allclose(ld, lse_want, atol=1e-12)
+
+
+def test_single_selected_block_is_attention_inside_that_block():
+    q, k, v, tok, N = _tiny_problem(1)
+    bv = O.block_valid(tok, 16)
+    qp, kp, vp = O.permute(q, tok), O.permute(k, tok), O.permute(v, tok)
+    sel = {(0, 0, 3): np.array([5], np.int32)}
+    op, _ = O.sparse_attn_fwd(qp, kp, vp, bv, sel, 0.5, 16, blocks=[(0, 0, 3)])
+    n, m = bv[0, 0, 3], bv[0, 0, 5]
+    Q = torch.from_numpy(qp[0, 0, 48:48 + n])
+    K = torch.from_numpy(kp[0, 0, 80:80 + m])
+    V = torch.from_numpy(vp[0, 0, 80:80 + m])
+    want = torch.softmax(0.5 * Q @ K.T, dim=1) @ V
+    assert np.allclose(op[0, 0, 48:48 + n], want.numpy(), atol=1e-12)
+    assert (op[0, 0, 48 + n:64] == 0).all()
+
+
+def test_backward_matches_central_finite_differences():
+    q, k, v, tok, N = _tiny_problem(2, C=4)
+    bv = O.block_valid(tok, 16)
+    rng = np.random.default_rng(9)
+    qp, kp, vp = O.permute(q, tok), O.permute(k, tok), O.permute(v, tok)
+    qb, kb = O.pool_blocks(qp, bv, 16), O.pool_blocks(kp, bv, 16)
+    sel, _ = O.select_blocks(qb, kb, bv, 0.5, 0.6, 2, 5, dtype=np.float64)   # frozen mask
+    dop = O.permute(rng.standard_normal(q.shape), tok)
+    op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, 0.5, 16)
+    dq, dk, dv = O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, 0.5, 16)
+
+    def loss(a, b_, c):
+        return float((O.sparse_attn_fwd(a, b_, c, bv, sel, 0.5, 16)[0] * dop).sum())
+
+    valid = np.nonzero(tok[0, 0] >= 0)[0]
+    h = 1e-6
+    for which, grad in ((0, dq), (1, dk), (2, dv)):
+        for _ in range(12):
+            s = int(rng.choice(valid))
+            c = int(rng.integers(0, 4))
+            args = [qp.copy(), kp.copy(), vp.copy()]
+            args[which][0, 0, s, c] += h
+            lp = loss(*args)
+            args[which][0, 0, s, c] -= 2 * h
+            lm = loss(*args)
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - grad[0, 0, s, c]) <= 1e-6 * max(1.0, abs(fd)), (which, s, c, fd, grad[0, 0, s, c])
+
+
+def test_backward_all_selected_matches_autograd_dense():
+    q, k, v, tok, N = _tiny_problem(3)
+    bv = O.block_valid(tok, 16)
+    rng = np.random.default_rng(10)
+    do = rng.standard_normal(q.shape)
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    out = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, scale=0.4)
+    (out * torch.from_numpy(do)).sum().backward()
+    # dense oracle
+    o, lse = O.dense_attn_fwd(q, k, v, 0.4)
+    dq, dk, dv = O.dense_attn_bwd(q, k, v, o, do, lse, 0.4)
+    for a, t in ((dq, tq), (dk, tk), (dv, tv)):
+        assert np.allclose(a, t.grad.numpy(), atol=1e-10)
+    # sparse oracle with every block selected
+    qp, kp, vp = O.permute(q, tok), O.permute(k, tok), O.permute(v, tok)
+    sel = _all_selected(bv)
+    op, lsp = O.sparse_attn_fwd(qp, kp, vp, bv, sel, 0.4, 16)
+    g = O.sparse_attn_bwd(qp, kp, vp, op, O.permute(do, tok), lsp, bv, sel, 0.4, 16)
+    for a, t in zip(g, (tq, tk, tv)):
+        assert np.allclose(O.unpermute(a, tok, N), t.grad.numpy(), atol=1e-10)
+    # restricting the gradient to some blocks gives those blocks' rows unchanged
+    gq = O.sparse_attn_bwd(qp, kp, vp, op, O.permute(do, tok), lsp, bv, sel, 0.4, 16,
+                           q_blocks=[(0, 1, 2)], k_blocks=[(0, 0, 7)])
+    assert np.allclose(gq[0][0, 1, 32:48], g[0][0, 1, 32:48])
+    assert np.allclose(gq[1][0, 0, 112:128], g[1][0, 0, 112:128])
+    assert np.allclose(gq[2][0, 0, 112:128], g[2][0, 0, 112:128])
+
+
+def test_full_chain_tiny_workload_invariants():
+    from workloads import workload
+    from workloads.synth import make_inputs
+    w = workload(0)
+    x = make_inputs(w, seed=0)
+    f = O.prism_forward(*(x[n].numpy() for n in ("q", "k", "v", "a2v")), w.grid, w.zone, list(w.cands),
+                        w.top_p, w.k_min, w.k_max)
+    assert (f["shape_id"] != 3).all()                       # 4x2x2 never fits a 2x4x8 zone
+    nb = f["bvalid"].shape[-1]
+    for (b, h, I), s in f["sel"].items():
+        assert w.k_min <= s.size <= w.k_max
+        assert (np.diff(s) > 0).all()
+    assert np.isfinite(f["o"]).all()
+    bw = O.prism_backward(f, x["do"].numpy())
+    assert np.isfinite(bw["dq"]).all() and nb == 16
