@@ -1,0 +1,285 @@
+// C-ABI entry points of libprism (declared in include/prism.h).  Every call validates its
+// arguments on the host, fills the launch descriptors and enqueues the kernels on the
+// caller's stream.  No device memory is allocated here; errors are reported through
+// prism_status plus a thread-local message.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "prism_internal.h"
+
+using namespace prism;
+
+namespace {
+
+thread_local std::string g_err;
+
+prism_status fail(prism_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+prism_status ok() {
+  g_err.clear();
+  return PRISM_OK;
+}
+
+prism_status launched(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(PRISM_ERR_LAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool valid_dtype(prism_dtype dt) { return dt == PRISM_F32 || dt == PRISM_BF16; }
+size_t esize(prism_dtype dt) { return dt == PRISM_BF16 ? 2 : 4; }
+
+prism_status check_grid(const prism_grid* g, Geo* out) {
+  if (!g) return fail(PRISM_ERR_ARG, "grid is null");
+  if (g->T < 1 || g->H < 1 || g->W < 1) return fail(PRISM_ERR_ARG, "grid extents must be >= 1");
+  if (g->zt < 1 || g->zh < 1 || g->zw < 1) return fail(PRISM_ERR_ARG, "zone extents must be >= 1");
+  const int64_t vz = int64_t(g->zt) * g->zh * g->zw;
+  if (vz > kMaxZoneVol) return fail(PRISM_ERR_SHAPE, "zone volume %lld exceeds %d", (long long)vz, kMaxZoneVol);
+  const int64_t n = int64_t(g->T) * g->H * g->W;
+  if (n > (int64_t(1) << 30)) return fail(PRISM_ERR_SHAPE, "grid too large");
+  Geo o;
+  o.T = g->T; o.H = g->H; o.W = g->W;
+  o.zt = g->zt; o.zh = g->zh; o.zw = g->zw;
+  o.nzt = (g->T + g->zt - 1) / g->zt;
+  o.nzh = (g->H + g->zh - 1) / g->zh;
+  o.nzw = (g->W + g->zw - 1) / g->zw;
+  o.nZ = o.nzt * o.nzh * o.nzw;
+  o.Vz = int(vz);
+  o.N = int(n);
+  if (out) *out = o;
+  return PRISM_OK;
+}
+
+prism_status check_shapes(const prism_shapes* s, const Geo& g, ShapeTab* out) {
+  if (!s) return fail(PRISM_ERR_ARG, "shapes is null");
+  if (s->n < 1 || s->n > PRISM_MAX_SHAPES) return fail(PRISM_ERR_ARG, "shapes->n must be in [1, %d]", PRISM_MAX_SHAPES);
+  if (s->vol < 1) return fail(PRISM_ERR_ARG, "shapes->vol must be >= 1");
+  if (g.Vz % s->vol != 0) return fail(PRISM_ERR_SHAPE, "zone volume %d is not a multiple of block volume %d", g.Vz, s->vol);
+  ShapeTab t = {};
+  t.n = s->n;
+  t.vol = s->vol;
+  int nfeas = 0;
+  for (int c = 0; c < s->n; ++c) {
+    if (s->bt[c] < 1 || s->bh[c] < 1 || s->bw[c] < 1) return fail(PRISM_ERR_ARG, "shape %d has an extent < 1", c);
+    if (int64_t(s->bt[c]) * s->bh[c] * s->bw[c] != s->vol)
+      return fail(PRISM_ERR_SHAPE, "shape %d (%dx%dx%d) does not hold vol=%d tokens", c, s->bt[c], s->bh[c], s->bw[c], s->vol);
+    t.bt[c] = s->bt[c];
+    t.bh[c] = s->bh[c];
+    t.bw[c] = s->bw[c];
+    t.lg[c][0] = float(std::log2(double(s->bt[c])));
+    t.lg[c][1] = float(std::log2(double(s->bh[c])));
+    t.lg[c][2] = float(std::log2(double(s->bw[c])));
+    t.feasible[c] = (g.zt % s->bt[c] == 0) && (g.zh % s->bh[c] == 0) && (g.zw % s->bw[c] == 0);
+    nfeas += t.feasible[c];
+  }
+  if (nfeas == 0) return fail(PRISM_ERR_SHAPE, "no candidate shape tiles the %dx%dx%d zone", g.zt, g.zh, g.zw);
+  if (out) *out = t;
+  return PRISM_OK;
+}
+
+bool supported_attn_d(int d) { return d == 64 || d == 128; }
+bool supported_stats_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
+
+}  // namespace
+
+extern "C" {
+
+const char* prism_last_error(void) { return g_err.c_str(); }
+
+int64_t prism_num_zones(const prism_grid* grid) {
+  Geo g;
+  if (check_grid(grid, &g) != PRISM_OK) return -1;
+  return g.nZ;
+}
+
+int64_t prism_num_blocks(const prism_grid* grid, const prism_shapes* shapes) {
+  Geo g;
+  if (check_grid(grid, &g) != PRISM_OK) return -1;
+  if (check_shapes(shapes, g, nullptr) != PRISM_OK) return -1;
+  return int64_t(g.nZ) * (g.Vz / shapes->vol);
+}
+
+prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
+                              const prism_grid* grid, float* stats, hipStream_t stream) {
+  if (!v || !a2v || !stats) return fail(PRISM_ERR_ARG, "prism_zone_stats: null pointer");
+  if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "prism_zone_stats: B and Hh must be >= 1");
+  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "prism_zone_stats: unknown dtype %d", int(dtype));
+  if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "prism_zone_stats: d=%d not in {32,64,128,256}", d);
+  Geo g;
+  prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  return launched(launch_zone_stats(v, a2v, dtype, B * Hh, d, g, stats, stream), "prism_zone_stats");
+}
+
+prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_grid* grid,
+                                 const prism_shapes* shapes, const prism_shape_params* params,
+                                 int32_t* shape_id, float* margin, hipStream_t stream) {
+  if (!stats || !shape_id || !params) return fail(PRISM_ERR_ARG, "prism_assign_shapes: null pointer");
+  if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "prism_assign_shapes: B and Hh must be >= 1");
+  Geo g;
+  prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  ShapeTab t;
+  st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  const prism_shape_params p = *params;
+  if (!std::isfinite(p.alpha) || !std::isfinite(p.tau_lo) || !std::isfinite(p.tau_hi) || !(p.tau_hi > p.tau_lo))
+    return fail(PRISM_ERR_ARG, "prism_assign_shapes: need finite alpha and tau_hi > tau_lo");
+  if (!(p.g_min > 0.f) || !(p.eps >= 0.f)) return fail(PRISM_ERR_ARG, "prism_assign_shapes: need g_min > 0, eps >= 0");
+  return launched(launch_assign_shapes(stats, B * Hh, g, t, p, shape_id, margin, stream), "prism_assign_shapes");
+}
+
+prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int Hh, int d,
+                           const prism_grid* grid, const prism_shapes* shapes, const int32_t* shape_id,
+                           int inverse, int32_t* block_valid, hipStream_t stream) {
+  if (!x || !y || !shape_id) return fail(PRISM_ERR_ARG, "prism_permute: null pointer");
+  if (B < 1 || Hh < 1 || d < 1) return fail(PRISM_ERR_ARG, "prism_permute: B, Hh, d must be >= 1");
+  if (inverse != 0 && inverse != 1) return fail(PRISM_ERR_ARG, "prism_permute: inverse must be 0 or 1");
+  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "prism_permute: unknown dtype %d", int(dtype));
+  if ((size_t(d) * esize(dtype)) % 16 != 0) return fail(PRISM_ERR_DTYPE, "prism_permute: d*sizeof(dtype) must be a multiple of 16");
+  if (x == y) return fail(PRISM_ERR_ARG, "prism_permute: x and y must not alias");
+  Geo g;
+  prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  ShapeTab t;
+  st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  return launched(launch_permute(x, y, dtype, B * Hh, d, g, t, shape_id, inverse, block_valid, stream), "prism_permute");
+}
+
+size_t prism_select_workspace_size(int B, int Hh, int nb, int d) {
+  if (B < 1 || Hh < 1 || nb < 1 || d < 1) return 0;
+  return select_ws_bytes(B * Hh, nb, d);
+}
+
+prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dtype, const int32_t* block_valid,
+                                 int B, int Hh, int nb, int vol, int d, float scale,
+                                 const prism_select_params* params, int32_t* sel_idx, int32_t* sel_cnt,
+                                 int32_t* rev_ptr, int32_t* rev_idx, float* sel_margin, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
+  if (!qp || !kp || !block_valid || !params || !sel_idx || !sel_cnt || !rev_ptr || !rev_idx || !workspace)
+    return fail(PRISM_ERR_ARG, "prism_select_blocks: null pointer");
+  if (B < 1 || Hh < 1 || nb < 1 || vol < 1) return fail(PRISM_ERR_ARG, "prism_select_blocks: sizes must be >= 1");
+  if (nb > kMaxSelectNb) return fail(PRISM_ERR_SHAPE, "prism_select_blocks: nb=%d exceeds %d", nb, kMaxSelectNb);
+  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "prism_select_blocks: unknown dtype %d", int(dtype));
+  if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "prism_select_blocks: d=%d not in {32,64,128,256}", d);
+  const prism_select_params p = *params;
+  if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(PRISM_ERR_ARG, "prism_select_blocks: top_p must be in (0, 1]");
+  if (p.k_min < 1 || p.k_max < p.k_min) return fail(PRISM_ERR_ARG, "prism_select_blocks: need 1 <= k_min <= k_max");
+  if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "prism_select_blocks: scale must be finite");
+  if (ws_bytes < select_ws_bytes(B * Hh, nb, d))
+    return fail(PRISM_ERR_ARG, "prism_select_blocks: workspace of %zu bytes < required %zu", ws_bytes,
+                select_ws_bytes(B * Hh, nb, d));
+  return launched(launch_select(qp, kp, dtype, block_valid, B * Hh, nb, vol, d, scale, p, sel_idx, sel_cnt,
+                                rev_ptr, rev_idx, sel_margin, workspace, stream),
+                  "prism_select_blocks");
+}
+
+static prism_status check_attn_common(const char* who, prism_dtype dtype, int B, int Hh, int nb, int vol, int d,
+                                      int k_max, float scale) {
+  if (B < 1 || Hh < 1 || nb < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, nb must be >= 1", who);
+  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "%s: unknown dtype %d", who, int(dtype));
+  if (!supported_attn_d(d)) return fail(PRISM_ERR_DTYPE, "%s: d=%d not in {64,128}", who, d);
+  if (vol < 1 || vol > kTileRows) return fail(PRISM_ERR_SHAPE, "%s: vol=%d must be in [1, %d]", who, vol, kTileRows);
+  if ((size_t(vol) * d * esize(dtype)) % 16 != 0) return fail(PRISM_ERR_SHAPE, "%s: vol*d*sizeof(dtype) must be a multiple of 16", who);
+  if (k_max < 1) return fail(PRISM_ERR_ARG, "%s: k_max must be >= 1", who);
+  if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "%s: scale must be finite", who);
+  if (int64_t(B) * Hh * nb * vol > (int64_t(1) << 31)) return fail(PRISM_ERR_SHAPE, "%s: too many rows", who);
+  return PRISM_OK;
+}
+
+prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
+                                   const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   int k_max, int B, int Hh, int nb, int vol, int d, float scale, void* op,
+                                   float* lse, hipStream_t stream) {
+  if (!qp || !kp || !vp || !block_valid || !sel_idx || !sel_cnt || !op || !lse)
+    return fail(PRISM_ERR_ARG, "prism_sparse_attn_fwd: null pointer");
+  prism_status st = check_attn_common("prism_sparse_attn_fwd", dtype, B, Hh, nb, vol, d, k_max, scale);
+  if (st != PRISM_OK) return st;
+  AttnArgs a = {};
+  a.q = qp; a.k = kp; a.v = vp; a.out = op; a.lse_out = lse;
+  a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt;
+  a.BH = B * Hh; a.nb = nb; a.vol = vol; a.k_max = k_max; a.nrows = nb * vol; a.d = d;
+  a.dense = 0; a.scale = scale;
+  return launched(launch_attn_fwd(a, dtype, stream), "prism_sparse_attn_fwd");
+}
+
+size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol) {
+  if (B < 1 || Hh < 1 || nb < 1 || vol < 1) return 0;
+  return align256(size_t(B) * Hh * nb * vol * 4);
+}
+
+prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* vp, const void* op, const void* dop,
+                                   const float* lse, prism_dtype dtype, const int32_t* block_valid,
+                                   const int32_t* sel_idx, const int32_t* sel_cnt, int k_max,
+                                   const int32_t* rev_ptr, const int32_t* rev_idx, int B, int Hh, int nb, int vol,
+                                   int d, float scale, void* dqp, void* dkp, void* dvp, void* workspace,
+                                   size_t ws_bytes, hipEvent_t* marks, hipStream_t stream) {
+  if (!qp || !kp || !vp || !op || !dop || !lse || !block_valid || !sel_idx || !sel_cnt || !rev_ptr || !rev_idx ||
+      !dqp || !dkp || !dvp || !workspace)
+    return fail(PRISM_ERR_ARG, "prism_sparse_attn_bwd: null pointer");
+  prism_status st = check_attn_common("prism_sparse_attn_bwd", dtype, B, Hh, nb, vol, d, k_max, scale);
+  if (st != PRISM_OK) return st;
+  if (ws_bytes < prism_bwd_workspace_size(B, Hh, nb, vol))
+    return fail(PRISM_ERR_ARG, "prism_sparse_attn_bwd: workspace of %zu bytes < required %zu", ws_bytes,
+                prism_bwd_workspace_size(B, Hh, nb, vol));
+  AttnArgs a = {};
+  a.q = qp; a.k = kp; a.v = vp; a.o = op; a.dout = dop; a.lse_in = lse;
+  a.Dbuf = static_cast<float*>(workspace);
+  a.dq = dqp; a.dk = dkp; a.dv = dvp;
+  a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.rev_ptr = rev_ptr; a.rev_idx = rev_idx;
+  a.BH = B * Hh; a.nb = nb; a.vol = vol; a.k_max = k_max; a.nrows = nb * vol; a.d = d;
+  a.dense = 0; a.scale = scale;
+  return launched(launch_attn_bwd(a, dtype, marks, stream), "prism_sparse_attn_bwd");
+}
+
+prism_status prism_dense_attn_fwd(const void* q, const void* k, const void* v, prism_dtype dtype, int B, int Hh,
+                                  int N, int d, float scale, void* o, float* lse, hipStream_t stream) {
+  if (!q || !k || !v || !o || !lse) return fail(PRISM_ERR_ARG, "prism_dense_attn_fwd: null pointer");
+  if (N < 1) return fail(PRISM_ERR_ARG, "prism_dense_attn_fwd: N must be >= 1");
+  const int nb = (N + kTileRows - 1) / kTileRows;
+  prism_status st = check_attn_common("prism_dense_attn_fwd", dtype, B, Hh, nb, kTileRows, d, 1, scale);
+  if (st != PRISM_OK) return st;
+  AttnArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.out = o; a.lse_out = lse;
+  a.BH = B * Hh; a.nb = nb; a.vol = kTileRows; a.k_max = nb; a.nrows = N; a.d = d;
+  a.dense = 1; a.scale = scale;
+  return launched(launch_attn_fwd(a, dtype, stream), "prism_dense_attn_fwd");
+}
+
+size_t prism_dense_bwd_workspace_size(int B, int Hh, int N) {
+  if (B < 1 || Hh < 1 || N < 1) return 0;
+  return align256(size_t(B) * Hh * N * 4);
+}
+
+prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                                  const float* lse, prism_dtype dtype, int B, int Hh, int N, int d, float scale,
+                                  void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes, hipEvent_t* marks,
+                                  hipStream_t stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv || !workspace)
+    return fail(PRISM_ERR_ARG, "prism_dense_attn_bwd: null pointer");
+  if (N < 1) return fail(PRISM_ERR_ARG, "prism_dense_attn_bwd: N must be >= 1");
+  const int nb = (N + kTileRows - 1) / kTileRows;
+  prism_status st = check_attn_common("prism_dense_attn_bwd", dtype, B, Hh, nb, kTileRows, d, 1, scale);
+  if (st != PRISM_OK) return st;
+  if (ws_bytes < prism_dense_bwd_workspace_size(B, Hh, N))
+    return fail(PRISM_ERR_ARG, "prism_dense_attn_bwd: workspace too small");
+  AttnArgs a = {};
+  a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse_in = lse;
+  a.Dbuf = static_cast<float*>(workspace);
+  a.dq = dq; a.dk = dk; a.dv = dv;
+  a.BH = B * Hh; a.nb = nb; a.vol = kTileRows; a.k_max = nb; a.nrows = N; a.d = d;
+  a.dense = 1; a.scale = scale;
+  return launched(launch_attn_bwd(a, dtype, marks, stream), "prism_dense_attn_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,206 @@
+// Internal declarations of libprism: device helpers shared by the kernels and the host
+// launchers called by the C-ABI layer (prism_api.hip).  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/prism.h"
+
+namespace prism {
+
+constexpr int kMaxZoneVol = 4096;   // zone-local LDS map of the A2V norm
+constexpr int kMaxSelectNb = 16000; // one score row of the selection kernel lives in LDS (< 64 KB)
+constexpr int kTileRows = 64;       // query/key rows per attention tile
+
+// ----------------------------------------------------------------------------------
+// Element access.  bf16 is stored as raw 16-bit words and widened by a shift; narrowing
+// uses round-to-nearest-even.
+// ----------------------------------------------------------------------------------
+struct bf16_t {
+  uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) { return __uint_as_float(uint32_t(x.bits) << 16); }
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float f);
+template <>
+__device__ __forceinline__ float from_f32<float>(float f) {
+  return f;
+}
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float f) {
+  uint32_t u = __float_as_uint(f);
+  bf16_t r;
+  if ((u & 0x7fffffffu) > 0x7f800000u) {
+    r.bits = 0x7fc0;
+  } else {
+    u += 0x7fffu + ((u >> 16) & 1u);
+    r.bits = uint16_t(u >> 16);
+  }
+  return r;
+}
+
+// Load 8 consecutive elements starting at p (16-byte aligned for bf16, 32 for f32).
+__device__ __forceinline__ void load8(const bf16_t* p, float (&x)[8]) {
+  const uint4 u = *reinterpret_cast<const uint4*>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(w[i] << 16);
+    x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// ----------------------------------------------------------------------------------
+// Reductions (64-lane wavefronts).
+// ----------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Sum over a workgroup of NT threads; `red` holds at least NT/64 floats.  Every thread
+// gets the result.  Fixed order, so the result is deterministic.
+template <int NT>
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  constexpr int NW = NT / 64;
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += red[i];
+  return s;
+}
+template <int NT>
+__device__ __forceinline__ float block_max(float v, float* red) {
+  constexpr int NW = NT / 64;
+  v = wave_max(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  float s = red[0];
+#pragma unroll
+  for (int i = 1; i < NW; ++i) s = fmaxf(s, red[i]);
+  return s;
+}
+template <int NT>
+__device__ __forceinline__ int block_sum_i(int v, int* red) {
+  constexpr int NW = NT / 64;
+  v = wave_sum_i(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) s += red[i];
+  return s;
+}
+// Exclusive prefix sum of one int per thread over the workgroup (thread order); the
+// total is returned through *total.  `red` holds at least NT/64 + 1 ints.
+template <int NT>
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int n = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += n;
+  }
+  __syncthreads();
+  if (lane == 63) red[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NW; ++i) {
+    if (i < w) off += red[i];
+    tot += red[i];
+  }
+  *total = tot;
+  return off + incl - v;
+}
+
+// ----------------------------------------------------------------------------------
+// Host-side geometry shared by the launchers.
+// ----------------------------------------------------------------------------------
+struct Geo {
+  int T, H, W, zt, zh, zw, nzt, nzh, nzw;
+  int nZ, Vz, N;
+};
+
+struct ShapeTab {
+  int n, vol;
+  int bt[PRISM_MAX_SHAPES], bh[PRISM_MAX_SHAPES], bw[PRISM_MAX_SHAPES];
+  float lg[PRISM_MAX_SHAPES][3];  // log2 of each extent
+  int feasible[PRISM_MAX_SHAPES];
+};
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse_in;
+  float* Dbuf;
+  void* out;
+  float* lse_out;
+  void* dq;
+  void* dk;
+  void* dv;
+  const int32_t* bvalid;
+  const int32_t* sel_idx;
+  const int32_t* sel_cnt;
+  const int32_t* rev_ptr;
+  const int32_t* rev_idx;
+  int BH, nb, vol, k_max, nrows, d;
+  int dense;  // 1: unpermuted [N][d] tensors, 64-row tiles, every block selected
+  float scale;
+};
+
+// Launchers (each returns the first HIP error of its launches).
+hipError_t launch_zone_stats(const void* v, const void* a2v, prism_dtype dt, int BH, int d,
+                             const Geo& g, float* stats, hipStream_t s);
+hipError_t launch_assign_shapes(const float* stats, int BH, const Geo& g, const ShapeTab& tab,
+                                const prism_shape_params& p, int32_t* shape_id, float* margin,
+                                hipStream_t s);
+hipError_t launch_permute(const void* x, void* y, prism_dtype dt, int BH, int d, const Geo& g,
+                          const ShapeTab& tab, const int32_t* shape_id, int inverse,
+                          int32_t* block_valid, hipStream_t s);
+hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const int32_t* bvalid,
+                         int BH, int nb, int vol, int d, float scale, const prism_select_params& p,
+                         int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
+                         float* sel_margin, void* ws, hipStream_t s);
+size_t select_ws_bytes(int BH, int nb, int d);
+hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, hipEvent_t* marks, hipStream_t s);
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace prism

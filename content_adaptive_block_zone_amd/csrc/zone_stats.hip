@@ -1,0 +1,174 @@
+// Zone statistics (Prism abstract: per-zone variance of the video features taken per
+// channel, and norms of the audio-to-video cross-attention output; Table 9 caption:
+// r_{v,d}, the audio coupling gate and the audio directional variance).
+//
+// One workgroup per (batch*head, zone).  The zone is streamed row by row: a group of
+// D/8 lanes owns one (t, h) row of the zone and walks it along w, each lane holding 8
+// channels.  Increments along w stay in registers; the neighbour rows along h and t are
+// read again (they hit L2, HBM traffic stays one pass over V and the A2V output).  The
+// per-token A2V norm goes to a zone-local LDS map, from which the audio increments are
+// taken after the streaming pass.
+#include "prism_internal.h"
+
+namespace prism {
+namespace {
+
+constexpr int NT = 256;
+
+template <typename T, int D>
+__global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, const T* __restrict__ a2v,
+                                                   float* __restrict__ stats, Geo g) {
+  constexpr int G = D / 8;      // lanes per token
+  constexpr int RPP = NT / G;   // rows in flight per pass
+  __shared__ float s_a[kMaxZoneVol];
+  __shared__ float s_red[RPP * 3 * 8 * G];  // == 3 * 8 * NT
+  __shared__ float s_share[3][D];
+  __shared__ float s_tmp[8];
+
+  const int tid = threadIdx.x;
+  const int z = blockIdx.x % g.nZ;
+  const int bh = blockIdx.x / g.nZ;
+  const int iw = z % g.nzw, ih = (z / g.nzw) % g.nzh, it = z / (g.nzw * g.nzh);
+  const int t0 = it * g.zt, h0 = ih * g.zh, w0 = iw * g.zw;
+  const int et = min(g.zt, g.T - t0), eh = min(g.zh, g.H - h0), ew = min(g.zw, g.W - w0);
+  const size_t base = size_t(bh) * g.N * D;
+  const size_t row_stride_h = size_t(g.W) * D, row_stride_t = size_t(g.H) * g.W * D;
+  const int cg = tid % G, rg = tid / G;
+
+  float ssd[3][8];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ssd[a][k] = 0.f;
+
+  for (int row = rg; row < et * eh; row += RPP) {
+    const int lt = row / eh, lh = row % eh;
+    const size_t off = base + (size_t((t0 + lt) * g.H + h0 + lh) * g.W + w0) * D + cg * 8;
+    const T* vr = v + off;
+    const T* ar = a2v + off;
+    const bool has_t = lt + 1 < et, has_h = lh + 1 < eh;
+    float prev[8];
+    for (int lw = 0; lw < ew; ++lw) {
+      float x[8], y[8], u[8];
+      load8(vr + size_t(lw) * D, x);
+      if (lw > 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float dd = x[k] - prev[k];
+          ssd[2][k] = fmaf(dd, dd, ssd[2][k]);
+        }
+      }
+      if (has_h) {
+        load8(vr + size_t(lw) * D + row_stride_h, y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float dd = x[k] - y[k];
+          ssd[1][k] = fmaf(dd, dd, ssd[1][k]);
+        }
+      }
+      if (has_t) {
+        load8(vr + size_t(lw) * D + row_stride_t, y);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float dd = x[k] - y[k];
+          ssd[0][k] = fmaf(dd, dd, ssd[0][k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) prev[k] = x[k];
+      load8(ar + size_t(lw) * D, u);
+      float sq = 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) sq = fmaf(u[k], u[k], sq);
+#pragma unroll
+      for (int o = G / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+      if (cg == 0) s_a[(lt * g.zh + lh) * g.zw + lw] = sqrtf(sq);
+    }
+  }
+
+  // ---- video: per-channel semivariance, share per axis, mean over channels
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s_red[(rg * 3 + a) * D + cg * 8 + k] = ssd[a][k];
+  __syncthreads();
+  const float np_t = float(max(et - 1, 0) * eh * ew);
+  const float np_h = float(et * max(eh - 1, 0) * ew);
+  const float np_w = float(et * eh * max(ew - 1, 0));
+  const float npair[3] = {np_t, np_h, np_w};
+  for (int c = tid; c < D; c += NT) {
+    float gam[3];
+#pragma unroll
+    for (int a = 0; a < 3; ++a) {
+      float s = 0.f;
+      for (int r = 0; r < RPP; ++r) s += s_red[(r * 3 + a) * D + c];
+      gam[a] = npair[a] > 0.f ? 0.5f * s / npair[a] : 0.f;
+    }
+    const float den = gam[0] + gam[1] + gam[2] + 1e-12f;
+#pragma unroll
+    for (int a = 0; a < 3; ++a) s_share[a][c] = gam[a] / den;
+  }
+  __syncthreads();
+  float sh[3] = {0.f, 0.f, 0.f};
+  for (int c = tid; c < D; c += NT) {
+#pragma unroll
+    for (int a = 0; a < 3; ++a) sh[a] += s_share[a][c];
+  }
+
+  // ---- audio: norm map increments and zone mean
+  float sa[3] = {0.f, 0.f, 0.f}, asum = 0.f;
+  const int nval = et * eh * ew;
+  const int plane = g.zh * g.zw;
+  for (int p = tid; p < nval; p += NT) {
+    const int lt = p / (eh * ew), lh = (p / ew) % eh, lw = p % ew;
+    const int idx = (lt * g.zh + lh) * g.zw + lw;
+    const float a = s_a[idx];
+    asum += a;
+    if (lt + 1 < et) { const float dd = a - s_a[idx + plane]; sa[0] = fmaf(dd, dd, sa[0]); }
+    if (lh + 1 < eh) { const float dd = a - s_a[idx + g.zw]; sa[1] = fmaf(dd, dd, sa[1]); }
+    if (lw + 1 < ew) { const float dd = a - s_a[idx + 1]; sa[2] = fmaf(dd, dd, sa[2]); }
+  }
+  float res[7];
+#pragma unroll
+  for (int a = 0; a < 3; ++a) res[a] = block_sum<NT>(sh[a], s_tmp);
+#pragma unroll
+  for (int a = 0; a < 3; ++a) res[3 + a] = block_sum<NT>(sa[a], s_tmp);
+  res[6] = block_sum<NT>(asum, s_tmp);
+  if (tid == 0) {
+    float* out = stats + (size_t(bh) * g.nZ + z) * 8;
+    out[0] = res[0] / float(D);
+    out[1] = res[1] / float(D);
+    out[2] = res[2] / float(D);
+    out[3] = np_t > 0.f ? 0.5f * res[3] / np_t : 0.f;
+    out[4] = np_h > 0.f ? 0.5f * res[4] / np_h : 0.f;
+    out[5] = np_w > 0.f ? 0.5f * res[5] / np_w : 0.f;
+    out[6] = res[6] / float(nval);
+    out[7] = float(nval);
+  }
+}
+
+template <typename T>
+hipError_t launch_t(const void* v, const void* a2v, int BH, int d, const Geo& g, float* stats,
+                    hipStream_t s) {
+  dim3 grid(unsigned(BH) * unsigned(g.nZ)), block(NT);
+  const T* pv = static_cast<const T*>(v);
+  const T* pa = static_cast<const T*>(a2v);
+  switch (d) {
+    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256>), grid, block, 0, s, pv, pa, stats, g); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_zone_stats(const void* v, const void* a2v, prism_dtype dt, int BH, int d,
+                             const Geo& g, float* stats, hipStream_t s) {
+  if (dt == PRISM_BF16) return launch_t<bf16_t>(v, a2v, BH, d, g, stats, s);
+  return launch_t<float>(v, a2v, BH, d, g, stats, s);
+}
+
+}  // namespace prism

@@ -1,0 +1,120 @@
+"""One Prism attention layer as a sequence of C-ABI calls.
+
+PrismLayer owns the device buffers (allocated once with torch) and calls the library in
+the method's order (Figure 2 caption): zone statistics -> shape assignment -> permute
+Q, K, V -> pooling + hybrid selection (+ reverse index) -> block-sparse attention ->
+inverse permute of O; the backward permutes dO, runs the sparse backward and inverse
+permutes dQ, dK, dV.  Everything is enqueued on torch's current stream."""
+
+from __future__ import annotations
+
+from typing import Optional, Sequence, Tuple
+
+import torch
+
+from . import api
+from .api import ShapeRule
+
+Shape = Tuple[int, int, int]
+
+
+class PrismLayer:
+    def __init__(self, B: int, Hh: int, d: int, grid: Sequence[int], zone: Sequence[int],
+                 cands: Sequence[Shape], top_p: float, k_min: int, k_max: int,
+                 dtype: torch.dtype = torch.bfloat16, device="cuda", scale: Optional[float] = None,
+                 rule: ShapeRule = ShapeRule()):
+        self.B, self.Hh, self.d = B, Hh, d
+        self.dtype, self.device = dtype, torch.device(device)
+        self.grid = api.make_grid(grid, zone)
+        self.shapes = api.make_shapes(cands)
+        self.shape_params = api.make_shape_params(rule)
+        self.sel_params = api.make_select_params(top_p, k_min, k_max)
+        self.scale = api.default_scale(d) if scale is None else float(scale)
+        self.vol = self.shapes.vol
+        self.N = int(grid[0] * grid[1] * grid[2])
+        self.nZ = api.prism_num_zones(self.grid)
+        self.nb = api.prism_num_blocks(self.grid, self.shapes)
+        if self.nZ < 0 or self.nb < 0:
+            raise ValueError(api.prism_last_error())
+        self.Npad = self.nb * self.vol
+        self.k_max = int(k_max)
+        dev, i32, f32 = self.device, torch.int32, torch.float32
+        e = lambda *s, dt=dtype: torch.empty(s, dtype=dt, device=dev)  # noqa: E731
+        B_, H_ = B, Hh
+        self.stats = e(B_, H_, self.nZ, 8, dt=f32)
+        self.shape_id = e(B_, H_, self.nZ, dt=i32)
+        self.shape_margin = e(B_, H_, self.nZ, dt=f32)
+        self.bvalid = e(B_, H_, self.nb, dt=i32)
+        self.qp, self.kp, self.vp = (e(B_, H_, self.Npad, d) for _ in range(3))
+        self.op = e(B_, H_, self.Npad, d)
+        self.lse = e(B_, H_, self.Npad, dt=f32)
+        self.sel_idx = e(B_, H_, self.nb, self.k_max, dt=i32)
+        self.sel_cnt = e(B_, H_, self.nb, dt=i32)
+        self.sel_margin = e(B_, H_, self.nb, dt=f32)
+        self.rev_ptr = e(B_, H_, self.nb + 1, dt=i32)
+        self.rev_idx = e(B_, H_, self.nb * self.k_max, dt=i32)
+        self.ws_sel = e(api.prism_select_workspace_size(B, Hh, self.nb, d), dt=torch.uint8)
+        self.ws_bwd = e(api.prism_bwd_workspace_size(B, Hh, self.nb, self.vol), dt=torch.uint8)
+        self.o = e(B_, H_, self.N, d)
+        self._grad_bufs = None
+
+    def _grads(self):
+        if self._grad_bufs is None:
+            e = lambda *s: torch.empty(s, dtype=self.dtype, device=self.device)  # noqa: E731
+            B, H, P, N, d = self.B, self.Hh, self.Npad, self.N, self.d
+            self._grad_bufs = dict(dop=e(B, H, P, d), dqp=e(B, H, P, d), dkp=e(B, H, P, d), dvp=e(B, H, P, d),
+                                   dq=e(B, H, N, d), dk=e(B, H, N, d), dv=e(B, H, N, d))
+        return self._grad_bufs
+
+    # ---- stages (each is exactly one library call)
+    def zone_stats(self, v, a2v):
+        api.prism_zone_stats(v, a2v, self.grid, self.stats)
+
+    def assign_shapes(self):
+        api.prism_assign_shapes(self.stats, self.grid, self.shapes, self.shape_params, self.shape_id,
+                                self.shape_margin)
+
+    def permute(self, x, y, inverse=False, block_valid=None):
+        api.prism_permute(x, y, self.grid, self.shapes, self.shape_id, inverse, block_valid)
+
+    def select(self):
+        api.prism_select_blocks(self.qp, self.kp, self.bvalid, self.vol, self.scale, self.sel_params,
+                                self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.ws_sel,
+                                self.sel_margin)
+
+    def attn_fwd(self):
+        api.prism_sparse_attn_fwd(self.qp, self.kp, self.vp, self.bvalid, self.sel_idx, self.sel_cnt,
+                                  self.vol, self.scale, self.op, self.lse)
+
+    def attn_bwd(self, marks=None):
+        g = self._grads()
+        api.prism_sparse_attn_bwd(self.qp, self.kp, self.vp, self.op, g["dop"], self.lse, self.bvalid,
+                                  self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.vol, self.scale,
+                                  g["dqp"], g["dkp"], g["dvp"], self.ws_bwd, marks)
+
+    # ---- whole layer
+    def forward(self, q, k, v, a2v):
+        self.zone_stats(v, a2v)
+        self.assign_shapes()
+        self.permute(q, self.qp, block_valid=self.bvalid)
+        self.permute(k, self.kp)
+        self.permute(v, self.vp)
+        self.select()
+        self.attn_fwd()
+        self.permute(self.op, self.o, inverse=True)
+        return self.o
+
+    def backward(self, do, marks=None):
+        g = self._grads()
+        self.permute(do, g["dop"])
+        self.attn_bwd(marks)
+        self.permute(g["dqp"], g["dq"], inverse=True)
+        self.permute(g["dkp"], g["dk"], inverse=True)
+        self.permute(g["dvp"], g["dv"], inverse=True)
+        return g["dq"], g["dk"], g["dv"]
+
+    @classmethod
+    def for_workload(cls, w, device="cuda", heads: Optional[int] = None):
+        dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
+        return cls(w.B, w.heads if heads is None else heads, w.d, w.grid, w.zone, list(w.cands), w.top_p,
+                   w.k_min, w.k_max, dtype=dt, device=device)

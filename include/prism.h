@@ -1,0 +1,197 @@
+/*
+ * libprism: content-adaptive block-sparse video self-attention (Prism) for MI355X.
+ *
+ * The method (Prism paper, abstract and Figure 2 caption): the video token grid is cut
+ * into spatiotemporal macro-zones; each zone gets a block shape chosen from the
+ * per-axis variance of the video value features (Table 9 caption, r_{v,d}) and from the
+ * norm of the audio-to-video cross-attention output (Table 9 caption, the gate a-bar and
+ * the audio directional variance); tokens are permuted so that every block is a
+ * contiguous run; block-pooled Q/K scores drive a hybrid Top-k/Top-p selection per
+ * query block (Table 7 caption); exact softmax attention then runs over the selected
+ * blocks, forward and backward.
+ *
+ * Conventions shared by every call.
+ *   Memory     Every pointer is DEVICE memory allocated and owned by the caller, except
+ *              the small descriptor structs (grid, shapes, params), which are HOST
+ *              memory read during the call.  The library never allocates or frees device
+ *              memory and keeps no state between calls.  Scratch space comes from the
+ *              caller through (workspace, ws_bytes); its required size is returned by the
+ *              matching *_workspace_size function.
+ *   Layout     Token tensors are row-major [B][Hh][N][d] with tokens in t-major raster
+ *              order n = (t*H + h)*W + w.  Permuted ("slot order") tensors are
+ *              [B][Hh][Npad][d], Npad = nb * vol, where block I owns slots
+ *              [I*vol, (I+1)*vol) and its valid rows come first (block_valid[I] of them).
+ *   Streams    Each call enqueues its kernels on `stream` (may be 0) and returns without
+ *              synchronizing.  Inputs must stay valid until that work has run.
+ *   Errors     A call validates every argument on the host before launching anything and
+ *              returns a prism_status; on failure nothing has been enqueued and
+ *              prism_last_error() gives a message (thread-local, valid until the next call
+ *              on that thread).  No C++ exception crosses this interface.
+ *   dtypes     PRISM_BF16 (bfloat16 storage, float32 accumulation) or PRISM_F32.
+ *              Statistics, pooled means, scores, LSE and D are always float32.
+ */
+#ifndef PRISM_H
+#define PRISM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_ERR_ARG = 1,    /* null pointer, negative size, parameter out of range */
+  PRISM_ERR_DTYPE = 2,  /* unknown dtype or dtype/size combination not supported */
+  PRISM_ERR_SHAPE = 3,  /* sizes inconsistent with each other (zone, shapes, nb, vol) */
+  PRISM_ERR_LAUNCH = 4  /* the HIP runtime refused a launch */
+} prism_status;
+
+typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+
+/* Video latent grid (T, H, W) and macro-zone extents (zt, zh, zw).  Zones tile the grid
+ * from the origin in t-major raster order; the grid is padded at its far edges up to a
+ * multiple of the zone (abstract: spatiotemporal macro-zones). */
+typedef struct {
+  int32_t T, H, W;
+  int32_t zt, zh, zw;
+} prism_grid;
+
+#define PRISM_MAX_SHAPES 16
+
+/* Candidate block shapes (b_T, b_H, b_W), all holding `vol` tokens (Table 11 caption:
+ * shapes b_T b_H b_W; one candidate set holds a single volume).  A candidate can be
+ * assigned to a zone only if each extent divides the zone's extent.  List order is the
+ * tie-break order. */
+typedef struct {
+  int32_t n, vol;
+  int32_t bt[PRISM_MAX_SHAPES], bh[PRISM_MAX_SHAPES], bw[PRISM_MAX_SHAPES];
+} prism_shapes;
+
+/* Shape rule constants: power-law exponent alpha of b*_d ~ g_d^-alpha (Table 10 caption),
+ * gate thresholds tau_lo/tau_hi on m_z / m-bar, guidance floor g_min, ratio guard eps.
+ * The documented defaults are 0.5, 1, 2, 1e-3, 1e-12. */
+typedef struct {
+  float alpha, tau_lo, tau_hi, g_min, eps;
+} prism_shape_params;
+
+/* Hybrid selection (Table 7 caption): the Top-p count is the smallest number of key
+ * blocks whose cumulative pooled attention weight strictly exceeds top_p, then clamped
+ * to [k_min, k_max] and to the number of live key blocks.  0 < top_p <= 1,
+ * 1 <= k_min <= k_max. */
+typedef struct {
+  float top_p;
+  int32_t k_min, k_max;
+} prism_select_params;
+
+/* Number of zones and of blocks (nb = zones * zt*zh*zw / vol) for a grid and candidate
+ * set.  Host-only helpers; return -1 on invalid arguments. */
+int64_t prism_num_zones(const prism_grid* grid);
+int64_t prism_num_blocks(const prism_grid* grid, const prism_shapes* shapes);
+
+/* (a1) Zone statistics (abstract; Table 9 caption).
+ * v, a2v   [B][Hh][N][d] value features and A2V cross-attention output, N = T*H*W.
+ * stats    out float [B][Hh][nZ][8]: r_v[t,h,w] (per-channel directional share of the
+ *          lag-one semivariance of v, averaged over channels), gamma_a[t,h,w] (lag-one
+ *          semivariance of the per-token norm ||a2v||), m_z (mean norm), n_z (valid
+ *          tokens).  Neighbour pairs never cross a zone border or the grid edge.
+ * Requires d % 8 == 0, 8 <= d <= 256, zt*zh*zw <= 4096. */
+prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh,
+                              int d, const prism_grid* grid, float* stats, hipStream_t stream);
+
+/* (a2) Shape assignment (abstract: finer blocks along fast-varying, audio-coupled axes;
+ * Table 10 caption: b*_d ~ g_d^-alpha and its quantization).
+ * stats    float [B][Hh][nZ][8] from prism_zone_stats.
+ * shape_id out int32 [B][Hh][nZ]: index into shapes of the feasible candidate nearest, in
+ *          log2 extents, to lambda_d = log2(vol)/3 - alpha (log2 g_d - mean_d log2 g_d),
+ *          where g_d = max((1 - a) r_v,d + a v-hat_a,d, g_min), a = clamp((m_z/m-bar -
+ *          tau_lo)/(tau_hi - tau_lo), 0, 1), v-hat_a = gamma_a / (sum gamma_a + eps).
+ * margin   optional out float [B][Hh][nZ]: (D_2 - D_1)/D_2 between best and runner-up. */
+prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_grid* grid,
+                                 const prism_shapes* shapes, const prism_shape_params* params,
+                                 int32_t* shape_id, float* margin, hipStream_t stream);
+
+/* (a3) Token permutation into blocks (abstract: each block's tokens are contiguous).
+ * Slot order: zones in raster order; a zone's blocks in raster order over its block grid;
+ * inside a block, the tokens lying in the real grid first (raster order), then padding.
+ * inverse == 0: x [B][Hh][N][d] -> y [B][Hh][Npad][d], zeros at padding slots.
+ * inverse == 1: x [B][Hh][Npad][d] -> y [B][Hh][N][d], padding slots dropped.
+ * block_valid optional out int32 [B][Hh][nb]: valid slots per block (0 = dead block).
+ * Requires d * sizeof(dtype) % 16 == 0. */
+prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int Hh, int d,
+                           const prism_grid* grid, const prism_shapes* shapes,
+                           const int32_t* shape_id, int inverse, int32_t* block_valid,
+                           hipStream_t stream);
+
+/* (a4, a5) Block pooling and hybrid Top-k/Top-p selection (abstract; Figure 2 caption;
+ * Table 7 caption).
+ * qp, kp       [B][Hh][nb*vol][d] permuted Q and K.
+ * block_valid  int32 [B][Hh][nb].
+ * Pooled means (float32) of each block's valid rows give scores scale * <Qbar_I, Kbar_J>
+ * over live key blocks; softmax, then the hybrid count on the descending order (ties to
+ * the lower block index).  Dead query blocks select nothing.
+ * sel_idx  out int32 [B][Hh][nb][k_max], ascending, -1 padded;  sel_cnt out [B][Hh][nb].
+ * rev_ptr  out int32 [B][Hh][nb+1] and rev_idx out int32 [B][Hh][nb*k_max]: for each key
+ *          block, the query blocks that selected it, ascending (-1 padded).
+ * sel_margin optional out float [B][Hh][nb]: smallest relative distance of the row's
+ *          decision from flipping (gap at the cut, distance of the cumulative sum to p).
+ * workspace    device scratch of prism_select_workspace_size() bytes. */
+size_t prism_select_workspace_size(int B, int Hh, int nb, int d);
+prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dtype,
+                                 const int32_t* block_valid, int B, int Hh, int nb, int vol, int d,
+                                 float scale, const prism_select_params* params, int32_t* sel_idx,
+                                 int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
+                                 float* sel_margin, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* (a6) Block-sparse attention forward (Figure 2 caption).  Query row i of block I attends
+ * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:
+ *   O_i = softmax_j(scale q_i.k_j) v_j,  lse_i = ln sum_j exp(scale q_i.k_j).
+ * op   out [B][Hh][nb*vol][d] (zeros at padding rows);  lse out float [B][Hh][nb*vol]
+ * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}. */
+prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
+                                   const int32_t* block_valid, const int32_t* sel_idx,
+                                   const int32_t* sel_cnt, int k_max, int B, int Hh, int nb, int vol,
+                                   int d, float scale, void* op, float* lse, hipStream_t stream);
+
+/* (a7) Block-sparse attention backward, selection held fixed.
+ * With D_i = dO_i.O_i, P_ij = exp(scale q_i.k_j - lse_i), dS_ij = P_ij (dO_i.v_j - D_i):
+ *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
+ * dqp, dkp, dvp out [B][Hh][nb*vol][d] (zeros at padding rows).  dK/dV walk the reverse
+ * index; no atomics, results are deterministic.
+ * marks    optional array of 4 caller-created hipEvents recorded on `stream` before the
+ *          D kernel, after it, after the dK/dV kernel and after the dQ kernel.
+ * workspace    device scratch of prism_bwd_workspace_size() bytes. */
+size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol);
+prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* vp, const void* op,
+                                   const void* dop, const float* lse, prism_dtype dtype,
+                                   const int32_t* block_valid, const int32_t* sel_idx,
+                                   const int32_t* sel_cnt, int k_max, const int32_t* rev_ptr,
+                                   const int32_t* rev_idx, int B, int Hh, int nb, int vol, int d,
+                                   float scale, void* dqp, void* dkp, void* dvp, void* workspace,
+                                   size_t ws_bytes, hipEvent_t* marks, hipStream_t stream);
+
+/* Dense attention comparator on unpermuted [B][Hh][N][d] tensors (every key attended),
+ * the same kernels run with every block selected; used to measure the sparse path's
+ * speedup.  lse float [B][Hh][N].  Requires d in {64, 128}. */
+prism_status prism_dense_attn_fwd(const void* q, const void* k, const void* v, prism_dtype dtype,
+                                  int B, int Hh, int N, int d, float scale, void* o, float* lse,
+                                  hipStream_t stream);
+size_t prism_dense_bwd_workspace_size(int B, int Hh, int N);
+prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, prism_dtype dtype, int B,
+                                  int Hh, int N, int d, float scale, void* dq, void* dk, void* dv,
+                                  void* workspace, size_t ws_bytes, hipEvent_t* marks,
+                                  hipStream_t stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* prism_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H */

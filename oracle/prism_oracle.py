@@ -449,6 +449,47 @@ def select_blocks(qbar: np.ndarray, kbar: np.ndarray, bvalid: np.ndarray, scale:
     return sel, near
 
 
+def select_blocks_all(qbar: np.ndarray, kbar: np.ndarray, bvalid: np.ndarray, scale: float,
+                      top_p: float, k_min: int, k_max: int, dtype=np.float32):
+    """select_blocks over every row, with each head's score matrix formed at once (same
+    arithmetic as select_row, in matrix form: one matmul, row-wise softmax, row-wise
+    stable descending sort, row-wise cumulative sums)."""
+    B, Hh, nb, C = qbar.shape
+    sel, near = {}, {}
+    for b in range(B):
+        for h in range(Hh):
+            live = bvalid[b, h] > 0
+            J = np.nonzero(live)[0]
+            Ilive = np.nonzero(live)[0]
+            K = np.asarray(kbar[b, h, J]).astype(dtype)
+            Qm = np.asarray(qbar[b, h, Ilive]).astype(dtype)
+            logits = (Qm @ K.T) * dtype(scale)
+            e = np.exp(logits - logits.max(axis=1, keepdims=True))
+            P = (e / e.sum(axis=1, keepdims=True, dtype=dtype)).astype(dtype)
+            order = np.argsort(-P, axis=1, kind="stable")
+            Ps = np.take_along_axis(P, order, axis=1)
+            Cs = np.cumsum(Ps, axis=1, dtype=dtype)
+            Cd = np.cumsum(Ps.astype(np.float64), axis=1)
+            nl = J.size
+            for r, I in enumerate(Ilive):
+                over = np.nonzero(Cs[r] > dtype(top_p))[0]
+                n_p = int(over[0]) + 1 if over.size else nl
+                n = _clamp(n_p, k_min, k_max, nl)
+                sel[(b, h, int(I))] = np.sort(J[order[r, :n]]).astype(np.int32)
+                nr = False
+                if n < nl and (float(Ps[r, n - 1]) - float(Ps[r, n])) <= NEAR_TIE * float(Ps[r, n - 1]):
+                    nr = True
+                if abs(Cd[r, n_p - 1] - top_p) < NEAR_TIE and _clamp(n_p + 1, k_min, k_max, nl) != n:
+                    nr = True
+                if n_p >= 2 and abs(Cd[r, n_p - 2] - top_p) < NEAR_TIE and _clamp(n_p - 1, k_min, k_max, nl) != n:
+                    nr = True
+                near[(b, h, int(I))] = nr
+            for I in np.nonzero(~live)[0]:
+                sel[(b, h, int(I))] = np.zeros(0, dtype=np.int32)
+                near[(b, h, int(I))] = False
+    return sel, near
+
+
 def selection_arrays(sel: Dict, B: int, Hh: int, nb: int, k_max: int):
     """ELL form of a full selection: idx [B,Hh,nb,k_max] (-1 padded) and cnt [B,Hh,nb]."""
     idx = np.full((B, Hh, nb, k_max), -1, dtype=np.int32)
@@ -457,6 +498,24 @@ def selection_arrays(sel: Dict, B: int, Hh: int, nb: int, k_max: int):
         idx[b, h, I, :s.size] = s
         cnt[b, h, I] = s.size
     return idx, cnt
+
+
+def reverse_index_sorted(idx: np.ndarray, cnt: np.ndarray):
+    """reverse_index by one stable sort of the (I, J) pairs on J per head (pairs are
+    listed in ascending I, so each key block's query blocks stay ascending)."""
+    B, Hh, nb, k_max = idx.shape
+    rev_ptr = np.zeros((B, Hh, nb + 1), dtype=np.int32)
+    rev_idx = np.full((B, Hh, nb * k_max), -1, dtype=np.int32)
+    pos = np.arange(k_max)[None, :]
+    for b in range(B):
+        for h in range(Hh):
+            m = pos < cnt[b, h][:, None]
+            I = np.broadcast_to(np.arange(nb)[:, None], (nb, k_max))[m]
+            J = idx[b, h][m]
+            o = np.argsort(J, kind="stable")
+            rev_idx[b, h, :o.size] = I[o]
+            rev_ptr[b, h, 1:] = np.cumsum(np.bincount(J, minlength=nb))
+    return rev_ptr, rev_idx
 
 
 def reverse_index(idx: np.ndarray, cnt: np.ndarray):
@@ -516,6 +575,15 @@ def sparse_attn_fwd(qp, kp, vp, bvalid, sel: Dict, scale: float, vol: int,
     return O, L
 
 
+def _transpose_selection(sel: Dict) -> Dict:
+    """(b, h, J) -> ascending array of the query blocks I whose selection holds J."""
+    cols: Dict[Tuple[int, int, int], List[int]] = {}
+    for (b, h, I) in sorted(sel):
+        for J in sel[(b, h, I)]:
+            cols.setdefault((b, h, int(J)), []).append(I)
+    return {k: np.array(v, dtype=np.int32) for k, v in cols.items()}
+
+
 def sparse_attn_bwd(qp, kp, vp, op, dop, lse, bvalid, sel: Dict, scale: float, vol: int,
                     q_blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
                     k_blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
@@ -525,41 +593,45 @@ def sparse_attn_bwd(qp, kp, vp, op, dop, lse, bvalid, sel: Dict, scale: float, v
         D_i = dO_i . O_i,  P_ij = exp(scale q_i.k_j - LSE_i),  dV_j = sum_i P_ij dO_i,
         dP_ij = dO_i . v_j,  dS_ij = P_ij (dP_ij - D_i),
         dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
-    q_blocks limits dQ to the listed query blocks, k_blocks limits dK/dV to the listed
-    key blocks (all by default).  Returns float64 dQ', dK', dV'."""
+    dQ is accumulated per query block over its selected key blocks, dK/dV per key block
+    over the query blocks that selected it.  q_blocks / k_blocks limit the work to the
+    listed blocks (all by default); other rows stay 0.  Returns float64 dQ', dK', dV'."""
     qp, kp, vp, op, dop = (np.asarray(a, dtype=np.float64) for a in (qp, kp, vp, op, dop))
     B, Hh, Np, C = qp.shape
     nb = Np // vol
     dQ, dK, dV = np.zeros_like(qp), np.zeros_like(kp), np.zeros_like(vp)
-    Dfull = (dop * op).sum(axis=-1)
-    qset = None if q_blocks is None else set(q_blocks)
-    kset = None if k_blocks is None else set(k_blocks)
-    for b in range(B):
-        for h in range(Hh):
-            for I in range(nb):
-                n = int(bvalid[b, h, I])
-                js = sel.get((b, h, I), np.zeros(0, dtype=np.int32))
-                if n == 0 or js.size == 0:
-                    continue
-                want_q = qset is None or (b, h, I) in qset
-                want_k = [J for J in js if kset is None or (b, h, int(J)) in kset]
-                if not want_q and not want_k:
-                    continue
-                q = _rows(qp, b, h, I, vol, n)
-                do = _rows(dop, b, h, I, vol, n)
-                Di = Dfull[b, h, I * vol: I * vol + n][:, None]
-                li = lse[b, h, I * vol: I * vol + n][:, None]
-                for J in js:
-                    m = int(bvalid[b, h, J])
-                    k = _rows(kp, b, h, J, vol, m)
-                    v = _rows(vp, b, h, J, vol, m)
-                    P = np.exp((q @ k.T) * scale - li)
-                    dS = P * (do @ v.T - Di)
-                    if want_q:
-                        dQ[b, h, I * vol: I * vol + n] += scale * (dS @ k)
-                    if kset is None or (b, h, int(J)) in kset:
-                        dV[b, h, J * vol: J * vol + m] += P.T @ do
-                        dK[b, h, J * vol: J * vol + m] += scale * (dS.T @ q)
+    lse = np.asarray(lse, dtype=np.float64)
+
+    def rows(x, b, h, I):
+        return x[b, h, I * vol: I * vol + int(bvalid[b, h, I])]
+
+    def grads_of_rows(q, do, o, li, k, v):
+        """P and dS of query rows (q, dO, O, LSE) against key rows (k, v)."""
+        Di = (do * o).sum(axis=1, keepdims=True)
+        P = np.exp((q @ k.T) * scale - li[:, None])
+        return P, P * (do @ v.T - Di)
+
+    allq = [(b, h, I) for b in range(B) for h in range(Hh) for I in range(nb)]
+    for (b, h, I) in (allq if q_blocks is None else q_blocks):
+        js = sel.get((b, h, I), ())
+        if bvalid[b, h, I] == 0 or len(js) == 0:
+            continue
+        k = np.concatenate([rows(kp, b, h, int(J)) for J in js])
+        v = np.concatenate([rows(vp, b, h, int(J)) for J in js])
+        q = rows(qp, b, h, I)
+        P, dS = grads_of_rows(q, rows(dop, b, h, I), rows(op, b, h, I), rows(lse, b, h, I), k, v)
+        dQ[b, h, I * vol: I * vol + q.shape[0]] = scale * (dS @ k)
+    cols = _transpose_selection(sel)
+    for (b, h, J) in (allq if k_blocks is None else k_blocks):
+        Is = [int(I) for I in cols.get((b, h, J), ()) if bvalid[b, h, I] > 0]
+        m = int(bvalid[b, h, J])
+        if m == 0 or not Is:
+            continue
+        cat = lambda x: np.concatenate([rows(x, b, h, I) for I in Is])  # noqa: E731
+        q, do = cat(qp), cat(dop)
+        P, dS = grads_of_rows(q, do, cat(op), cat(lse), rows(kp, b, h, J), rows(vp, b, h, J))
+        dV[b, h, J * vol: J * vol + m] = P.T @ do
+        dK[b, h, J * vol: J * vol + m] = scale * (dS.T @ q)
     return dQ, dK, dV
 
 

@@ -1,0 +1,128 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function the header declares, and rejects invalid arguments before launching anything."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from oracle import prism_oracle as O
+from workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from content_adaptive_block_zone_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from content_adaptive_block_zone_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from content_adaptive_block_zone_amd import _lib
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.PROTOTYPES, f"binding lacks {n}"
+    assert set(_lib.PROTOTYPES) == set(names)
+
+
+def test_zone_and_block_counts_match_the_oracle(lib):
+    from content_adaptive_block_zone_amd import api
+    for w in WORKLOADS:
+        g = api.make_grid(w.grid, w.zone)
+        s = api.make_shapes(list(w.cands))
+        nz = O.num_zones(w.grid, w.zone)
+        assert api.prism_num_zones(g) == nz
+        assert api.prism_num_blocks(g, s) == nz * (w.zone[0] * w.zone[1] * w.zone[2]) // w.vol
+
+
+def test_host_helpers_reject_bad_geometry(lib):
+    from content_adaptive_block_zone_amd import api
+    assert api.prism_num_zones(api.make_grid((0, 8, 8), (2, 4, 8))) == -1
+    assert api.prism_num_zones(api.make_grid((4, 8, 8), (64, 64, 64))) == -1        # zone too large
+    mixed = api.make_shapes([(1, 4, 4), (2, 2, 2)])                                 # unequal volumes
+    assert api.prism_num_blocks(api.make_grid((4, 8, 8), (2, 4, 8)), mixed) == -1
+    nofit = api.make_shapes([(4, 2, 2)])                                            # never fits 2x4x8
+    assert api.prism_num_blocks(api.make_grid((4, 8, 8), (2, 4, 8)), nofit) == -1
+    assert api.prism_select_workspace_size(0, 1, 1, 64) == 0
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_calls_validate_before_launch(lib):
+    """Every call with one bad argument returns its error code and a message; the fake
+    pointers below are never dereferenced because validation fails first."""
+    from content_adaptive_block_zone_amd import _lib, api
+    P = ctypes.c_void_p(64)
+    g = api.make_grid((4, 8, 8), (2, 4, 8))
+    s = api.make_shapes([(1, 4, 4), (2, 2, 4), (2, 4, 2), (4, 2, 2)])
+    sp = api.make_shape_params()
+    sel = api.make_select_params(0.9, 2, 8)
+    F32, BF16 = _lib.PRISM_F32, _lib.PRISM_BF16
+    E = _lib
+
+    cases = [
+        ("prism_zone_stats", (None, P, F32, 1, 2, 64, g, P, None), E.PRISM_ERR_ARG),
+        ("prism_zone_stats", (P, P, 7, 1, 2, 64, g, P, None), E.PRISM_ERR_DTYPE),
+        ("prism_zone_stats", (P, P, F32, 1, 2, 48, g, P, None), E.PRISM_ERR_DTYPE),
+        ("prism_zone_stats", (P, P, F32, 0, 2, 64, g, P, None), E.PRISM_ERR_ARG),
+        ("prism_zone_stats", (P, P, F32, 1, 2, 64, api.make_grid((4, 8, 8), (64, 64, 2)), P, None),
+         E.PRISM_ERR_SHAPE),
+        ("prism_assign_shapes", (P, 1, 2, g, api.make_shapes([(1, 4, 4), (1, 2, 2)]), sp, P, None, None),
+         E.PRISM_ERR_SHAPE),
+        ("prism_assign_shapes", (P, 1, 2, g, s, api.make_shape_params(api.ShapeRule(tau_lo=2.0, tau_hi=1.0)),
+                                 P, None, None), E.PRISM_ERR_ARG),
+        ("prism_assign_shapes", (P, 1, 2, g, s, api.make_shape_params(api.ShapeRule(g_min=0.0)), P, None, None),
+         E.PRISM_ERR_ARG),
+        ("prism_permute", (P, P, F32, 1, 2, 64, g, s, P, 2, None, None), E.PRISM_ERR_ARG),
+        ("prism_permute", (P, P, BF16, 1, 2, 4, g, s, P, 0, None, None), E.PRISM_ERR_DTYPE),
+        ("prism_permute", (P, P, F32, 1, 2, 64, g, s, P, 0, None, None), E.PRISM_ERR_ARG),   # x aliases y
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 16, 16, 64, 0.125, api.make_select_params(0.0, 2, 8),
+                                 P, P, P, P, None, P, 1 << 30, None), E.PRISM_ERR_ARG),
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 16, 16, 64, 0.125, api.make_select_params(0.9, 5, 4),
+                                 P, P, P, P, None, P, 1 << 30, None), E.PRISM_ERR_ARG),
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 16, 16, 64, 0.125, sel, P, P, P, P, None, P, 16, None),
+         E.PRISM_ERR_ARG),                                                             # workspace too small
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 20000, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 40,
+                                 None), E.PRISM_ERR_SHAPE),
+        ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 8, 1, 2, 16, 16, 96, 0.125, P, P, None),
+         E.PRISM_ERR_DTYPE),
+        ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 8, 1, 2, 16, 128, 64, 0.125, P, P, None),
+         E.PRISM_ERR_SHAPE),
+        ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 0, 1, 2, 16, 16, 64, 0.125, P, P, None),
+         E.PRISM_ERR_ARG),
+        ("prism_sparse_attn_bwd", (P, P, P, P, P, P, F32, P, P, P, 8, P, P, 1, 2, 16, 16, 64, 0.125, P, P, P,
+                                   P, 8, None, None), E.PRISM_ERR_ARG),
+        ("prism_dense_attn_fwd", (P, P, P, F32, 1, 2, 0, 64, 0.125, P, P, None), E.PRISM_ERR_ARG),
+        ("prism_dense_attn_bwd", (P, P, P, P, P, P, F32, 1, 2, 256, 64, float("nan"), P, P, P, P, 1 << 30,
+                                  None, None), E.PRISM_ERR_ARG),
+    ]
+    for name, args, want in cases:
+        st = getattr(lib, name)(*args)
+        assert st == want, (name, args, st, lib.prism_last_error())
+        assert lib.prism_last_error().decode(), name
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    from content_adaptive_block_zone_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load()

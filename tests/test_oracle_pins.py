@@ -493,3 +493,19 @@ def test_full_chain_tiny_workload_invariants():
     assert np.isfinite(f["o"]).all()
     bw = O.prism_backward(f, x["do"].numpy())
     assert np.isfinite(bw["dq"]).all() and nb == 16
+
+
+def test_vectorised_selection_and_reverse_match_row_forms():
+    rng = np.random.default_rng(11)
+    nb, d = 40, 16
+    qb = rng.standard_normal((1, 2, nb, d)).astype(np.float32)
+    kb = rng.standard_normal((1, 2, nb, d)).astype(np.float32)
+    bv = rng.integers(0, 3, size=(1, 2, nb)).astype(np.int32) * 8
+    s1, n1 = O.select_blocks(qb, kb, bv, 0.7, 0.8, 2, 9)
+    s2, n2 = O.select_blocks_all(qb, kb, bv, 0.7, 0.8, 2, 9)
+    assert s1.keys() == s2.keys()
+    for k in s1:
+        assert s1[k].tolist() == s2[k].tolist() and n1[k] == n2[k]
+    idx, cnt = O.selection_arrays(s1, 1, 2, nb, 9)
+    a, b = O.reverse_index(idx, cnt), O.reverse_index_sorted(idx, cnt)
+    assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
