@@ -1,0 +1,277 @@
+"""Benchmark of one Prism attention layer (forward + backward) on one MI355X.
+
+A step is one pass of the whole path over the 2K-like workload (B=1, 4-head slice of a
+40-head layer, d=128, grid 21x90x160 = 302,400 tokens, 64-token shapes, Top-p 0.85,
+Top-k 32..768): zone statistics, shape assignment, permutation of Q/K/V, pooling +
+hybrid selection + reverse index, sparse attention forward, inverse permutation of O,
+permutation of dO, sparse attention backward, inverse permutation of dQ/dK/dV.
+Inputs are seeded synthetic tensors already resident in HBM.
+
+Prints one JSON line.  `value` is effective TFLOP/s of the whole step: 14*d flops per
+selected valid (query, key) token pair (forward 4d, backward 10d) divided by the step
+time.  Also reported: ms per step (= per layer), attention-only TFLOP/s, per-stage
+times, the dense comparator's time on the same inputs and the speedup over it, the
+roofline of the dominant kernel, and the CPU oracle timed on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+MI355X_BF16_DENSE_TFLOPS = 2500.0
+MI355X_HBM_GBPS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def selected_pairs(L):
+    """Sum over heads and query blocks of n_I * sum_{J in sel(I)} n_J (valid token pairs)."""
+    import torch
+    idx = L.sel_idx.long()                                           # [B, Hh, nb, k_max]
+    bv = L.bvalid.long()                                             # [B, Hh, nb]
+    nJ = torch.gather(bv, 2, idx.clamp(min=0).reshape(L.B, L.Hh, -1)).reshape(idx.shape)
+    keys = (nJ * (idx >= 0)).sum(dim=-1)
+    return int((keys * bv).sum().item())
+
+
+def density(L):
+    import torch
+    live = (L.bvalid > 0).sum(dim=-1).double()                      # [B, Hh]
+    per_head = L.sel_cnt.double().sum(dim=-1) / (live * live)
+    return float(per_head.mean().item())
+
+
+def run_gpu(args):
+    import torch
+
+    from content_adaptive_block_zone_amd import _lib, api
+    from content_adaptive_block_zone_amd.pipeline import PrismLayer
+    from workloads import workload
+    from workloads.synth import make_inputs
+
+    _lib.load()
+    w = workload(args.workload)
+    t0 = time.time()
+    x = make_inputs(w, seed=args.workload)
+    log(f"[bench] inputs of {w.name} generated in {time.time() - t0:.1f}s")
+    dev = torch.device("cuda:0")
+    q, k, v, a2v, do = (x[n].to(dev) for n in ("q", "k", "v", "a2v", "do"))
+    L = PrismLayer.for_workload(w, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is None:
+            L.forward(q, k, v, a2v)
+            L.backward(do)
+            return
+        L.zone_stats(v, a2v)
+        L.assign_shapes()
+        L.permute(q, L.qp, block_valid=L.bvalid)
+        L.permute(k, L.kp)
+        L.permute(v, L.vp)
+        ev["select0"].record(stream)
+        L.select()
+        ev["fwd0"].record(stream)
+        L.attn_fwd()
+        ev["fwd1"].record(stream)
+        L.permute(L.op, L.o, inverse=True)
+        g = L._grads()
+        L.permute(do, g["dop"])
+        L.attn_bwd(marks=ev["marks"])
+        L.permute(g["dqp"], g["dq"], inverse=True)
+        L.permute(g["dkp"], g["dk"], inverse=True)
+        L.permute(g["dvp"], g["dv"], inverse=True)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    # events for the kernels timed inside the region (one set per step)
+    def new_events():
+        e = {n: torch.cuda.Event(enable_timing=True) for n in ("select0", "fwd0", "fwd1")}
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for m in marks:
+            m.record(stream)                      # materialise the handles
+        e["marks"] = marks
+        return e
+
+    evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+    ms_step = 1e3 * t_total / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_step:.3f} ms/step")
+
+    t_select = sum(e["select0"].elapsed_time(e["fwd0"]) for e in evs) / len(evs)
+    t_fwd = sum(e["fwd0"].elapsed_time(e["fwd1"]) for e in evs) / len(evs)
+    t_pre = sum(e["marks"][0].elapsed_time(e["marks"][1]) for e in evs) / len(evs)
+    t_dkdv = sum(e["marks"][1].elapsed_time(e["marks"][2]) for e in evs) / len(evs)
+    t_dq = sum(e["marks"][2].elapsed_time(e["marks"][3]) for e in evs) / len(evs)
+
+    pairs = selected_pairs(L)
+    dens = density(L)
+    d = w.d
+    f_sel = 14.0 * d * pairs
+    value = f_sel / (ms_step * 1e-3) / 1e12
+    t_attn = t_fwd + t_pre + t_dkdv + t_dq
+    attn_tflops = f_sel / (t_attn * 1e-3) / 1e12
+
+    # dominant kernel: the one with the largest share of the step
+    kern = {"sparse_attn_fwd": (t_fwd, 4.0 * d * pairs), "sparse_attn_bwd_dkdv": (t_dkdv, 8.0 * d * pairs),
+            "sparse_attn_bwd_dq": (t_dq, 2.0 * d * pairs)}
+    dom = max(kern, key=lambda n: kern[n][0])
+    t_dom, flops_dom = kern[dom]
+    achieved = flops_dom / (t_dom * 1e-3) / 1e12
+
+    # per-stage breakdown from one extra instrumented pass (outside the timed region)
+    stage = {}
+    names = ["zone_stats", "assign_shapes", "permute_qkv", "select", "attn_fwd", "unpermute_o", "permute_do",
+             "attn_bwd", "unpermute_grads"]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    g = L._grads()
+    calls = [lambda: L.zone_stats(v, a2v), L.assign_shapes,
+             lambda: (L.permute(q, L.qp, block_valid=L.bvalid), L.permute(k, L.kp), L.permute(v, L.vp)),
+             L.select, L.attn_fwd, lambda: L.permute(L.op, L.o, inverse=True), lambda: L.permute(do, g["dop"]),
+             L.attn_bwd,
+             lambda: (L.permute(g["dqp"], g["dq"], inverse=True), L.permute(g["dkp"], g["dk"], inverse=True),
+                      L.permute(g["dvp"], g["dv"], inverse=True))]
+    ev[0].record(stream)
+    for i, c in enumerate(calls):
+        c()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    for i, n in enumerate(names):
+        stage[n] = round(ev[i].elapsed_time(ev[i + 1]), 4)
+
+    # dense comparator on the same (unpermuted) inputs
+    dense = None
+    if not args.no_dense:
+        o_d = torch.empty_like(q)
+        lse_d = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+        dq_d, dk_d, dv_d = (torch.empty_like(q) for _ in range(3))
+        ws = torch.empty(api.prism_dense_bwd_workspace_size(w.B, w.heads, w.N, w.d), dtype=torch.uint8, device=dev)
+        wsf = torch.empty(max(1, api.prism_dense_fwd_workspace_size(w.B, w.heads, w.N, w.d)), dtype=torch.uint8,
+                          device=dev)
+
+        def dense_step():
+            api.prism_dense_attn_fwd(q, k, v, L.scale, o_d, lse_d, wsf)
+            api.prism_dense_attn_bwd(q, k, v, o_d, do, lse_d, L.scale, dq_d, dk_d, dv_d, ws)
+
+        dense_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.dense_steps):
+            dense_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / args.dense_steps
+        dflops = 14.0 * d * w.N * w.N * w.B * w.heads
+        dense = dict(ms=round(dense_ms, 3), tflops=round(dflops / (dense_ms * 1e-3) / 1e12, 2),
+                     speedup=round(dense_ms / ms_step, 3))
+        log(f"[bench] dense comparator: {dense}")
+
+    res = dict(
+        metric="ms/layer & effective TFLOP/s, sparse attn fwd+bwd at 2K; speedup vs dense",
+        value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(ms_step, 3), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="bf16" if w.dtype == "bf16" else "f32", data="synthetic",
+        config=dict(workload=f"{w.name}: B={w.B}, {w.heads} heads, d={w.d}, grid {w.grid[0]}x{w.grid[1]}x{w.grid[2]} "
+                             f"({w.N} tokens), zone {w.zone[0]}x{w.zone[1]}x{w.zone[2]}, {len(w.cands)} shapes of "
+                             f"{w.vol} tokens, top-p {w.top_p}, top-k {w.k_min}..{w.k_max}",
+                    B=w.B, heads=w.heads, d=w.d, tokens=w.N, nb=L.nb, npad=L.Npad, density=round(dens, 4),
+                    selected_pairs=pairs),
+        ms_per_layer=round(ms_step, 3),
+        attn_tflops=round(attn_tflops, 3),
+        attn_ms=dict(fwd=round(t_fwd, 4), bwd_pre=round(t_pre, 4), bwd_dkdv=round(t_dkdv, 4), bwd_dq=round(t_dq, 4)),
+        select_ms=round(t_select, 4),
+        stage_ms=stage,
+        dense=dense,
+        speedup_vs_dense=None if dense is None else dense["speedup"],
+        roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 3), peak=MI355X_BF16_DENSE_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / MI355X_BF16_DENSE_TFLOPS, 5), traffic=None,
+                      avg_ms=round(t_dom, 4), flops_per_launch=flops_dom),
+    )
+    return res, (w, x)
+
+
+def cpu_baseline(w, x, budget_blocks: int):
+    """The oracle as it stands, on one head of the same inputs: the whole chain for that
+    head with the attention restricted to `budget_blocks` query blocks (forward, and
+    the full backward of exactly those blocks' selected pairs)."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import prism_oracle as O
+
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    h = 0
+    n = {k: t[:, h:h + 1].float().numpy().astype(np.float64) for k, t in x.items()}
+    t0 = time.perf_counter()
+    scale = 1.0 / math.sqrt(w.d)
+    stats = O.zone_stats(n["v"], n["a2v"], w.grid, w.zone)
+    sid, _ = O.assign_shapes(stats.astype(np.float32), list(w.cands), w.zone)
+    tok = O.slot_map(w.grid, w.zone, list(w.cands), sid)
+    bv = O.block_valid(tok, w.vol)
+    qp, kp, vp = O.permute(n["q"], tok), O.permute(n["k"], tok), O.permute(n["v"], tok)
+    qb, kb = O.pool_blocks(qp, bv, w.vol), O.pool_blocks(kp, bv, w.vol)
+    live = np.nonzero(bv[0, 0] > 0)[0]
+    rows = live[np.linspace(0, live.size - 1, budget_blocks).astype(int)]
+    sel, _ = O.select_blocks(qb.astype(np.float32), kb.astype(np.float32), bv, scale, w.top_p, w.k_min,
+                             w.k_max, rows=rows)
+    blocks = [(0, 0, int(I)) for I in rows]
+    op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, scale, w.vol, blocks=blocks)
+    dop = O.permute(n["do"], tok)
+    touched = sorted({(0, 0, int(J)) for s in sel.values() for J in s})
+    O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, scale, w.vol, q_blocks=blocks, k_blocks=touched)
+    dt = time.perf_counter() - t0
+    pairs = sum(int(bv[0, 0, I]) * int(bv[0, 0, s].sum()) for (_, _, I), s in sel.items())
+    flops = 14.0 * w.d * pairs
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                seconds=round(dt, 2),
+                sample=(f"head 0 of {w.name}: zone stats, shapes, permutation and pooling of the whole head, "
+                        f"selection, forward and backward of {budget_blocks} query blocks "
+                        f"({pairs} valid token pairs, 14*d flops each), float64 numpy"))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=4)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--dense-steps", type=int, default=1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-blocks", type=int, default=48)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: every Prism step is independent per head, so a multi-GPU "
+              "layer shards heads with no communication; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    res, (w, x) = run_gpu(args)
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle sample ...")
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_blocks)
+        log(f"[bench] cpu baseline: {res['cpu_baseline']}")
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -98,12 +98,24 @@ def prism_select_workspace_size(B: int, Hh: int, nb: int, d: int) -> int:
     return int(load().prism_select_workspace_size(B, Hh, nb, d))
 
 
-def prism_bwd_workspace_size(B: int, Hh: int, nb: int, vol: int) -> int:
-    return int(load().prism_bwd_workspace_size(B, Hh, nb, vol))
+def _dtc(dtype) -> int:
+    return PRISM_BF16 if dtype == torch.bfloat16 else PRISM_F32
 
 
-def prism_dense_bwd_workspace_size(B: int, Hh: int, N: int) -> int:
-    return int(load().prism_dense_bwd_workspace_size(B, Hh, N))
+def prism_fwd_workspace_size(B: int, Hh: int, nb: int, vol: int, d: int, dtype=torch.bfloat16) -> int:
+    return int(load().prism_fwd_workspace_size(B, Hh, nb, vol, d, _dtc(dtype)))
+
+
+def prism_bwd_workspace_size(B: int, Hh: int, nb: int, vol: int, d: int, dtype=torch.bfloat16) -> int:
+    return int(load().prism_bwd_workspace_size(B, Hh, nb, vol, d, _dtc(dtype)))
+
+
+def prism_dense_fwd_workspace_size(B: int, Hh: int, N: int, d: int, dtype=torch.bfloat16) -> int:
+    return int(load().prism_dense_fwd_workspace_size(B, Hh, N, d, _dtc(dtype)))
+
+
+def prism_dense_bwd_workspace_size(B: int, Hh: int, N: int, d: int, dtype=torch.bfloat16) -> int:
+    return int(load().prism_dense_bwd_workspace_size(B, Hh, N, d, _dtc(dtype)))
 
 
 def prism_last_error() -> str:
@@ -166,7 +178,7 @@ def prism_select_blocks(qp: torch.Tensor, kp: torch.Tensor, block_valid: torch.T
 
 
 def prism_sparse_attn_fwd(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, scale: float, op, lse,
-                          stream=None) -> None:
+                          workspace=None, stream=None) -> None:
     B, Hh, npad, d = qp.shape
     nb = npad // vol
     km = sel_idx.shape[-1]
@@ -176,7 +188,8 @@ def prism_sparse_attn_fwd(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, s
         _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"),
         _ptr(sel_idx, torch.int32, (B, Hh, nb, km), "sel_idx"), _ptr(sel_cnt, torch.int32, (B, Hh, nb), "sel_cnt"),
         km, B, Hh, nb, vol, d, float(scale), _ptr(op, shape=qp.shape, name="op"),
-        _ptr(lse, torch.float32, (B, Hh, npad), "lse"), _stream(stream)), "prism_sparse_attn_fwd")
+        _ptr(lse, torch.float32, (B, Hh, npad), "lse"), _ptr(workspace, torch.uint8, name="workspace"),
+        0 if workspace is None else workspace.numel(), _stream(stream)), "prism_sparse_attn_fwd")
 
 
 def prism_sparse_attn_bwd(qp, kp, vp, op, dop, lse, block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, vol: int,
@@ -198,13 +211,15 @@ def prism_sparse_attn_bwd(qp, kp, vp, op, dop, lse, block_valid, sel_idx, sel_cn
         mk, _stream(stream)), "prism_sparse_attn_bwd")
 
 
-def prism_dense_attn_fwd(q, k, v, scale: float, o, lse, stream=None) -> None:
+def prism_dense_attn_fwd(q, k, v, scale: float, o, lse, workspace=None, stream=None) -> None:
     B, Hh, N, d = q.shape
     dt = _same_dtype(q, k, v, o)
     check(load().prism_dense_attn_fwd(_ptr(q, name="q"), _ptr(k, shape=q.shape, name="k"),
                                       _ptr(v, shape=q.shape, name="v"), dt, B, Hh, N, d, float(scale),
                                       _ptr(o, shape=q.shape, name="o"), _ptr(lse, torch.float32, (B, Hh, N), "lse"),
-                                      _stream(stream)), "prism_dense_attn_fwd")
+                                      _ptr(workspace, torch.uint8, name="workspace"),
+                                      0 if workspace is None else workspace.numel(), _stream(stream)),
+          "prism_dense_attn_fwd")
 
 
 def prism_dense_attn_bwd(q, k, v, o, do, lse, scale: float, dq, dk, dv, workspace, marks=None, stream=None) -> None:

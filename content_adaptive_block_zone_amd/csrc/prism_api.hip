@@ -197,25 +197,46 @@ static prism_status check_attn_common(const char* who, prism_dtype dtype, int B,
   return PRISM_OK;
 }
 
+static AttnArgs sparse_args(int B, int Hh, int nb, int vol, int d, int k_max, float scale) {
+  AttnArgs a = {};
+  a.BH = B * Hh; a.nb = nb; a.vol = vol; a.k_max = k_max; a.nrows = nb * vol; a.d = d;
+  a.dense = 0; a.scale = scale;
+  return a;
+}
+
+static AttnArgs dense_args(int B, int Hh, int N, int d, float scale) {
+  AttnArgs a = {};
+  const int nb = (N + kTileRows - 1) / kTileRows;
+  a.BH = B * Hh; a.nb = nb; a.vol = kTileRows; a.k_max = nb; a.nrows = N; a.d = d;
+  a.dense = 1; a.scale = scale;
+  return a;
+}
+
+size_t prism_fwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype) {
+  if (B < 1 || Hh < 1 || nb < 1 || vol < 1 || !valid_dtype(dtype)) return 0;
+  return attn_fwd_ws_bytes(sparse_args(B, Hh, nb, vol, d, 1, 1.f), dtype);
+}
+
 prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
                                    const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
                                    int k_max, int B, int Hh, int nb, int vol, int d, float scale, void* op,
-                                   float* lse, hipStream_t stream) {
+                                   float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
   if (!qp || !kp || !vp || !block_valid || !sel_idx || !sel_cnt || !op || !lse)
     return fail(PRISM_ERR_ARG, "prism_sparse_attn_fwd: null pointer");
   prism_status st = check_attn_common("prism_sparse_attn_fwd", dtype, B, Hh, nb, vol, d, k_max, scale);
   if (st != PRISM_OK) return st;
-  AttnArgs a = {};
+  AttnArgs a = sparse_args(B, Hh, nb, vol, d, k_max, scale);
+  const size_t need = attn_fwd_ws_bytes(a, dtype);
+  if (ws_bytes < need || (need > 0 && !workspace))
+    return fail(PRISM_ERR_ARG, "prism_sparse_attn_fwd: workspace of %zu bytes < required %zu", ws_bytes, need);
   a.q = qp; a.k = kp; a.v = vp; a.out = op; a.lse_out = lse;
   a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt;
-  a.BH = B * Hh; a.nb = nb; a.vol = vol; a.k_max = k_max; a.nrows = nb * vol; a.d = d;
-  a.dense = 0; a.scale = scale;
-  return launched(launch_attn_fwd(a, dtype, stream), "prism_sparse_attn_fwd");
+  return launched(launch_attn_fwd(a, dtype, workspace, stream), "prism_sparse_attn_fwd");
 }
 
-size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol) {
-  if (B < 1 || Hh < 1 || nb < 1 || vol < 1) return 0;
-  return align256(size_t(B) * Hh * nb * vol * 4);
+size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype) {
+  if (B < 1 || Hh < 1 || nb < 1 || vol < 1 || !valid_dtype(dtype)) return 0;
+  return attn_bwd_ws_bytes(sparse_args(B, Hh, nb, vol, d, 1, 1.f), dtype);
 }
 
 prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* vp, const void* op, const void* dop,
@@ -229,36 +250,40 @@ prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* v
     return fail(PRISM_ERR_ARG, "prism_sparse_attn_bwd: null pointer");
   prism_status st = check_attn_common("prism_sparse_attn_bwd", dtype, B, Hh, nb, vol, d, k_max, scale);
   if (st != PRISM_OK) return st;
-  if (ws_bytes < prism_bwd_workspace_size(B, Hh, nb, vol))
-    return fail(PRISM_ERR_ARG, "prism_sparse_attn_bwd: workspace of %zu bytes < required %zu", ws_bytes,
-                prism_bwd_workspace_size(B, Hh, nb, vol));
-  AttnArgs a = {};
+  AttnArgs a = sparse_args(B, Hh, nb, vol, d, k_max, scale);
+  const size_t need = attn_bwd_ws_bytes(a, dtype);
+  if (ws_bytes < need)
+    return fail(PRISM_ERR_ARG, "prism_sparse_attn_bwd: workspace of %zu bytes < required %zu", ws_bytes, need);
   a.q = qp; a.k = kp; a.v = vp; a.o = op; a.dout = dop; a.lse_in = lse;
-  a.Dbuf = static_cast<float*>(workspace);
   a.dq = dqp; a.dk = dkp; a.dv = dvp;
   a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.rev_ptr = rev_ptr; a.rev_idx = rev_idx;
-  a.BH = B * Hh; a.nb = nb; a.vol = vol; a.k_max = k_max; a.nrows = nb * vol; a.d = d;
-  a.dense = 0; a.scale = scale;
-  return launched(launch_attn_bwd(a, dtype, marks, stream), "prism_sparse_attn_bwd");
+  return launched(launch_attn_bwd(a, dtype, workspace, marks, stream), "prism_sparse_attn_bwd");
+}
+
+size_t prism_dense_fwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype) {
+  if (B < 1 || Hh < 1 || N < 1 || !valid_dtype(dtype)) return 0;
+  return attn_fwd_ws_bytes(dense_args(B, Hh, N, d, 1.f), dtype);
 }
 
 prism_status prism_dense_attn_fwd(const void* q, const void* k, const void* v, prism_dtype dtype, int B, int Hh,
-                                  int N, int d, float scale, void* o, float* lse, hipStream_t stream) {
+                                  int N, int d, float scale, void* o, float* lse, void* workspace, size_t ws_bytes,
+                                  hipStream_t stream) {
   if (!q || !k || !v || !o || !lse) return fail(PRISM_ERR_ARG, "prism_dense_attn_fwd: null pointer");
   if (N < 1) return fail(PRISM_ERR_ARG, "prism_dense_attn_fwd: N must be >= 1");
   const int nb = (N + kTileRows - 1) / kTileRows;
   prism_status st = check_attn_common("prism_dense_attn_fwd", dtype, B, Hh, nb, kTileRows, d, 1, scale);
   if (st != PRISM_OK) return st;
-  AttnArgs a = {};
+  AttnArgs a = dense_args(B, Hh, N, d, scale);
+  const size_t need = attn_fwd_ws_bytes(a, dtype);
+  if (ws_bytes < need || (need > 0 && !workspace))
+    return fail(PRISM_ERR_ARG, "prism_dense_attn_fwd: workspace of %zu bytes < required %zu", ws_bytes, need);
   a.q = q; a.k = k; a.v = v; a.out = o; a.lse_out = lse;
-  a.BH = B * Hh; a.nb = nb; a.vol = kTileRows; a.k_max = nb; a.nrows = N; a.d = d;
-  a.dense = 1; a.scale = scale;
-  return launched(launch_attn_fwd(a, dtype, stream), "prism_dense_attn_fwd");
+  return launched(launch_attn_fwd(a, dtype, workspace, stream), "prism_dense_attn_fwd");
 }
 
-size_t prism_dense_bwd_workspace_size(int B, int Hh, int N) {
-  if (B < 1 || Hh < 1 || N < 1) return 0;
-  return align256(size_t(B) * Hh * N * 4);
+size_t prism_dense_bwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype) {
+  if (B < 1 || Hh < 1 || N < 1 || !valid_dtype(dtype)) return 0;
+  return attn_bwd_ws_bytes(dense_args(B, Hh, N, d, 1.f), dtype);
 }
 
 prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -271,15 +296,12 @@ prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, c
   const int nb = (N + kTileRows - 1) / kTileRows;
   prism_status st = check_attn_common("prism_dense_attn_bwd", dtype, B, Hh, nb, kTileRows, d, 1, scale);
   if (st != PRISM_OK) return st;
-  if (ws_bytes < prism_dense_bwd_workspace_size(B, Hh, N))
-    return fail(PRISM_ERR_ARG, "prism_dense_attn_bwd: workspace too small");
-  AttnArgs a = {};
+  AttnArgs a = dense_args(B, Hh, N, d, scale);
+  const size_t need = attn_bwd_ws_bytes(a, dtype);
+  if (ws_bytes < need) return fail(PRISM_ERR_ARG, "prism_dense_attn_bwd: workspace of %zu bytes < required %zu", ws_bytes, need);
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse_in = lse;
-  a.Dbuf = static_cast<float*>(workspace);
   a.dq = dq; a.dk = dk; a.dv = dv;
-  a.BH = B * Hh; a.nb = nb; a.vol = kTileRows; a.k_max = nb; a.nrows = N; a.d = d;
-  a.dense = 1; a.scale = scale;
-  return launched(launch_attn_bwd(a, dtype, marks, stream), "prism_dense_attn_bwd");
+  return launched(launch_attn_bwd(a, dtype, workspace, marks, stream), "prism_dense_attn_bwd");
 }
 
 }  // extern "C"

@@ -198,8 +198,13 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
                          int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
                          float* sel_margin, void* ws, hipStream_t s);
 size_t select_ws_bytes(int BH, int nb, int d);
-hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, hipStream_t s);
-hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, hipEvent_t* marks, hipStream_t s);
+// Attention: the bf16 / d=128 / 64-token path runs on MFMA kernels, everything else on the
+// scalar kernels.  The forward workspace holds a transposed copy of V; the backward one
+// holds D then transposed copies of Q, K and dO.
+size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
+size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
+hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);
+hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s);
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 

@@ -54,7 +54,8 @@ class PrismLayer:
         self.rev_ptr = e(B_, H_, self.nb + 1, dt=i32)
         self.rev_idx = e(B_, H_, self.nb * self.k_max, dt=i32)
         self.ws_sel = e(api.prism_select_workspace_size(B, Hh, self.nb, d), dt=torch.uint8)
-        self.ws_bwd = e(api.prism_bwd_workspace_size(B, Hh, self.nb, self.vol), dt=torch.uint8)
+        self.ws_fwd = e(max(1, api.prism_fwd_workspace_size(B, Hh, self.nb, self.vol, d, dtype)), dt=torch.uint8)
+        self.ws_bwd = e(api.prism_bwd_workspace_size(B, Hh, self.nb, self.vol, d, dtype), dt=torch.uint8)
         self.o = e(B_, H_, self.N, d)
         self._grad_bufs = None
 
@@ -84,7 +85,7 @@ class PrismLayer:
 
     def attn_fwd(self):
         api.prism_sparse_attn_fwd(self.qp, self.kp, self.vp, self.bvalid, self.sel_idx, self.sel_cnt,
-                                  self.vol, self.scale, self.op, self.lse)
+                                  self.vol, self.scale, self.op, self.lse, self.ws_fwd)
 
     def attn_bwd(self, marks=None):
         g = self._grads()

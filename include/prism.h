@@ -151,11 +151,15 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
  * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:
  *   O_i = softmax_j(scale q_i.k_j) v_j,  lse_i = ln sum_j exp(scale q_i.k_j).
  * op   out [B][Hh][nb*vol][d] (zeros at padding rows);  lse out float [B][Hh][nb*vol]
- * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}. */
+ * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}.  bf16 with vol = 64 and
+ * d = 128 runs on the matrix cores and needs prism_fwd_workspace_size() bytes of device
+ * scratch (a transposed copy of vp); other cases need none (workspace may be NULL). */
+size_t prism_fwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
                                    const int32_t* block_valid, const int32_t* sel_idx,
                                    const int32_t* sel_cnt, int k_max, int B, int Hh, int nb, int vol,
-                                   int d, float scale, void* op, float* lse, hipStream_t stream);
+                                   int d, float scale, void* op, float* lse, void* workspace,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* (a7) Block-sparse attention backward, selection held fixed.
  * With D_i = dO_i.O_i, P_ij = exp(scale q_i.k_j - lse_i), dS_ij = P_ij (dO_i.v_j - D_i):
@@ -164,8 +168,9 @@ prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* v
  * index; no atomics, results are deterministic.
  * marks    optional array of 4 caller-created hipEvents recorded on `stream` before the
  *          D kernel, after it, after the dK/dV kernel and after the dQ kernel.
- * workspace    device scratch of prism_bwd_workspace_size() bytes. */
-size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol);
+ * workspace    device scratch of prism_bwd_workspace_size() bytes (D, and on the matrix-core
+ *              path transposed copies of qp, kp and dop). */
+size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* vp, const void* op,
                                    const void* dop, const float* lse, prism_dtype dtype,
                                    const int32_t* block_valid, const int32_t* sel_idx,
@@ -177,10 +182,11 @@ prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* v
 /* Dense attention comparator on unpermuted [B][Hh][N][d] tensors (every key attended),
  * the same kernels run with every block selected; used to measure the sparse path's
  * speedup.  lse float [B][Hh][N].  Requires d in {64, 128}. */
+size_t prism_dense_fwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype);
 prism_status prism_dense_attn_fwd(const void* q, const void* k, const void* v, prism_dtype dtype,
                                   int B, int Hh, int N, int d, float scale, void* o, float* lse,
-                                  hipStream_t stream);
-size_t prism_dense_bwd_workspace_size(int B, int Hh, int N);
+                                  void* workspace, size_t ws_bytes, hipStream_t stream);
+size_t prism_dense_bwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype);
 prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                                   const void* dout, const float* lse, prism_dtype dtype, int B,
                                   int Hh, int N, int d, float scale, void* dq, void* dk, void* dv,

@@ -224,3 +224,64 @@ def test_determinism_bitwise():
         res.append([o] + g + [L.sel_idx.clone(), L.rev_idx.clone()])
     for a, b in zip(*res):
         assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("case", ["tiny-f32", "480p-2heads", "ragged-105"])
+def test_dense_comparator(case):
+    """The dense comparator (every key attended, unpermuted tokens, ragged last tile) against
+    the oracle's dense attention."""
+    from content_adaptive_block_zone_amd import api
+    rng = np.random.default_rng(5)
+    if case == "tiny-f32":
+        w, x = inputs(0)
+        q, k, v, do = (x[n] for n in ("q", "k", "v", "do"))
+        kind = "f32"
+    elif case == "480p-2heads":
+        w, x = inputs(1)
+        q, k, v, do = (x[n][:, :2].contiguous() for n in ("q", "k", "v", "do"))
+        kind = "bf16"
+    else:
+        shp = (1, 3, 105, 128)
+        q, k, v, do = (torch.from_numpy(rng.standard_normal(shp).astype(np.float32)).to(torch.bfloat16)
+                       for _ in range(4))
+        kind = "bf16"
+    B, Hh, N, d = q.shape
+    scale = 1.0 / np.sqrt(d)
+    gq, gk, gv, gdo = (t.cuda() for t in (q, k, v, do))
+    o = torch.empty_like(gq)
+    lse = torch.empty(B, Hh, N, dtype=torch.float32, device="cuda")
+    wsf = torch.empty(max(1, api.prism_dense_fwd_workspace_size(B, Hh, N, d, gq.dtype)), dtype=torch.uint8,
+                      device="cuda")
+    api.prism_dense_attn_fwd(gq, gk, gv, scale, o, lse, wsf)
+    dq, dk, dv = (torch.empty_like(gq) for _ in range(3))
+    ws = torch.empty(api.prism_dense_bwd_workspace_size(B, Hh, N, d, gq.dtype), dtype=torch.uint8, device="cuda")
+    api.prism_dense_attn_bwd(gq, gk, gv, o, gdo, lse, scale, dq, dk, dv, ws)
+    torch.cuda.synchronize()
+    nq, nk, nv, ndo = (f64(t) for t in (q, k, v, do))
+    wo, wl = O.dense_attn_fwd(nq, nk, nv, scale)
+    assert_close_out(f64(o), wo, kind, f"dense O {case}")
+    assert np.abs(f64(lse) - wl).max() <= TOL[kind]["lse_abs"]
+    g = O.dense_attn_bwd(nq, nk, nv, f64(o), ndo, f64(lse), scale)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), g):
+        assert_close_grad(f64(got), want, kind, f"dense {name} {case}")
+
+
+def test_all_blocks_selected_equals_dense():
+    """p = 1 with k_min = k_max = every block: the sparse path over permuted tokens gives
+    the dense result (480p-like workload, 2 heads, bf16)."""
+    from content_adaptive_block_zone_amd import api
+    from content_adaptive_block_zone_amd.pipeline import PrismLayer
+    w, x = inputs(1)
+    q, k, v, a2v, do = (x[n][:, :2].contiguous().cuda() for n in ("q", "k", "v", "a2v", "do"))
+    nb = O.num_zones(w.grid, w.zone) * 16
+    L = PrismLayer(w.B, 2, w.d, w.grid, w.zone, list(w.cands), 1.0, nb, nb)
+    o = L.forward(q, k, v, a2v).clone()
+    dq, dk, dv = (t.clone() for t in L.backward(do))
+    live = (L.bvalid > 0).sum(dim=-1)
+    assert (L.sel_cnt[L.bvalid > 0] == live.reshape(1, 2, 1).expand_as(L.sel_cnt)[L.bvalid > 0]).all()
+    nq, nk, nv, ndo = (f64(t) for t in (q, k, v, do))
+    wo, wl = O.dense_attn_fwd(nq, nk, nv, L.scale)
+    assert_close_out(f64(o), wo, "bf16", "all-selected O vs dense")
+    g = O.dense_attn_bwd(nq, nk, nv, wo, ndo, wl, L.scale)
+    for name, got, want in zip(("dQ", "dK", "dV"), (dq, dk, dv), g):
+        assert_close_grad(f64(got), want, "bf16", f"all-selected {name} vs dense")

@@ -116,7 +116,7 @@ WORKLOADS: List[Workload] = [
         field=FieldRecipe("zoned", M=8, f_lo=1 / 64, f_hi=1 / 16),
         blobs=BlobRecipe(n=3, sigma_lo=3.0, sigma_hi=6.0),
         top_p=0.85, k_min=32, k_max=512,
-        q_gain=1.0, density_target=(0.10, 0.15),
+        q_gain=0.8052, density_target=(0.10, 0.15),     # from oracle/calibrate_gain.py 3
     ),
     Workload(
         name="2k-like", B=1, heads=4, d=128, grid=(21, 90, 160), zone=(4, 16, 16),
@@ -124,7 +124,7 @@ WORKLOADS: List[Workload] = [
         field=FieldRecipe("zoned", M=8, f_lo=1 / 32, f_hi=1 / 8),
         blobs=BlobRecipe(n=3, sigma_lo=3.0, sigma_hi=6.0),
         top_p=0.85, k_min=32, k_max=768,
-        q_gain=1.0, density_target=(0.09, 0.11),
+        q_gain=1.5092, density_target=(0.09, 0.11),     # from oracle/calibrate_gain.py 4
     ),
 ]
 
