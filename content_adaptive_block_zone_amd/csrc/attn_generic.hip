@@ -281,31 +281,22 @@ hipError_t launch_attn_bwd_generic(const AttnArgs& a, prism_dtype dt, hipEvent_t
 }
 
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, void* ws, hipStream_t s);
-hipError_t launch_attn_bwd_mfma(const AttnArgs& a, void* ws, hipEvent_t* marks, hipStream_t s);
-size_t attn_mfma_ws_bytes(int BH, int nb, int copies);
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_bwd_mfma(const AttnArgs& a, hipEvent_t* marks, hipStream_t s);
 
-size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt) {
-  return attn_mfma_supported(a, dt) ? attn_mfma_ws_bytes(a.BH, a.nb, 1) : 0;
-}
+size_t attn_fwd_ws_bytes(const AttnArgs&, prism_dtype) { return 0; }
 
-size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt) {
-  const size_t dbuf = align256(size_t(a.BH) * a.nrows * 4);
-  return dbuf + (attn_mfma_supported(a, dt) ? attn_mfma_ws_bytes(a.BH, a.nb, 3) : 0);
-}
+size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype) { return align256(size_t(a.BH) * a.nrows * 4); }
 
-hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s) {
-  if (attn_mfma_supported(a, dt)) return launch_attn_fwd_mfma(a, ws, s);
+hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void*, hipStream_t s) {
+  if (attn_mfma_supported(a, dt)) return launch_attn_fwd_mfma(a, s);
   return launch_attn_fwd_generic(a, dt, s);
 }
 
 hipError_t launch_attn_bwd(const AttnArgs& a_in, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s) {
   AttnArgs a = a_in;
   a.Dbuf = static_cast<float*>(ws);
-  if (attn_mfma_supported(a, dt)) {
-    char* rest = static_cast<char*>(ws) + align256(size_t(a.BH) * a.nrows * 4);
-    return launch_attn_bwd_mfma(a, rest, marks, s);
-  }
+  if (attn_mfma_supported(a, dt)) return launch_attn_bwd_mfma(a, marks, s);
   return launch_attn_bwd_generic(a, dt, marks, s);
 }
 

@@ -199,8 +199,7 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
                          float* sel_margin, void* ws, hipStream_t s);
 size_t select_ws_bytes(int BH, int nb, int d);
 // Attention: the bf16 / d=128 / 64-token path runs on MFMA kernels, everything else on the
-// scalar kernels.  The forward workspace holds a transposed copy of V; the backward one
-// holds D then transposed copies of Q, K and dO.
+// scalar kernels.  The forward needs no scratch; the backward's holds D (one float per row).
 size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
 size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);

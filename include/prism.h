@@ -151,9 +151,9 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
  * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:
  *   O_i = softmax_j(scale q_i.k_j) v_j,  lse_i = ln sum_j exp(scale q_i.k_j).
  * op   out [B][Hh][nb*vol][d] (zeros at padding rows);  lse out float [B][Hh][nb*vol]
- * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}.  bf16 with vol = 64 and
- * d = 128 runs on the matrix cores and needs prism_fwd_workspace_size() bytes of device
- * scratch (a transposed copy of vp); other cases need none (workspace may be NULL). */
+ * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}; bf16 with vol = 64 and
+ * d = 128 runs on the matrix cores.  workspace: prism_fwd_workspace_size() bytes of device
+ * scratch (currently 0 for every case; workspace may then be NULL). */
 size_t prism_fwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
                                    const int32_t* block_valid, const int32_t* sel_idx,
@@ -168,8 +168,7 @@ prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* v
  * index; no atomics, results are deterministic.
  * marks    optional array of 4 caller-created hipEvents recorded on `stream` before the
  *          D kernel, after it, after the dK/dV kernel and after the dQ kernel.
- * workspace    device scratch of prism_bwd_workspace_size() bytes (D, and on the matrix-core
- *              path transposed copies of qp, kp and dop). */
+ * workspace    device scratch of prism_bwd_workspace_size() bytes (D = rowsum(dO*O) per row). */
 size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* vp, const void* op,
                                    const void* dop, const float* lse, prism_dtype dtype,

@@ -61,9 +61,8 @@ def test_host_helpers_reject_bad_geometry(lib):
     assert api.prism_num_blocks(api.make_grid((4, 8, 8), (2, 4, 8)), nofit) == -1
     assert api.prism_select_workspace_size(0, 1, 1, 64) == 0
     import torch
-    assert api.prism_fwd_workspace_size(1, 4, 5760, 64, 128, torch.bfloat16) >= 4 * 5760 * 64 * 128 * 2
     assert api.prism_fwd_workspace_size(1, 2, 16, 16, 64, torch.float32) == 0
-    assert api.prism_bwd_workspace_size(1, 4, 5760, 64, 128, torch.bfloat16) >= 3 * 4 * 5760 * 64 * 128 * 2
+    assert api.prism_bwd_workspace_size(1, 4, 5760, 64, 128, torch.bfloat16) >= 4 * 5760 * 64 * 4
 
 
 def _status(fn, *args):
@@ -112,8 +111,6 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_SHAPE),
         ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 0, 1, 2, 16, 16, 64, 0.125, P, P, None, 0, None),
          E.PRISM_ERR_ARG),
-        ("prism_sparse_attn_fwd", (P, P, P, BF16, P, P, P, 8, 1, 2, 16, 64, 128, 0.125, P, P, None, 0, None),
-         E.PRISM_ERR_ARG),                                                             # matrix-core path needs scratch
         ("prism_sparse_attn_bwd", (P, P, P, P, P, P, F32, P, P, P, 8, P, P, 1, 2, 16, 16, 64, 0.125, P, P, P,
                                    P, 8, None, None), E.PRISM_ERR_ARG),
         ("prism_dense_attn_fwd", (P, P, P, F32, 1, 2, 0, 64, 0.125, P, P, None, 0, None), E.PRISM_ERR_ARG),
