@@ -35,14 +35,32 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def selected_pairs(L):
-    """Sum over heads and query blocks of n_I * sum_{J in sel(I)} n_J (valid token pairs)."""
+def selection_sums(L):
+    """Sums over heads of the selection, all in valid token rows:
+    tok_pairs = sum_I n_I * sum_{J in sel(I)} n_J      (valid (query, key) token pairs)
+    key_rows  = sum_I sum_{J in sel(I)} n_J            (key rows streamed, query-major kernels)
+    qry_rows  = sum_I cnt_I * n_I                      (query rows streamed, key-major kernel)
+    rows      = sum_I n_I                              (valid rows)"""
     import torch
     idx = L.sel_idx.long()                                           # [B, Hh, nb, k_max]
     bv = L.bvalid.long()                                             # [B, Hh, nb]
     nJ = torch.gather(bv, 2, idx.clamp(min=0).reshape(L.B, L.Hh, -1)).reshape(idx.shape)
-    keys = (nJ * (idx >= 0)).sum(dim=-1)
-    return int((keys * bv).sum().item())
+    keys = (nJ * (idx >= 0)).sum(dim=-1)                             # [B, Hh, nb]
+    return dict(tok_pairs=int((keys * bv).sum().item()), key_rows=int(keys.sum().item()),
+                qry_rows=int((L.sel_cnt.long() * bv).sum().item()), rows=int(bv.sum().item()),
+                block_pairs=int(L.sel_cnt.long().sum().item()))
+
+
+def kernel_bytes(sums, d):
+    """Algorithmic HBM bytes of one launch of each attention kernel (bf16 tensors, fp32 LSE/D):
+    every selected pair streams the valid rows of the other block's two tiles once; each owner
+    block reads its own tiles and writes its outputs once."""
+    e = 2
+    return {
+        "sparse_attn_fwd": sums["key_rows"] * 2 * d * e + sums["rows"] * (2 * d * e + 4),
+        "sparse_attn_bwd_dkdv": sums["qry_rows"] * (2 * d * e + 8) + sums["rows"] * 4 * d * e,
+        "sparse_attn_bwd_dq": sums["key_rows"] * 2 * d * e + sums["rows"] * (3 * d * e + 8),
+    }
 
 
 def density(L):
@@ -123,7 +141,8 @@ def run_gpu(args):
     t_dkdv = sum(e["marks"][1].elapsed_time(e["marks"][2]) for e in evs) / len(evs)
     t_dq = sum(e["marks"][2].elapsed_time(e["marks"][3]) for e in evs) / len(evs)
 
-    pairs = selected_pairs(L)
+    sums = selection_sums(L)
+    pairs = sums["tok_pairs"]
     dens = density(L)
     d = w.d
     f_sel = 14.0 * d * pairs
@@ -131,12 +150,16 @@ def run_gpu(args):
     t_attn = t_fwd + t_pre + t_dkdv + t_dq
     attn_tflops = f_sel / (t_attn * 1e-3) / 1e12
 
-    # dominant kernel: the one with the largest share of the step
-    kern = {"sparse_attn_fwd": (t_fwd, 4.0 * d * pairs), "sparse_attn_bwd_dkdv": (t_dkdv, 8.0 * d * pairs),
-            "sparse_attn_bwd_dq": (t_dq, 2.0 * d * pairs)}
-    dom = max(kern, key=lambda n: kern[n][0])
-    t_dom, flops_dom = kern[dom]
-    achieved = flops_dom / (t_dom * 1e-3) / 1e12
+    # dominant kernel: the one with the largest share of the step.  At about 64 flop per
+    # streamed byte these kernels sit far below MI355X's ridge point (2.5 PFLOP/s / 8 TB/s
+    # = 312 flop/B), so their roofline is HBM bandwidth on algorithmic bytes.
+    kb = kernel_bytes(sums, d)
+    kern = {"sparse_attn_fwd": t_fwd, "sparse_attn_bwd_dkdv": t_dkdv, "sparse_attn_bwd_dq": t_dq}
+    dom = max(kern, key=lambda n: kern[n])
+    t_dom = kern[dom]
+    achieved = kb[dom] / (t_dom * 1e-3) / 1e9
+    kflops = {"sparse_attn_fwd": 4.0 * d * pairs, "sparse_attn_bwd_dkdv": 8.0 * d * pairs,
+              "sparse_attn_bwd_dq": 2.0 * d * pairs}
 
     # per-stage breakdown from one extra instrumented pass (outside the timed region)
     stage = {}
@@ -195,7 +218,7 @@ def run_gpu(args):
                              f"({w.N} tokens), zone {w.zone[0]}x{w.zone[1]}x{w.zone[2]}, {len(w.cands)} shapes of "
                              f"{w.vol} tokens, top-p {w.top_p}, top-k {w.k_min}..{w.k_max}",
                     B=w.B, heads=w.heads, d=w.d, tokens=w.N, nb=L.nb, npad=L.Npad, density=round(dens, 4),
-                    selected_pairs=pairs),
+                    selected_token_pairs=pairs, selected_block_pairs=sums["block_pairs"]),
         ms_per_layer=round(ms_step, 3),
         attn_tflops=round(attn_tflops, 3),
         attn_ms=dict(fwd=round(t_fwd, 4), bwd_pre=round(t_pre, 4), bwd_dkdv=round(t_dkdv, 4), bwd_dq=round(t_dq, 4)),
@@ -203,9 +226,13 @@ def run_gpu(args):
         stage_ms=stage,
         dense=dense,
         speedup_vs_dense=None if dense is None else dense["speedup"],
-        roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 3), peak=MI355X_BF16_DENSE_TFLOPS,
-                      unit="TFLOP/s", frac=round(achieved / MI355X_BF16_DENSE_TFLOPS, 5), traffic=None,
-                      avg_ms=round(t_dom, 4), flops_per_launch=flops_dom),
+        roofline=dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=MI355X_HBM_GBPS, unit="GB/s",
+                      frac=round(achieved / MI355X_HBM_GBPS, 4), traffic=None, avg_ms=round(t_dom, 4),
+                      bytes_per_launch=kb[dom],
+                      mfma_tflops=round(kflops[dom] / (t_dom * 1e-3) / 1e12, 2),
+                      mfma_frac=round(kflops[dom] / (t_dom * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4)),
+        kernels={n: dict(ms=round(kern[n], 4), gbps=round(kb[n] / (kern[n] * 1e-3) / 1e9, 1),
+                         frac_hbm=round(kb[n] / (kern[n] * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4)) for n in kern},
     )
     return res, (w, x)
 

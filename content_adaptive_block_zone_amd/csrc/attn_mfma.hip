@@ -101,6 +101,50 @@ __device__ __forceinline__ size_t row0_of(const AttnArgs& a, int bh, int I) {
   return size_t(bh) * a.nrows + size_t(I) * TR;
 }
 
+// Owner block of a workgroup: blocks in order within a head, heads in order, so that the
+// heads' K/V pass through the 256 MB last-level cache one at a time.  (Remapping the grid
+// so that each XCD works through a contiguous run of blocks measured slower on the 2K
+// workload, both with heads interleaved and with heads kept in order.)
+__device__ __forceinline__ void owner_of(const AttnArgs& a, int& I, int& bh) {
+  I = blockIdx.x % a.nb;
+  bh = blockIdx.x / a.nb;
+}
+
+// The streamed block list of a workgroup, with each block's valid-row count, is copied to
+// LDS once (packed as J | n << 16), so that finding the next block to prefetch costs an
+// LDS read instead of two dependent global loads.  Lists longer than kMetaCap (or block
+// indices past 16 bits) fall back to reading global memory per step.
+constexpr int kMetaCap = 2048;
+struct BlockList {
+  const int32_t* lst;  // nullptr in dense mode (block k is k)
+  int cnt;
+  bool in_lds;
+};
+__device__ __forceinline__ BlockList load_list(const AttnArgs& a, int bh, const int32_t* lst, int cnt, int* meta) {
+  BlockList L{lst, cnt, !a.dense && cnt <= kMetaCap && a.nb < 65536};
+  if (L.in_lds)
+    for (int k = threadIdx.x; k < cnt; k += NT) {
+      const int J = lst[k];
+      meta[k] = J | (nrows_of(a, bh, J) << 16);
+    }
+  __syncthreads();
+  return L;
+}
+__device__ __forceinline__ void list_at(const AttnArgs& a, int bh, const BlockList& L, const int* meta, int k, int& J,
+                                        int& n) {
+  if (a.dense) {
+    J = k;
+    n = min(TR, a.nrows - k * TR);
+  } else if (L.in_lds) {
+    const int m = meta[k];
+    J = m & 0xffff;
+    n = m >> 16;
+  } else {
+    J = L.lst[k];
+    n = nrows_of(a, bh, J);
+  }
+}
+
 // ---- staging: a 64x128 bf16 tile = 1024 chunks of 16 bytes, 4 per thread.  Thread t
 // fetches rows 4*(t/16)+i (i = 0..3) of column chunk 8*(t%16): every load instruction of a
 // wave reads whole 256-byte rows, and the thread holds the 4 consecutive rows of each of its
@@ -153,7 +197,8 @@ __device__ __forceinline__ V ldt8(const uint16_t* tt, int c, int g) {
 __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[TR * LP];
   __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LPT];
-  const int I = blockIdx.x, bh = blockIdx.y;
+  int I, bh;
+  owner_of(a, I, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, G = lane >> 4;
   const int nI = nrows_of(a, bh, I);
   const size_t q0 = row0_of(a, bh, I);
@@ -161,8 +206,9 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   const bf16_t* K = static_cast<const bf16_t*>(a.k);
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   bf16_t* O = static_cast<bf16_t*>(a.out);
+  __shared__ int sMeta[kMetaCap];
   const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
-  const int32_t* lst = a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max;
+  const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
   const int qrow = 16 * w + l16;
   const bool qok = qrow < nI;
 
@@ -178,8 +224,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   Chunks ck, cv;
   int J = 0, nJ = 0;
   if (cnt > 0) {
-    J = a.dense ? 0 : lst[0];
-    nJ = nrows_of(a, bh, J);
+    list_at(a, bh, bl, sMeta, 0, J, nJ);
     fetch(ck, K + row0_of(a, bh, J) * D, nJ);
     fetch(cv, V + row0_of(a, bh, J) * D, nJ);
   }
@@ -190,8 +235,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
     __syncthreads();
     const int nJc = nJ;
     if (it + 1 < cnt) {
-      J = a.dense ? it + 1 : lst[it + 1];
-      nJ = nrows_of(a, bh, J);
+      list_at(a, bh, bl, sMeta, it + 1, J, nJ);
       fetch(ck, K + row0_of(a, bh, J) * D, nJ);
       fetch(cv, V + row0_of(a, bh, J) * D, nJ);
     }
@@ -260,7 +304,8 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[TR * LP];
   __shared__ __attribute__((aligned(16))) uint16_t sV[TR * LP];
   __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LPT];
-  const int I = blockIdx.x, bh = blockIdx.y;
+  int I, bh;
+  owner_of(a, I, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, G = lane >> 4;
   const int nI = nrows_of(a, bh, I);
   const size_t q0 = row0_of(a, bh, I);
@@ -269,8 +314,9 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   const bf16_t* Gd = static_cast<const bf16_t*>(a.dout);
   bf16_t* dQ = static_cast<bf16_t*>(a.dq);
+  __shared__ int sMeta[kMetaCap];
   const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
-  const int32_t* lst = a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max;
+  const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
   const int qrow = 16 * w + l16;
   const bool qok = qrow < nI;
 
@@ -290,8 +336,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
   Chunks ck, cv;
   int J = 0, nJ = 0;
   if (cnt > 0) {
-    J = a.dense ? 0 : lst[0];
-    nJ = nrows_of(a, bh, J);
+    list_at(a, bh, bl, sMeta, 0, J, nJ);
     fetch(ck, K + row0_of(a, bh, J) * D, nJ);
     fetch(cv, V + row0_of(a, bh, J) * D, nJ);
   }
@@ -303,8 +348,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
     __syncthreads();
     const int nJc = nJ;
     if (it + 1 < cnt) {
-      J = a.dense ? it + 1 : lst[it + 1];
-      nJ = nrows_of(a, bh, J);
+      list_at(a, bh, bl, sMeta, it + 1, J, nJ);
       fetch(ck, K + row0_of(a, bh, J) * D, nJ);
       fetch(cv, V + row0_of(a, bh, J) * D, nJ);
     }
@@ -353,7 +397,8 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sQt[D * LPT];
   __shared__ __attribute__((aligned(16))) uint16_t sGt[D * LPT];
   __shared__ float sL[TR], sD[TR];
-  const int J = blockIdx.x, bh = blockIdx.y;
+  int J, bh;
+  owner_of(a, J, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, G = lane >> 4;
   const int nJ = nrows_of(a, bh, J);
   const size_t k0 = row0_of(a, bh, J);
@@ -363,6 +408,7 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
   const bf16_t* Gd = static_cast<const bf16_t*>(a.dout);
   bf16_t* dK = static_cast<bf16_t*>(a.dk);
   bf16_t* dV = static_cast<bf16_t*>(a.dv);
+  __shared__ int sMeta[kMetaCap];
   int cnt = 0;
   const int32_t* lst = nullptr;
   if (a.dense) {
@@ -372,6 +418,7 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
     cnt = rp[J + 1] - rp[J];
     lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rp[J];
   }
+  const BlockList bl = load_list(a, bh, lst, cnt, sMeta);
   const int key = 16 * w + l16;
   const bool kok = key < nJ;
   bf16x8 kf[4], vf[4];
@@ -388,19 +435,24 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
   }
   const float sl2 = a.scale * LOG2E;
 
+  // LSE and D of the prefetched query block are loaded raw (row index clamped into the
+  // block) and masked only when staged, so that no arithmetic waits on the prefetch.
   Chunks cq, cg;
   float pl = 0.f, pd = 0.f;
-  if (cnt > 0) {
-    const int I = a.dense ? 0 : lst[0];
-    const int nI = nrows_of(a, bh, I);
+  int nIn = 0;
+  auto fetch_q = [&](int k) {
+    int I;
+    list_at(a, bh, bl, sMeta, k, I, nIn);
     const size_t q0 = row0_of(a, bh, I);
-    fetch(cq, Q + q0 * D, nI);
-    fetch(cg, Gd + q0 * D, nI);
+    fetch(cq, Q + q0 * D, nIn);
+    fetch(cg, Gd + q0 * D, nIn);
     if (tid < TR) {
-      pl = tid < nI ? a.lse_in[q0 + tid] * LOG2E : INFINITY;
-      pd = tid < nI ? a.Dbuf[q0 + tid] : 0.f;
+      const size_t r = q0 + min(tid, nIn - 1);
+      pl = a.lse_in[r];
+      pd = a.Dbuf[r];
     }
-  }
+  };
+  if (cnt > 0) fetch_q(0);
   for (int it = 0; it < cnt; ++it) {
     __syncthreads();
     put_rows(cq, sQ);
@@ -408,21 +460,11 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
     put_cols<false>(cq, sQt);
     put_cols<false>(cg, sGt);
     if (tid < TR) {
-      sL[tid] = pl;
-      sD[tid] = pd;
+      sL[tid] = tid < nIn ? pl * LOG2E : INFINITY;
+      sD[tid] = tid < nIn ? pd : 0.f;
     }
     __syncthreads();
-    if (it + 1 < cnt) {
-      const int I = a.dense ? it + 1 : lst[it + 1];
-      const int nI = nrows_of(a, bh, I);
-      const size_t q0 = row0_of(a, bh, I);
-      fetch(cq, Q + q0 * D, nI);
-      fetch(cg, Gd + q0 * D, nI);
-      if (tid < TR) {
-        pl = tid < nI ? a.lse_in[q0 + tid] * LOG2E : INFINITY;
-        pd = tid < nI ? a.Dbuf[q0 + tid] : 0.f;
-      }
-    }
+    if (it + 1 < cnt) fetch_q(it + 1);
     // S, dP tiles qt: rows = queries 16qt + 4G + i, column = this lane's key
     f32x4 s_[4], dp[4];
 #pragma unroll
@@ -489,7 +531,7 @@ int attn_mfma_supported(const AttnArgs& a, prism_dtype dt) {
 }
 
 hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL(k_fwd, dim3(a.nb, a.BH), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(k_fwd, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -498,9 +540,9 @@ hipError_t launch_attn_bwd_mfma(const AttnArgs& a, hipEvent_t* marks, hipStream_
   const size_t rows = size_t(a.BH) * a.nrows;
   hipLaunchKernelGGL(k_bwd_pre_bf16, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, s, a, rows);
   if (marks) (void)hipEventRecord(marks[1], s);
-  hipLaunchKernelGGL(k_dkdv, dim3(a.nb, a.BH), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(k_dkdv, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   if (marks) (void)hipEventRecord(marks[2], s);
-  hipLaunchKernelGGL(k_dq, dim3(a.nb, a.BH), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(k_dq, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   if (marks) (void)hipEventRecord(marks[3], s);
   return hipGetLastError();
 }
