@@ -621,7 +621,15 @@ def sparse_attn_bwd(qp, kp, vp, op, dop, lse, bvalid, sel: Dict, scale: float, v
         q = rows(qp, b, h, I)
         P, dS = grads_of_rows(q, rows(dop, b, h, I), rows(op, b, h, I), rows(lse, b, h, I), k, v)
         dQ[b, h, I * vol: I * vol + q.shape[0]] = scale * (dS @ k)
-    cols = _transpose_selection(sel)
+    if k_blocks is None:
+        cols = _transpose_selection(sel)
+    else:  # only the requested key blocks: which query blocks list J (lists are ascending)
+        def lists(s, J):
+            i = int(np.searchsorted(s, J))
+            return i < len(s) and s[i] == J
+        empty = np.zeros(0, dtype=np.int32)
+        cols = {(b, h, J): np.array([I for I in range(nb) if lists(sel.get((b, h, I), empty), J)], dtype=np.int32)
+                for (b, h, J) in k_blocks}
     for (b, h, J) in (allq if k_blocks is None else k_blocks):
         Is = [int(I) for I in cols.get((b, h, J), ()) if bvalid[b, h, I] > 0]
         m = int(bvalid[b, h, J])
