@@ -646,23 +646,25 @@ def sparse_attn_bwd(qp, kp, vp, op, dop, lse, bvalid, sel: Dict, scale: float, v
 def dense_attn_fwd(q, k, v, scale: float):
     """Full softmax attention on unpermuted tokens, float64: O [B,Hh,N,C], LSE [B,Hh,N]."""
     q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
-    s = np.einsum("bhic,bhjc->bhij", q, k) * scale
+    T = lambda x: np.swapaxes(x, -1, -2)  # noqa: E731
+    s = (q @ T(k)) * scale
     m = s.max(axis=-1, keepdims=True)
     e = np.exp(s - m)
     z = e.sum(axis=-1, keepdims=True)
-    return np.einsum("bhij,bhjc->bhic", e / z, v), (m + np.log(z))[..., 0]
+    return (e / z) @ v, (m + np.log(z))[..., 0]
 
 
 def dense_attn_bwd(q, k, v, o, do, lse, scale: float):
     """Gradients of full softmax attention, float64 (same formulas as sparse_attn_bwd
     with every key selected)."""
     q, k, v, o, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, o, do))
-    P = np.exp(np.einsum("bhic,bhjc->bhij", q, k) * scale - lse[..., None])
+    T = lambda x: np.swapaxes(x, -1, -2)  # noqa: E731
+    P = np.exp((q @ T(k)) * scale - lse[..., None])
     D = (do * o).sum(axis=-1)[..., None]
-    dS = P * (np.einsum("bhic,bhjc->bhij", do, v) - D)
-    dq = scale * np.einsum("bhij,bhjc->bhic", dS, k)
-    dk = scale * np.einsum("bhij,bhic->bhjc", dS, q)
-    dv = np.einsum("bhij,bhic->bhjc", P, do)
+    dS = P * ((do @ T(v)) - D)
+    dq = scale * (dS @ k)
+    dk = scale * (T(dS) @ q)
+    dv = T(P) @ do
     return dq, dk, dv
 
 
