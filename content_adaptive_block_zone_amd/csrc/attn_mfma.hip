@@ -4,22 +4,25 @@
 // Shape of the work.  Every (query block, key block) pair costs 2 MFLOP per product but
 // needs a whole 64x128 tile pair from memory, and the key lists of neighbouring query
 // blocks barely overlap, so these kernels are bound by how fast tiles arrive, not by the
-// matrix cores.  The design therefore spends registers on occupancy and prefetch and reads
-// each streamed tile from memory exactly once per pair:
+// matrix cores.  The design therefore spends registers on occupancy and prefetch and
+// reads each streamed tile from memory exactly once per pair:
 //   * a workgroup of 4 wavefronts owns one 64-row block (the query block in the forward
-//     and dQ kernels, the key block in the dK/dV kernel); wave w owns rows 16w..16w+15;
+//     and dQ kernels, the key block in the dK/dV kernel);
 //   * the streamed block (K/V, or Q/dO) is staged in LDS once per pair and shared by the
 //     four waves; the next pair's tiles are fetched into registers while the current one
-//     is computed;
-//   * v_mfma_f32_16x16x32 {bf16, f16}: operand A = 16 rows x 32 k (lane l: row l%16,
-//     k = 8(l/16)..+7), B likewise with columns, C = 4 registers, lane l register i at
-//     row 4(l/16)+i, column l%16.
+//     is computed.
+// Forward: wave w owns rows 16w..16w+15 and uses v_mfma_f32_16x16x32 {bf16, f16}
+// (A = 16 rows x 32 k, lane l: row l%16, k = 8(l/16)..+7; B likewise with columns;
+// C = 4 registers, lane l register i at row 4(l/16)+i, column l%16).
+// Backward: the waves split the 64x64 pair 2x2 and use v_mfma_f32_32x32x16_bf16, which
+// does twice the work per LDS operand byte; the dQ waves sum their two key halves once at
+// the end, the dK/dV waves swap P and dS halves through LDS each pair.
 // Products whose contraction runs over the streamed block's rows (P V, Q^T dS, dO^T P,
-// K^T dS) take the owner's accumulator registers directly as the B operand: the four
-// registers of two consecutive 16-row tiles are the 8 k-values of one lane.  The matching
-// A operand is a transposed tile that the staging writes into LDS with its rows in that
-// same order ("kappa16": within each 32-row group, position 8G+e holds row
-// 4G + e%4 + 16*(e/4)), so that operand is one 16-byte LDS read as well.
+// K^T dS) take accumulator registers directly as the B operand.  The matching A operand
+// is a transposed tile that the staging writes into LDS with its rows in the order of
+// those registers ("kappa16" for the 16x16 tiles, "kappa32" for the 32x32 tiles; see
+// tpos and tpos32), so that operand is one 16-byte LDS read as well.  kappa16: within
+// each 32-row group, position 8G+e holds row 4G + e%4 + 16*(e/4).
 // The forward's P V product runs in fp16 (probabilities in [0, 1] keep 11 bits; bf16 V
 // values are exact in fp16 within its range), the rest in bf16; all accumulation is fp32.
 #include "prism_internal.h"
@@ -193,6 +196,46 @@ __device__ __forceinline__ V ldt8(const uint16_t* tt, int c, int g) {
   return lds8<V>(tt + c * LPT + (((g ^ (c >> 4)) & 7) << 3));
 }
 
+// ---- 32x32x16 products (backward kernels).  A = 32 rows x 16 k (lane l: row l%32,
+// k = 8(l/32)..+7), B likewise with columns, C = 16 registers: lane l register e at row
+// 8(e/4) + 4(l/32) + e%4, column l%32.  Registers 8s..8s+7 of an accumulator are the B
+// operand of a product contracting over its rows when the A operand lists those rows in
+// "kappa32" order: position p of each 16-row group holds row p with bits 2 and 3 swapped.
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) z[e] = 0.f;
+  return z;
+}
+__device__ __forceinline__ int acc_row32(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
+__device__ __forceinline__ int tpos32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
+__device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[8 * s + e];
+  return r;
+}
+// transposed copy in kappa32 order: tt[c][tpos32(r)]
+__device__ __forceinline__ void put_cols32(const Chunks& c, uint16_t* tt) {
+  const int rq = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;
+  const int p0 = tpos32(4 * rq);  // rows 4rq..4rq+3 sit at p0..p0+3
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = (c.v[i][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
+    *reinterpret_cast<u32x2*>(tt + tswz(c8 + j, p0)) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  }
+}
+// rows 8j+4g .. +3 of column `col` of a 32x32 accumulator tile, times s, as 4 bf16
+__device__ __forceinline__ void store4_32(bf16_t* p, const f32x16& c, int j, float s) {
+  *reinterpret_cast<u32x2*>(p) = u32x2{pk2(c[4 * j] * s, c[4 * j + 1] * s), pk2(c[4 * j + 2] * s, c[4 * j + 3] * s)};
+}
+
 // ------------------------------------------------------------------ forward
 __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[TR * LP];
@@ -296,17 +339,21 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ dQ
-// Owner: query block I (wave w: query rows 16w..).  Streamed: K and V of each selected
-// key block (K row-major for S^T = K Q^T, V row-major for dP^T = V dO^T, K transposed for
-// dQ^T = K^T dS^T).
-__global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[TR * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[TR * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t sKt[D * LPT];
+// ------------------------------------------------------------------ dQ (32x32x16)
+// Owner: query block I.  Wave w = (qh = w&1, kh = w>>1) handles queries 32qh.. against
+// keys 32kh.. of every streamed key block and accumulates a partial dQ^T over its key
+// half; the two halves are summed through LDS at the end.
+__global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
+  constexpr int B_K = TR * LP * 2, B_KT = D * LPT * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * B_K + B_KT];
+  __shared__ int sMeta[kMetaCap];
+  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + B_K);
+  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + 2 * B_K);
   int I, bh;
   owner_of(a, I, bh);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, G = lane >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int qh = w & 1, kh = w >> 1;
   const int nI = nrows_of(a, bh, I);
   const size_t q0 = row0_of(a, bh, I);
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
@@ -314,23 +361,21 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   const bf16_t* Gd = static_cast<const bf16_t*>(a.dout);
   bf16_t* dQ = static_cast<bf16_t*>(a.dq);
-  __shared__ int sMeta[kMetaCap];
   const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
   const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
-  const int qrow = 16 * w + l16;
+  const int qrow = 32 * qh + l32;
   const bool qok = qrow < nI;
-
-  bf16x8 qf[4], gf[4];
+  bf16x8 qf[8], gf[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    qf[s] = gld8(Q + (q0 + qrow) * D + 32 * s + 8 * G, qok);
-    gf[s] = gld8(Gd + (q0 + qrow) * D + 32 * s + 8 * G, qok);
+  for (int s = 0; s < 8; ++s) {
+    qf[s] = gld8(Q + (q0 + qrow) * D + 16 * s + 8 * g, qok);
+    gf[s] = gld8(Gd + (q0 + qrow) * D + 16 * s + 8 * g, qok);
   }
   const float lse2 = qok ? a.lse_in[q0 + qrow] * LOG2E : INFINITY;
   const float Dq = qok ? a.Dbuf[q0 + qrow] : 0.f;
-  f32x4 dq[8];
+  f32x16 dq[4];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) dq[t] = zero4();
+  for (int t = 0; t < 4; ++t) dq[t] = zero16();
   const float sl2 = a.scale * LOG2E;
 
   Chunks ck, cv;
@@ -344,7 +389,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
     __syncthreads();
     put_rows(ck, sK);
     put_rows(cv, sV);
-    put_cols<false>(ck, sKt);
+    put_cols32(ck, sKt);
     __syncthreads();
     const int nJc = nJ;
     if (it + 1 < cnt) {
@@ -352,63 +397,75 @@ __global__ __launch_bounds__(NT, 2) void k_dq(AttnArgs a) {
       fetch(ck, K + row0_of(a, bh, J) * D, nJ);
       fetch(cv, V + row0_of(a, bh, J) * D, nJ);
     }
-    f32x4 st[4], dp[4];
+    // S^T, dP^T: rows = keys 32kh + acc_row32(e, g), column = query qrow
+    f32x16 st = zero16(), dp = zero16();
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      st[kt] = zero4();
-      dp[kt] = zero4();
+    for (int s = 0; s < 8; ++s) {
+      st = mma32(lds8<bf16x8>(sK + (32 * kh + l32) * LP + 16 * s + 8 * g), qf[s], st);
+      dp = mma32(lds8<bf16x8>(sV + (32 * kh + l32) * LP + 16 * s + 8 * g), gf[s], dp);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int e = 0; e < 16; ++e) {
+      const bool ok = 32 * kh + acc_row32(e, g) < nJc;
+      const float p = ok ? exp2f(st[e] * sl2 - lse2) : 0.f;
+      dp[e] = p * (dp[e] - Dq);
+    }
+    const bf16x8 s0 = pack8(dp, 0), s1 = pack8(dp, 1);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        st[kt] = mma(lds8<bf16x8>(sK + (16 * kt + l16) * LP + 32 * s + 8 * G), qf[s], st[kt]);
-        dp[kt] = mma(lds8<bf16x8>(sV + (16 * kt + l16) * LP + 32 * s + 8 * G), gf[s], dp[kt]);
-      }
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = 16 * kt + 4 * G + i < nJc;
-        const float p = ok ? exp2f(st[kt][i] * sl2 - lse2) : 0.f;
-        dp[kt][i] = p * (dp[kt][i] - Dq);
-      }
-    const bf16x8 s0 = pack_bf16(dp[0], dp[1]), s1 = pack_bf16(dp[2], dp[3]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      dq[t] = mma(ldt8<bf16x8>(sKt, 16 * t + l16, G), s0, dq[t]);
-      dq[t] = mma(ldt8<bf16x8>(sKt, 16 * t + l16, 4 + G), s1, dq[t]);
+    for (int t = 0; t < 4; ++t) {
+      dq[t] = mma32(ldt8<bf16x8>(sKt, 32 * t + l32, 4 * kh + g), s0, dq[t]);
+      dq[t] = mma32(ldt8<bf16x8>(sKt, 32 * t + l32, 4 * kh + 2 + g), s1, dq[t]);
     }
   }
-  if (qok || (!a.dense && qrow < TR)) {
+  // sum the two key halves: waves with kh = 1 hand their partials to kh = 0 through LDS
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + qh * (4 * 16 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(t * 16 + e) * 64 + lane] = dq[t][e];
+  }
+  __syncthreads();
+  if (kh == 0 && (qok || (!a.dense && qrow < TR))) {
     const float sc = qok ? a.scale : 0.f;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) store4(dQ + (q0 + qrow) * D + 16 * t + 4 * G, dq[t], sc);
+    for (int t = 0; t < 4; ++t) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dq[t][e] += red[(t * 16 + e) * 64 + lane];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store4_32(dQ + (q0 + qrow) * D + 32 * t + 8 * j + 4 * g, dq[t], j, sc);
+    }
   }
 }
 
-// ------------------------------------------------------------------ dK / dV
-// Owner: key block J (wave w: key rows 16w..).  Streamed: Q and dO of each query block
-// that selected J (reverse index), row-major for S = Q K^T and dP = dO V^T, transposed
-// for dK^T = Q^T dS and dV^T = dO^T P.
-__global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sQ[TR * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t sG[TR * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t sQt[D * LPT];
-  __shared__ __attribute__((aligned(16))) uint16_t sGt[D * LPT];
+// ------------------------------------------------------------------ dK / dV (32x32x16)
+// Owner: key block J.  Wave w = (kh = w&1, x = w>>1): keys 32kh.. of the owner block,
+// queries 32x.. of each streamed query block for S and dP.  Wave (kh, 0) accumulates dV^T
+// and wave (kh, 1) dK^T of those 32 keys over all 64 queries: after the softmax step the
+// pair swaps halves through LDS (x = 0 hands over its dS, x = 1 its P), so neither keeps a
+// partial sum of the other's output and no reduction is left for the end.
+__global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
+  constexpr int B_Q = TR * LP * 2, B_QT = D * LPT * 2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * B_Q + 2 * B_QT];
   __shared__ float sL[TR], sD[TR];
+  __shared__ int sMeta[kMetaCap];
+  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);
+  uint16_t* sG = reinterpret_cast<uint16_t*>(smem + B_Q);
+  uint16_t* sQt = reinterpret_cast<uint16_t*>(smem + 2 * B_Q);
+  uint16_t* sGt = reinterpret_cast<uint16_t*>(smem + 2 * B_Q + B_QT);
+  // swap area (2 KB per wave) over sQ, which is dead once S and dP are formed
+  bf16x8* xbuf = reinterpret_cast<bf16x8*>(smem);
   int J, bh;
   owner_of(a, J, bh);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, G = lane >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int kh = w & 1, x = w >> 1;
   const int nJ = nrows_of(a, bh, J);
   const size_t k0 = row0_of(a, bh, J);
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   const bf16_t* K = static_cast<const bf16_t*>(a.k);
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   const bf16_t* Gd = static_cast<const bf16_t*>(a.dout);
-  bf16_t* dK = static_cast<bf16_t*>(a.dk);
-  bf16_t* dV = static_cast<bf16_t*>(a.dv);
-  __shared__ int sMeta[kMetaCap];
   int cnt = 0;
   const int32_t* lst = nullptr;
   if (a.dense) {
@@ -419,92 +476,97 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv(AttnArgs a) {
     lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rp[J];
   }
   const BlockList bl = load_list(a, bh, lst, cnt, sMeta);
-  const int key = 16 * w + l16;
+  const int key = 32 * kh + l32;
   const bool kok = key < nJ;
-  bf16x8 kf[4], vf[4];
+  bf16x8 kf[8], vf[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    kf[s] = gld8(K + (k0 + key) * D + 32 * s + 8 * G, kok);
-    vf[s] = gld8(V + (k0 + key) * D + 32 * s + 8 * G, kok);
+  for (int s = 0; s < 8; ++s) {
+    kf[s] = gld8(K + (k0 + key) * D + 16 * s + 8 * g, kok);
+    vf[s] = gld8(V + (k0 + key) * D + 16 * s + 8 * g, kok);
   }
-  f32x4 dk[8], dv[8];
+  f32x16 acc[4];  // x = 0: dV^T, x = 1: dK^T (rows d = 32t + acc_row32, column key)
 #pragma unroll
-  for (int t = 0; t < 8; ++t) {
-    dk[t] = zero4();
-    dv[t] = zero4();
-  }
+  for (int t = 0; t < 4; ++t) acc[t] = zero16();
   const float sl2 = a.scale * LOG2E;
+  const uint16_t* At = x == 0 ? sGt : sQt;  // dO^T for dV, Q^T for dK
 
-  // LSE and D of the prefetched query block are loaded raw (row index clamped into the
-  // block) and masked only when staged, so that no arithmetic waits on the prefetch.
+  // The next query block's Q (with its LSE and D) is fetched right after the barrier and
+  // its dO after the swap, so that the two staging sets are never live together with the
+  // S and dP accumulators.
   Chunks cq, cg;
   float pl = 0.f, pd = 0.f;
   int nIn = 0;
+  size_t qn = 0;
   auto fetch_q = [&](int k) {
-    int I;
-    list_at(a, bh, bl, sMeta, k, I, nIn);
-    const size_t q0 = row0_of(a, bh, I);
-    fetch(cq, Q + q0 * D, nIn);
-    fetch(cg, Gd + q0 * D, nIn);
+    int Ib;
+    list_at(a, bh, bl, sMeta, k, Ib, nIn);
+    qn = row0_of(a, bh, Ib);
+    fetch(cq, Q + qn * D, nIn);
     if (tid < TR) {
-      const size_t r = q0 + min(tid, nIn - 1);
+      const size_t r = qn + min(tid, nIn - 1);
       pl = a.lse_in[r];
       pd = a.Dbuf[r];
     }
   };
-  if (cnt > 0) fetch_q(0);
+  if (cnt > 0) {
+    fetch_q(0);
+    fetch(cg, Gd + qn * D, nIn);
+  }
   for (int it = 0; it < cnt; ++it) {
     __syncthreads();
     put_rows(cq, sQ);
     put_rows(cg, sG);
-    put_cols<false>(cq, sQt);
-    put_cols<false>(cg, sGt);
+    put_cols32(cq, sQt);
+    put_cols32(cg, sGt);
     if (tid < TR) {
       sL[tid] = tid < nIn ? pl * LOG2E : INFINITY;
       sD[tid] = tid < nIn ? pd : 0.f;
     }
     __syncthreads();
-    if (it + 1 < cnt) fetch_q(it + 1);
-    // S, dP tiles qt: rows = queries 16qt + 4G + i, column = this lane's key
-    f32x4 s_[4], dp[4];
+    const bool more = it + 1 < cnt;
+    if (more) fetch_q(it + 1);
+    // S, dP: rows = queries 32x + acc_row32(e, g), column = key
+    f32x16 s_ = zero16(), dp = zero16();
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
-      s_[qt] = zero4();
-      dp[qt] = zero4();
+    for (int s = 0; s < 8; ++s) {
+      s_ = mma32(lds8<bf16x8>(sQ + (32 * x + l32) * LP + 16 * s + 8 * g), kf[s], s_);
+      dp = mma32(lds8<bf16x8>(sG + (32 * x + l32) * LP + 16 * s + 8 * g), vf[s], dp);
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int e = 0; e < 16; ++e) {
+      const int r = 32 * x + acc_row32(e, g);
+      const float p = exp2f(s_[e] * sl2 - sL[r]);
+      s_[e] = p;
+      dp[e] = p * (dp[e] - sD[r]);
+    }
+    // own: the operand this wave keeps; give: the one its partner (w ^ 2) needs
+    const bf16x8 P0 = pack8(s_, 0), P1 = pack8(s_, 1), S0 = pack8(dp, 0), S1 = pack8(dp, 1);
+    const bf16x8 own0 = x == 0 ? P0 : S0, own1 = x == 0 ? P1 : S1;
+    const bf16x8 give0 = x == 0 ? S0 : P0, give1 = x == 0 ? S1 : P1;
+    __syncthreads();  // every wave is done with sQ
+    xbuf[w * 128 + lane] = give0;
+    xbuf[w * 128 + 64 + lane] = give1;
+    __syncthreads();
+    const bf16x8 got0 = xbuf[(w ^ 2) * 128 + lane], got1 = xbuf[(w ^ 2) * 128 + 64 + lane];
+    // query half 0 comes from wave x = 0, half 1 from x = 1
+    const bf16x8 lo0 = x == 0 ? own0 : got0, lo1 = x == 0 ? own1 : got1;
+    const bf16x8 hi0 = x == 0 ? got0 : own0, hi1 = x == 0 ? got1 : own1;
+    if (more) fetch(cg, Gd + qn * D, nIn);
 #pragma unroll
-      for (int qt = 0; qt < 4; ++qt) {
-        s_[qt] = mma(lds8<bf16x8>(sQ + (16 * qt + l16) * LP + 32 * s + 8 * G), kf[s], s_[qt]);
-        dp[qt] = mma(lds8<bf16x8>(sG + (16 * qt + l16) * LP + 32 * s + 8 * G), vf[s], dp[qt]);
-      }
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * qt + 4 * G + i;
-        const float p = exp2f(s_[qt][i] * sl2 - sL[r]);
-        s_[qt][i] = p;
-        dp[qt][i] = p * (dp[qt][i] - sD[r]);
-      }
-    const bf16x8 p0 = pack_bf16(s_[0], s_[1]), p1 = pack_bf16(s_[2], s_[3]);
-    const bf16x8 d0 = pack_bf16(dp[0], dp[1]), d1 = pack_bf16(dp[2], dp[3]);
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      dv[t] = mma(ldt8<bf16x8>(sGt, 16 * t + l16, G), p0, dv[t]);
-      dv[t] = mma(ldt8<bf16x8>(sGt, 16 * t + l16, 4 + G), p1, dv[t]);
-      dk[t] = mma(ldt8<bf16x8>(sQt, 16 * t + l16, G), d0, dk[t]);
-      dk[t] = mma(ldt8<bf16x8>(sQt, 16 * t + l16, 4 + G), d1, dk[t]);
+    for (int t = 0; t < 4; ++t) {
+      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, g), lo0, acc[t]);
+      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, 2 + g), lo1, acc[t]);
+      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, 4 + g), hi0, acc[t]);
+      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, 6 + g), hi1, acc[t]);
     }
   }
   if (kok || (!a.dense && key < TR)) {
-    const float sk = kok ? a.scale : 0.f, sv = kok ? 1.f : 0.f;
+    const float sc = kok ? (x == 1 ? a.scale : 1.f) : 0.f;
+    bf16_t* out = static_cast<bf16_t*>(x == 1 ? a.dk : a.dv);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      store4(dK + (k0 + key) * D + 16 * t + 4 * G, dk[t], sk);
-      store4(dV + (k0 + key) * D + 16 * t + 4 * G, dv[t], sv);
-    }
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store4_32(out + (k0 + key) * D + 32 * t + 8 * j + 4 * g, acc[t], j, sc);
   }
 }
 
@@ -540,9 +602,9 @@ hipError_t launch_attn_bwd_mfma(const AttnArgs& a, hipEvent_t* marks, hipStream_
   const size_t rows = size_t(a.BH) * a.nrows;
   hipLaunchKernelGGL(k_bwd_pre_bf16, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, s, a, rows);
   if (marks) (void)hipEventRecord(marks[1], s);
-  hipLaunchKernelGGL(k_dkdv, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(k_dkdv32, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   if (marks) (void)hipEventRecord(marks[2], s);
-  hipLaunchKernelGGL(k_dq, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
+  hipLaunchKernelGGL(k_dq32, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   if (marks) (void)hipEventRecord(marks[3], s);
   return hipGetLastError();
 }
