@@ -63,6 +63,101 @@ def kernel_bytes(sums, d):
     }
 
 
+# kernel (bench name) -> symbol of its HIP kernel
+KERNEL_SYMBOL = {"sparse_attn_fwd": "k_fwd", "sparse_attn_bwd_dkdv": "k_dkdv32", "sparse_attn_bwd_dq": "k_dq32"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernels_2k_like_traffic.txt")
+# Counter calibration: one elementwise pass y = -x over 256 MiB of fp32 (reads and writes
+# 256 MiB each); FETCH_SIZE and WRITE_SIZE are scaled by what they report for it.
+COPY_MIB = 256
+
+
+def attn_source_sha256():
+    """Hash of the attention kernels' source: recorded counter traffic is reported only
+    while the kernels are the ones it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("attn_mfma.hip", "prism_internal.h"):
+        with open(os.path.join(ROOT, "content_adaptive_block_zone_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    sha, traffic = None, {}
+    for line in open(TRAFFIC_FILE):
+        f = line.split()
+        if len(f) == 2 and f[0] == "source_sha256":
+            sha = f[1]
+        elif len(f) == 3 and f[0] == "traffic_bytes_per_launch":
+            traffic[f[1]] = int(f[2])
+    if sha != attn_source_sha256():
+        return None
+    return traffic.get(kernel)
+
+
+def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
+    """Text summary of a `rocprofv3 --kernel-trace --stats` run of the benchmark and of its
+    FETCH_SIZE / WRITE_SIZE counter runs, with the traffic per launch of each attention
+    kernel scaled by what the counters read for the plain copy (written to stdout)."""
+    import csv
+    import glob
+    lines = ["# Commands (run from the repository root on one MI355X)"]
+    lines += [f"#   {c}" for c in commands]
+    lines.append("")
+    st = glob.glob(os.path.join(stats_dir, "*kernel_stats.csv"))[0]
+    lines.append("## Kernel time (rocprofv3 --kernel-trace --stats)")
+    lines.append(f"{'kernel':44s} {'calls':>6s} {'avg ms':>10s} {'total %':>8s}")
+    import re
+    for r in csv.DictReader(open(st)):
+        m = re.search(r"::(k_\w+)", r["Name"])
+        n = m.group(1) if m else r["Name"][:44]
+        lines.append(f"{n:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:10.4f} {float(r['Percentage']):8.2f}")
+    lines.append("")
+    per = {}
+    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        f = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        acc = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != cname:
+                continue
+            m = re.search(r"::(k_\w+)", r["Kernel_Name"])
+            n = m.group(1) if m else ("neg_kernel (calibration)" if "neg_kernel" in r["Kernel_Name"]
+                                      else r["Kernel_Name"][:44])
+            a = acc.setdefault(n, [0.0, set()])
+            a[0] += float(r["Counter_Value"])
+            a[1].add(r["Dispatch_Id"])
+        per[cname] = {n: v[0] / len(v[1]) for n, v in acc.items()}   # KiB per dispatch
+    copy = [n for n in per["FETCH_SIZE"] if n == "neg_kernel (calibration)"]
+    if len(copy) != 1:
+        raise SystemExit("no calibration pass in the counter runs (run the benchmark with --copy-mib 256)")
+    cn = copy[0]
+    ref_kib = COPY_MIB * 1024.0
+    sf = ref_kib / per["FETCH_SIZE"][cn]
+    sw = ref_kib / per["WRITE_SIZE"][cn]
+    lines.append("## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)")
+    lines.append(f"calibration: {cn} of {COPY_MIB} MiB reads FETCH_SIZE {per['FETCH_SIZE'][cn]:.0f} KiB and "
+                 f"WRITE_SIZE {per['WRITE_SIZE'][cn]:.0f} KiB per dispatch -> scale fetch x{sf:.3f}, write x{sw:.3f}")
+    lines.append(f"{'kernel':44s} {'FETCH KiB':>14s} {'WRITE KiB':>12s} {'scaled GB':>10s}")
+    for n in sorted(per["FETCH_SIZE"]):
+        if not n.startswith("k_"):
+            continue
+        fk, wk = per["FETCH_SIZE"][n], per["WRITE_SIZE"].get(n, 0.0)
+        tb = (fk * sf + wk * sw) * 1024.0
+        lines.append(f"{n:44s} {fk:14.0f} {wk:12.0f} {tb / 1e9:10.3f}")
+    lines.append("")
+    lines.append("## Machine-readable (read by bench.py for roofline.traffic)")
+    lines.append(f"source_sha256 {attn_source_sha256()}")
+    for bench_name, sym in KERNEL_SYMBOL.items():
+        if sym in per["FETCH_SIZE"]:
+            tb = (per["FETCH_SIZE"][sym] * sf + per["WRITE_SIZE"].get(sym, 0.0) * sw) * 1024.0
+            lines.append(f"traffic_bytes_per_launch {bench_name} {int(round(tb))}")
+    print("\n".join(lines))
+
+
 def density(L):
     import torch
     live = (L.bvalid > 0).sum(dim=-1).double()                      # [B, Hh]
@@ -115,6 +210,15 @@ def run_gpu(args):
         step()
         torch.cuda.synchronize()
         log(f"[bench] warmup step {i + 1}/{args.warmup} done")
+
+    if args.copy_mib:
+        # one plain elementwise pass of known size (y = -x): the counter runs scale
+        # FETCH_SIZE and WRITE_SIZE by what they read for it
+        src = torch.ones(args.copy_mib * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # events for the kernels timed inside the region (one set per step)
     def new_events():
@@ -227,7 +331,7 @@ def run_gpu(args):
         dense=dense,
         speedup_vs_dense=None if dense is None else dense["speedup"],
         roofline=dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=MI355X_HBM_GBPS, unit="GB/s",
-                      frac=round(achieved / MI355X_HBM_GBPS, 4), traffic=None, avg_ms=round(t_dom, 4),
+                      frac=round(achieved / MI355X_HBM_GBPS, 4), traffic=recorded_traffic(dom), avg_ms=round(t_dom, 4),
                       bytes_per_launch=kb[dom],
                       mfma_tflops=round(kflops[dom] / (t_dom * 1e-3) / 1e12, 2),
                       mfma_frac=round(kflops[dom] / (t_dom * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4)),
@@ -286,8 +390,17 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=48)
+    ap.add_argument("--cpu-blocks", type=int, default=400)
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one elementwise pass y = -x over this many MiB after warm-up (counter calibration)")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="print a text summary of rocprofv3 output directories and exit (no GPU)")
+    ap.add_argument("--profile-command", action="append", default=[],
+                    help="command line recorded in the summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile, args.profile_command)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every Prism step is independent per head, so a multi-GPU "
               "layer shards heads with no communication; run it with --gpus 1.", file=sys.stderr)
