@@ -119,7 +119,7 @@ def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
     lines.append("")
     per = {}
     for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        f = glob.glob(os.path.join(d, "*counter_collection.csv"))[0]
+        f = glob.glob(os.path.join(d, "*counter_collection*.csv"))[0]
         acc = {}
         for r in csv.DictReader(open(f)):
             if r["Counter_Name"] != cname:

@@ -49,18 +49,66 @@ __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t val) {
     p[i] = val;
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ qp, const T* __restrict__ kp,
-                                              const int32_t* __restrict__ bvalid, int nb, int vol, int d,
-                                              float* __restrict__ qbar, float* __restrict__ kbar) {
+// One workgroup per (block, head, tensor): D/8 lanes cover a row in 16-byte (bf16) or
+// 32-byte (fp32) chunks and the row groups take rows rg, rg + NT/G, ..., four rows per
+// step with their loads issued together; per-channel sums are reduced across the row
+// groups of a wavefront with lane shuffles, then across wavefronts in LDS.
+template <typename T, int D>
+__global__ __launch_bounds__(NT) void k_pool(const T* __restrict__ qp, const T* __restrict__ kp,
+                                             const int32_t* __restrict__ bvalid, int nb, int vol,
+                                             float* __restrict__ qbar, float* __restrict__ kbar) {
+  constexpr int G = D / 8;       // lanes per row
+  constexpr int RG = NT / G;     // row groups
+  constexpr int U = 4;           // rows per step
+  __shared__ float s_red[NT / 64][D];
   const int I = blockIdx.x, bh = blockIdx.y;
-  const T* x = (blockIdx.z == 0 ? qp : kp) + (size_t(bh) * nb + I) * vol * d;
-  float* out = (blockIdx.z == 0 ? qbar : kbar) + (size_t(bh) * nb + I) * d;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, cg = tid % G, rg = tid / G;
+  const T* x = (blockIdx.z == 0 ? qp : kp) + (size_t(bh) * nb + I) * vol * D + cg * 8;
+  float* out = (blockIdx.z == 0 ? qbar : kbar) + (size_t(bh) * nb + I) * D;
   const int n = bvalid[size_t(bh) * nb + I];
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    float s = 0.f;
-    for (int r = 0; r < n; ++r) s += to_f32(x[size_t(r) * d + c]);
-    out[c] = n > 0 ? s / float(n) : 0.f;
+  float acc[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  // rows past the valid count reread the last valid row and count zero times, so the
+  // loads of a step are unconditional and stay in flight together
+  for (int r0 = rg; r0 < n; r0 += U * RG) {
+    float v[U][8];
+#pragma unroll
+    for (int j = 0; j < U; ++j) load8(x + size_t(min(r0 + j * RG, n - 1)) * D, v[j]);
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float m = r0 + j * RG < n ? 1.f : 0.f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(v[j][k], m, acc[k]);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    float t = acc[k];
+#pragma unroll
+    for (int o = G; o < 64; o <<= 1) t += __shfl_xor(t, o, 64);
+    if (lane < G) s_red[wv][cg * 8 + k] = t;
+  }
+  __syncthreads();
+  for (int c = tid; c < D; c += NT) {
+    float t = 0.f;
+#pragma unroll
+    for (int w = 0; w < NT / 64; ++w) t += s_red[w][c];
+    out[c] = n > 0 ? t / float(n) : 0.f;
+  }
+}
+
+template <typename T>
+void launch_pool(const void* qp, const void* kp, const int32_t* bvalid, int BH, int nb, int vol, int d,
+                 float* qbar, float* kbar, hipStream_t s) {
+  const T* q = static_cast<const T*>(qp);
+  const T* k = static_cast<const T*>(kp);
+  const dim3 grid(nb, BH, 2);
+  switch (d) {
+    case 32: hipLaunchKernelGGL((k_pool<T, 32>), grid, dim3(NT), 0, s, q, k, bvalid, nb, vol, qbar, kbar); break;
+    case 64: hipLaunchKernelGGL((k_pool<T, 64>), grid, dim3(NT), 0, s, q, k, bvalid, nb, vol, qbar, kbar); break;
+    case 128: hipLaunchKernelGGL((k_pool<T, 128>), grid, dim3(NT), 0, s, q, k, bvalid, nb, vol, qbar, kbar); break;
+    default: hipLaunchKernelGGL((k_pool<T, 256>), grid, dim3(NT), 0, s, q, k, bvalid, nb, vol, qbar, kbar); break;
   }
 }
 
@@ -356,15 +404,11 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
   hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, w.bitmap, nbits, 0u);
   hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(rev_idx),
                      size_t(BH) * nb * p.k_max, 0xffffffffu);
-  const int pool_threads = d < 256 ? d : 256;
+  // d is one of 32, 64, 128, 256 (checked by the caller)
   if (dt == PRISM_BF16)
-    hipLaunchKernelGGL(k_pool<bf16_t>, dim3(nb, BH, 2), dim3(pool_threads), 0, s,
-                       static_cast<const bf16_t*>(qp), static_cast<const bf16_t*>(kp), bvalid, nb, vol, d,
-                       w.qbar, w.kbar);
+    launch_pool<bf16_t>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
   else
-    hipLaunchKernelGGL(k_pool<float>, dim3(nb, BH, 2), dim3(pool_threads), 0, s,
-                       static_cast<const float*>(qp), static_cast<const float*>(kp), bvalid, nb, vol, d,
-                       w.qbar, w.kbar);
+    launch_pool<float>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
   const int tiles = (nb + 63) / 64;
   hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, w.qbar, w.kbar, nb, d, scale, w.scores);
   hipLaunchKernelGGL(k_select, dim3(nb, BH), dim3(NT), size_t(nb) * 4, s, w.scores, bvalid, nb, p, p.k_max,

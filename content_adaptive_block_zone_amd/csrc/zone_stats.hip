@@ -4,28 +4,34 @@
 //
 // One workgroup per (batch*head, zone).  The zone is streamed row by row: a group of
 // D/8 lanes owns one (t, h) row of the zone and walks it along w, each lane holding 8
-// channels.  Increments along w stay in registers; the neighbour rows along h and t are
-// read again (they hit L2, HBM traffic stays one pass over V and the A2V output).  The
+// channels, four tokens per step with all their loads issued together (the kernel is
+// bound by memory latency, so the loads in flight per lane matter more than anything
+// else).  Increments along w stay in registers; the neighbour rows along h and t are read
+// again, close enough in time to hit in cache, so HBM traffic stays near one pass over V
+// and the A2V output.  The
 // per-token A2V norm goes to a zone-local LDS map, from which the audio increments are
-// taken after the streaming pass.
+// taken after the streaming pass.  Per-channel sums are reduced across the row groups of
+// a wavefront with lane shuffles, then across the four wavefronts in LDS.
 #include "prism_internal.h"
 
 namespace prism {
 namespace {
 
 constexpr int NT = 256;
+constexpr int NWAVE = NT / 64;
 
 template <typename T, int D>
 __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, const T* __restrict__ a2v,
                                                    float* __restrict__ stats, Geo g) {
   constexpr int G = D / 8;      // lanes per token
   constexpr int RPP = NT / G;   // rows in flight per pass
+  constexpr int U = 4;          // tokens along w per step
   __shared__ float s_a[kMaxZoneVol];
-  __shared__ float s_red[RPP * 3 * 8 * G];  // == 3 * 8 * NT
+  __shared__ float s_red[NWAVE][3][D];
   __shared__ float s_share[3][D];
   __shared__ float s_tmp[8];
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int z = blockIdx.x % g.nZ;
   const int bh = blockIdx.x / g.nZ;
   const int iw = z % g.nzw, ih = (z / g.nzw) % g.nzh, it = z / (g.nzw * g.nzh);
@@ -41,48 +47,55 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
 #pragma unroll
     for (int k = 0; k < 8; ++k) ssd[a][k] = 0.f;
 
+  // rows are numbered t-fastest, so the row groups of one pass read each other's t- and
+  // h-neighbour rows at about the same time and the rereads hit in cache
   for (int row = rg; row < et * eh; row += RPP) {
-    const int lt = row / eh, lh = row % eh;
+    const int lt = row % et, lh = row / et;
     const size_t off = base + (size_t((t0 + lt) * g.H + h0 + lh) * g.W + w0) * D + cg * 8;
     const T* vr = v + off;
     const T* ar = a2v + off;
     const bool has_t = lt + 1 < et, has_h = lh + 1 < eh;
+    // A neighbour row that does not exist is replaced by the row itself, and a token past
+    // the zone's end by the last one: their increments are exactly zero (the ragged tail
+    // is also multiplied by 0), so every load and update is unconditional and the loads
+    // of a step stay in flight together.
+    const size_t dh = has_h ? row_stride_h : 0, dt = has_t ? row_stride_t : 0;
     float prev[8];
-    for (int lw = 0; lw < ew; ++lw) {
-      float x[8], y[8], u[8];
-      load8(vr + size_t(lw) * D, x);
-      if (lw > 0) {
+    for (int lw0 = 0; lw0 < ew; lw0 += U) {
+      float x[U][8], yh[U][8], yt[U][8], u[U][8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float dd = x[k] - prev[k];
-          ssd[2][k] = fmaf(dd, dd, ssd[2][k]);
-        }
+      for (int j = 0; j < U; ++j) {
+        const size_t o = size_t(min(lw0 + j, ew - 1)) * D;
+        load8(vr + o, x[j]);
+        load8(vr + o + dh, yh[j]);
+        load8(vr + o + dt, yt[j]);
+        load8(ar + o, u[j]);
       }
-      if (has_h) {
-        load8(vr + size_t(lw) * D + row_stride_h, y);
+      if (lw0 == 0) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float dd = x[k] - y[k];
-          ssd[1][k] = fmaf(dd, dd, ssd[1][k]);
-        }
-      }
-      if (has_t) {
-        load8(vr + size_t(lw) * D + row_stride_t, y);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float dd = x[k] - y[k];
-          ssd[0][k] = fmaf(dd, dd, ssd[0][k]);
-        }
+        for (int k = 0; k < 8; ++k) prev[k] = x[0][k];
       }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) prev[k] = x[k];
-      load8(ar + size_t(lw) * D, u);
-      float sq = 0.f;
+      for (int j = 0; j < U; ++j) {
+        const int lw = lw0 + j;
+        const float m = lw < ew ? 1.f : 0.f;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) sq = fmaf(u[k], u[k], sq);
+        for (int k = 0; k < 8; ++k) {
+          const float dw = x[j][k] - prev[k];
+          const float dhh = (x[j][k] - yh[j][k]) * m;
+          const float dtt = (x[j][k] - yt[j][k]) * m;
+          ssd[2][k] = fmaf(dw, dw, ssd[2][k]);
+          ssd[1][k] = fmaf(dhh, dhh, ssd[1][k]);
+          ssd[0][k] = fmaf(dtt, dtt, ssd[0][k]);
+          prev[k] = x[j][k];
+        }
+        float sq = 0.f;
 #pragma unroll
-      for (int o = G / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-      if (cg == 0) s_a[(lt * g.zh + lh) * g.zw + lw] = sqrtf(sq);
+        for (int k = 0; k < 8; ++k) sq = fmaf(u[j][k], u[j][k], sq);
+#pragma unroll
+        for (int o = G / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+        if (cg == 0 && lw < ew) s_a[(lt * g.zh + lh) * g.zw + lw] = sqrtf(sq);
+      }
     }
   }
 
@@ -90,7 +103,12 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
 #pragma unroll
   for (int a = 0; a < 3; ++a)
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s_red[(rg * 3 + a) * D + cg * 8 + k] = ssd[a][k];
+    for (int k = 0; k < 8; ++k) {
+      float t = ssd[a][k];
+#pragma unroll
+      for (int o = G; o < 64; o <<= 1) t += __shfl_xor(t, o, 64);
+      if (lane < G) s_red[wv][a][cg * 8 + k] = t;
+    }
   __syncthreads();
   const float np_t = float(max(et - 1, 0) * eh * ew);
   const float np_h = float(et * max(eh - 1, 0) * ew);
@@ -101,7 +119,8 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
 #pragma unroll
     for (int a = 0; a < 3; ++a) {
       float s = 0.f;
-      for (int r = 0; r < RPP; ++r) s += s_red[(r * 3 + a) * D + c];
+#pragma unroll
+      for (int r = 0; r < NWAVE; ++r) s += s_red[r][a][c];
       gam[a] = npair[a] > 0.f ? 0.5f * s / npair[a] : 0.f;
     }
     const float den = gam[0] + gam[1] + gam[2] + 1e-12f;
