@@ -142,7 +142,8 @@ def directional_semivariance(Xz: np.ndarray, mask: np.ndarray) -> np.ndarray:
     return out
 
 
-def zone_stats(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS) -> np.ndarray:
+def zone_stats(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS,
+               global_variance: bool = False) -> np.ndarray:
     """Per-zone statistics, float64 [B, Hh, nZ, 8]:
         [0:3]  r_{v,d}: video channel-wise directional share along t, h, w
         [3:6]  gamma^a_d: directional semivariance of the A2V norm map
@@ -154,7 +155,12 @@ def zone_stats(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS) -> 
     s_{d,c} = gamma_{d,c} / (sum_d' gamma_{d',c} + eps) and r_{v,d} = mean_c s_{d,c}.
     Audio (abstract: norms of the audio-to-video cross-attention output): the
     per-token norm a_x = ||O_a2v[x]||_2, its zone mean m_z, and the same lag-one
-    semivariance on the scalar map a (Table 9 caption: audio directional variance)."""
+    semivariance on the scalar map a (Table 9 caption: audio directional variance).
+
+    global_variance (Table 9 caption, the variant without per-channel variance: the
+    feature variance is computed across all channels jointly): the channel-mean
+    semivariance gbar_d = mean_c gamma_{d,c} replaces the per-channel shares, and
+    r_{v,d} = gbar_d / (sum_d' gbar_d' + eps)."""
     v = np.asarray(v, dtype=np.float64)
     a2v = np.asarray(a2v, dtype=np.float64)
     B, Hh, N, C = v.shape
@@ -164,8 +170,12 @@ def zone_stats(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS) -> 
         for h in range(Hh):
             Vz, mask = zone_view(v[b, h], grid, zone)
             gv = directional_semivariance(Vz, mask)                        # [nZ, 3, C]
-            share = gv / (gv.sum(axis=1, keepdims=True) + eps)
-            out[b, h, :, 0:3] = share.mean(axis=2)
+            if global_variance:
+                gbar = gv.mean(axis=2)                                     # [nZ, 3]
+                out[b, h, :, 0:3] = gbar / (gbar.sum(axis=1, keepdims=True) + eps)
+            else:
+                share = gv / (gv.sum(axis=1, keepdims=True) + eps)
+                out[b, h, :, 0:3] = share.mean(axis=2)
             a = np.sqrt((a2v[b, h] ** 2).sum(axis=1))                     # [N]
             Az, _ = zone_view(a[:, None], grid, zone)                     # [nZ, zt, zh, zw, 1]
             out[b, h, :, 3:6] = directional_semivariance(Az, mask)[:, :, 0]
@@ -175,7 +185,8 @@ def zone_stats(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS) -> 
     return out
 
 
-def zone_stats_bruteforce(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS) -> np.ndarray:
+def zone_stats_bruteforce(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float = EPS,
+                          global_variance: bool = False) -> np.ndarray:
     """Same quantities as zone_stats, by explicit loops over zones, tokens and axes
     (tiny inputs only); used to pin the vectorised version."""
     T, H, W = grid
@@ -208,8 +219,12 @@ def zone_stats_bruteforce(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float
                                     ssd_a[d] += (a[n0] - a[n1]) ** 2
                         gv = np.array([0.5 * ssd_v[d] / cnt[d] if cnt[d] else np.zeros(C) for d in range(3)])
                         ga = np.array([0.5 * ssd_a[d] / cnt[d] if cnt[d] else 0.0 for d in range(3)])
-                        share = gv / (gv.sum(axis=0, keepdims=True) + eps)
-                        out[b, hh, z, 0:3] = share.mean(axis=1)
+                        if global_variance:
+                            gbar = [sum(gv[d]) / C for d in range(3)]
+                            out[b, hh, z, 0:3] = [g / (sum(gbar) + eps) for g in gbar]
+                        else:
+                            share = gv / (gv.sum(axis=0, keepdims=True) + eps)
+                            out[b, hh, z, 0:3] = share.mean(axis=1)
                         out[b, hh, z, 3:6] = ga
                         out[b, hh, z, 6] = sum(a[(t * H + h) * W + w] for (t, h, w) in toks) / len(toks)
                         out[b, hh, z, 7] = len(toks)

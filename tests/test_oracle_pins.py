@@ -103,6 +103,24 @@ def test_video_share_of_separable_field_matches_closed_form():
     assert abs(st[0] + st[1] + st[2] - 1.0) < 1e-9
 
 
+def test_global_variance_share_matches_closed_form():
+    # Channel 0 varies along t only (amplitude 2, period 3), channel 1 along h only
+    # (amplitude 0.5, period 5).  Per channel the shares are (1,0,0) and (0,1,0), so their
+    # mean is (1/2, 1/2, 0) whatever the amplitudes; jointly across channels the axes weigh
+    # by each channel's semivariance A^2 sin^2(omega/2), which the global variant must give.
+    grid = zone = (4, 16, 16)
+    w1, w2 = 2 * math.pi / 3, 2 * math.pi / 5
+    V = _grid_field(grid, lambda t, h, w, c: 2.0 * np.sin(w1 * t + 0.2) if c == 0 else 0.5 * np.sin(w2 * h + 0.9),
+                    C=2)
+    a2v = np.ones_like(V)
+    per = O.zone_stats(V, a2v, grid, zone)[0, 0, 0]
+    glo = O.zone_stats(V, a2v, grid, zone, global_variance=True)[0, 0, 0]
+    assert np.allclose(per[:3], [0.5, 0.5, 0.0], atol=1e-9)
+    gt, gh = 4.0 * math.sin(w1 / 2) ** 2, 0.25 * math.sin(w2 / 2) ** 2
+    assert np.allclose(glo[:3], [gt / (gt + gh), gh / (gt + gh), 0.0], atol=1e-9)
+    assert np.array_equal(per[3:], glo[3:])           # the audio statistics do not change
+
+
 def test_zone_stats_vectorised_equals_bruteforce_on_ragged_grid():
     rng = np.random.default_rng(7)
     grid, zone = (5, 6, 7), (2, 4, 4)
@@ -113,6 +131,9 @@ def test_zone_stats_vectorised_equals_bruteforce_on_ragged_grid():
     b = O.zone_stats_bruteforce(V, A, grid, zone)
     assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
     assert a[..., 7].sum() == 2 * N
+    ag = O.zone_stats(V, A, grid, zone, global_variance=True)
+    bg = O.zone_stats_bruteforce(V, A, grid, zone, global_variance=True)
+    assert np.allclose(ag, bg, rtol=1e-12, atol=1e-12)
 
 
 def test_audio_norm_statistics_closed_form():
