@@ -123,15 +123,24 @@ def prism_last_error() -> str:
 
 
 # ------------------------------------------------------------------ the six calls
-def prism_zone_stats(v: torch.Tensor, a2v: torch.Tensor, grid: PrismGrid, stats: torch.Tensor,
-                     stream=None) -> None:
+def _zone_stats(name: str, v: torch.Tensor, a2v: torch.Tensor, grid: PrismGrid, stats: torch.Tensor,
+                stream) -> None:
     B, Hh, N, d = v.shape
     nZ = prism_num_zones(grid)
     dt = _same_dtype(v, a2v)
-    check(load().prism_zone_stats(_ptr(v, shape=(B, Hh, N, d), name="v"),
-                                  _ptr(a2v, shape=(B, Hh, N, d), name="a2v"), dt, B, Hh, d, grid,
-                                  _ptr(stats, torch.float32, (B, Hh, nZ, 8), "stats"), _stream(stream)),
-          "prism_zone_stats")
+    check(getattr(load(), name)(_ptr(v, shape=(B, Hh, N, d), name="v"),
+                                _ptr(a2v, shape=(B, Hh, N, d), name="a2v"), dt, B, Hh, d, grid,
+                                _ptr(stats, torch.float32, (B, Hh, nZ, 8), "stats"), _stream(stream)), name)
+
+
+def prism_zone_stats(v: torch.Tensor, a2v: torch.Tensor, grid: PrismGrid, stats: torch.Tensor,
+                     stream=None) -> None:
+    _zone_stats("prism_zone_stats", v, a2v, grid, stats, stream)
+
+
+def prism_zone_stats_global(v: torch.Tensor, a2v: torch.Tensor, grid: PrismGrid, stats: torch.Tensor,
+                            stream=None) -> None:
+    _zone_stats("prism_zone_stats_global", v, a2v, grid, stats, stream)
 
 
 def prism_assign_shapes(stats: torch.Tensor, grid: PrismGrid, shapes: PrismShapes, params: PrismShapeParams,

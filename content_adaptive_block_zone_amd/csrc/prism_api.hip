@@ -108,16 +108,27 @@ int64_t prism_num_blocks(const prism_grid* grid, const prism_shapes* shapes) {
   return int64_t(g.nZ) * (g.Vz / shapes->vol);
 }
 
-prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
-                              const prism_grid* grid, float* stats, hipStream_t stream) {
-  if (!v || !a2v || !stats) return fail(PRISM_ERR_ARG, "prism_zone_stats: null pointer");
-  if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "prism_zone_stats: B and Hh must be >= 1");
-  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "prism_zone_stats: unknown dtype %d", int(dtype));
-  if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "prism_zone_stats: d=%d not in {32,64,128,256}", d);
+static prism_status zone_stats_common(const char* who, bool global_variance, const void* v, const void* a2v,
+                                      prism_dtype dtype, int B, int Hh, int d, const prism_grid* grid,
+                                      float* stats, hipStream_t stream) {
+  if (!v || !a2v || !stats) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "%s: B and Hh must be >= 1", who);
+  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "%s: unknown dtype %d", who, int(dtype));
+  if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "%s: d=%d not in {32,64,128,256}", who, d);
   Geo g;
   prism_status st = check_grid(grid, &g);
   if (st != PRISM_OK) return st;
-  return launched(launch_zone_stats(v, a2v, dtype, B * Hh, d, g, stats, stream), "prism_zone_stats");
+  return launched(launch_zone_stats(v, a2v, dtype, B * Hh, d, g, global_variance, stats, stream), who);
+}
+
+prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
+                              const prism_grid* grid, float* stats, hipStream_t stream) {
+  return zone_stats_common("prism_zone_stats", false, v, a2v, dtype, B, Hh, d, grid, stats, stream);
+}
+
+prism_status prism_zone_stats_global(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
+                                     const prism_grid* grid, float* stats, hipStream_t stream) {
+  return zone_stats_common("prism_zone_stats_global", true, v, a2v, dtype, B, Hh, d, grid, stats, stream);
 }
 
 prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_grid* grid,

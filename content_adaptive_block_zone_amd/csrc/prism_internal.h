@@ -186,7 +186,7 @@ struct AttnArgs {
 
 // Launchers (each returns the first HIP error of its launches).
 hipError_t launch_zone_stats(const void* v, const void* a2v, prism_dtype dt, int BH, int d,
-                             const Geo& g, float* stats, hipStream_t s);
+                             const Geo& g, bool global_variance, float* stats, hipStream_t s);
 hipError_t launch_assign_shapes(const float* stats, int BH, const Geo& g, const ShapeTab& tab,
                                 const prism_shape_params& p, int32_t* shape_id, float* margin,
                                 hipStream_t s);

@@ -20,7 +20,10 @@ namespace {
 constexpr int NT = 256;
 constexpr int NWAVE = NT / 64;
 
-template <typename T, int D>
+// GLOBAL: instead of taking each channel's share of its semivariance per axis and
+// averaging the shares, take the per-axis semivariance averaged over all channels
+// jointly and its share (the "global variance" variant of Eq. 1, Table 9 caption).
+template <typename T, int D, bool GLOBAL>
 __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, const T* __restrict__ a2v,
                                                    float* __restrict__ stats, Geo g) {
   constexpr int G = D / 8;      // lanes per token
@@ -123,9 +126,14 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
       for (int r = 0; r < NWAVE; ++r) s += s_red[r][a][c];
       gam[a] = npair[a] > 0.f ? 0.5f * s / npair[a] : 0.f;
     }
-    const float den = gam[0] + gam[1] + gam[2] + 1e-12f;
+    if (GLOBAL) {
 #pragma unroll
-    for (int a = 0; a < 3; ++a) s_share[a][c] = gam[a] / den;
+      for (int a = 0; a < 3; ++a) s_share[a][c] = gam[a];
+    } else {
+      const float den = gam[0] + gam[1] + gam[2] + 1e-12f;
+#pragma unroll
+      for (int a = 0; a < 3; ++a) s_share[a][c] = gam[a] / den;
+    }
   }
   __syncthreads();
   float sh[3] = {0.f, 0.f, 0.f};
@@ -155,9 +163,16 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
   res[6] = block_sum<NT>(asum, s_tmp);
   if (tid == 0) {
     float* out = stats + (size_t(bh) * g.nZ + z) * 8;
-    out[0] = res[0] / float(D);
-    out[1] = res[1] / float(D);
-    out[2] = res[2] / float(D);
+    if (GLOBAL) {  // shares of the channel-mean semivariances
+      const float den = (res[0] + res[1] + res[2]) / float(D) + 1e-12f;
+      out[0] = res[0] / float(D) / den;
+      out[1] = res[1] / float(D) / den;
+      out[2] = res[2] / float(D) / den;
+    } else {       // channel-mean of the per-channel shares
+      out[0] = res[0] / float(D);
+      out[1] = res[1] / float(D);
+      out[2] = res[2] / float(D);
+    }
     out[3] = np_t > 0.f ? 0.5f * res[3] / np_t : 0.f;
     out[4] = np_h > 0.f ? 0.5f * res[4] / np_h : 0.f;
     out[5] = np_w > 0.f ? 0.5f * res[5] / np_w : 0.f;
@@ -166,17 +181,17 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
   }
 }
 
-template <typename T>
+template <typename T, bool GLOBAL>
 hipError_t launch_t(const void* v, const void* a2v, int BH, int d, const Geo& g, float* stats,
                     hipStream_t s) {
   dim3 grid(unsigned(BH) * unsigned(g.nZ)), block(NT);
   const T* pv = static_cast<const T*>(v);
   const T* pa = static_cast<const T*>(a2v);
   switch (d) {
-    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32>), grid, block, 0, s, pv, pa, stats, g); break;
-    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64>), grid, block, 0, s, pv, pa, stats, g); break;
-    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128>), grid, block, 0, s, pv, pa, stats, g); break;
-    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -185,9 +200,12 @@ hipError_t launch_t(const void* v, const void* a2v, int BH, int d, const Geo& g,
 }  // namespace
 
 hipError_t launch_zone_stats(const void* v, const void* a2v, prism_dtype dt, int BH, int d,
-                             const Geo& g, float* stats, hipStream_t s) {
-  if (dt == PRISM_BF16) return launch_t<bf16_t>(v, a2v, BH, d, g, stats, s);
-  return launch_t<float>(v, a2v, BH, d, g, stats, s);
+                             const Geo& g, bool global_variance, float* stats, hipStream_t s) {
+  if (dt == PRISM_BF16)
+    return global_variance ? launch_t<bf16_t, true>(v, a2v, BH, d, g, stats, s)
+                           : launch_t<bf16_t, false>(v, a2v, BH, d, g, stats, s);
+  return global_variance ? launch_t<float, true>(v, a2v, BH, d, g, stats, s)
+                         : launch_t<float, false>(v, a2v, BH, d, g, stats, s);
 }
 
 }  // namespace prism

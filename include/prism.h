@@ -92,17 +92,27 @@ typedef struct {
 int64_t prism_num_zones(const prism_grid* grid);
 int64_t prism_num_blocks(const prism_grid* grid, const prism_shapes* shapes);
 
-/* (a1) Zone statistics (abstract; Table 9 caption).
+/* Zone statistics (abstract; Table 9 caption).
  * v, a2v   [B][Hh][N][d] value features and A2V cross-attention output, N = T*H*W.
+ *          Any feature tensor may stand in for v (Table 9 caption: query or key features).
  * stats    out float [B][Hh][nZ][8]: r_v[t,h,w] (per-channel directional share of the
  *          lag-one semivariance of v, averaged over channels), gamma_a[t,h,w] (lag-one
  *          semivariance of the per-token norm ||a2v||), m_z (mean norm), n_z (valid
  *          tokens).  Neighbour pairs never cross a zone border or the grid edge.
- * Requires d % 8 == 0, 8 <= d <= 256, zt*zh*zw <= 4096. */
+ * Requires d in {32, 64, 128, 256} and zt*zh*zw <= 4096; PRISM_ERR_DTYPE / PRISM_ERR_SHAPE
+ * otherwise. */
 prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh,
                               int d, const prism_grid* grid, float* stats, hipStream_t stream);
 
-/* (a2) Shape assignment (abstract: finer blocks along fast-varying, audio-coupled axes;
+/* The "global variance" variant of the zone statistics (Table 9 caption: the feature
+ * variance taken across all channels jointly instead of per channel): r_v[t,h,w] is the
+ * share of each axis in the channel-mean lag-one semivariance, gamma_bar_d /
+ * (sum_d gamma_bar_d + eps).  Everything else, arguments and errors included, as
+ * prism_zone_stats. */
+prism_status prism_zone_stats_global(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh,
+                                     int d, const prism_grid* grid, float* stats, hipStream_t stream);
+
+/* Shape assignment (abstract: finer blocks along fast-varying, audio-coupled axes;
  * Table 10 caption: b*_d ~ g_d^-alpha and its quantization).
  * stats    float [B][Hh][nZ][8] from prism_zone_stats.
  * shape_id out int32 [B][Hh][nZ]: index into shapes of the feasible candidate nearest, in
@@ -114,7 +124,7 @@ prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_
                                  const prism_shapes* shapes, const prism_shape_params* params,
                                  int32_t* shape_id, float* margin, hipStream_t stream);
 
-/* (a3) Token permutation into blocks (abstract: each block's tokens are contiguous).
+/* Token permutation into blocks (abstract: each block's tokens are contiguous).
  * Slot order: zones in raster order; a zone's blocks in raster order over its block grid;
  * inside a block, the tokens lying in the real grid first (raster order), then padding.
  * inverse == 0: x [B][Hh][N][d] -> y [B][Hh][Npad][d], zeros at padding slots.
@@ -147,7 +157,7 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
                                  float* sel_margin, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
 
-/* (a6) Block-sparse attention forward (Figure 2 caption).  Query row i of block I attends
+/* Block-sparse attention forward (Figure 2 caption).  Query row i of block I attends
  * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:
  *   O_i = softmax_j(scale q_i.k_j) v_j,  lse_i = ln sum_j exp(scale q_i.k_j).
  * op   out [B][Hh][nb*vol][d] (zeros at padding rows);  lse out float [B][Hh][nb*vol]
@@ -161,7 +171,7 @@ prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* v
                                    int d, float scale, void* op, float* lse, void* workspace,
                                    size_t ws_bytes, hipStream_t stream);
 
-/* (a7) Block-sparse attention backward, selection held fixed.
+/* Block-sparse attention backward, selection held fixed.
  * With D_i = dO_i.O_i, P_ij = exp(scale q_i.k_j - lse_i), dS_ij = P_ij (dO_i.v_j - D_i):
  *   dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i,  dV_j = sum_i P_ij dO_i.
  * dqp, dkp, dvp out [B][Hh][nb*vol][d] (zeros at padding rows).  dK/dV walk the reverse
