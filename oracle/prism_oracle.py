@@ -689,13 +689,25 @@ def dense_attn_bwd(q, k, v, o, do, lse, scale: float):
 # =================================================================================
 
 def prism_forward(q, k, v, a2v, grid, zone, cands, top_p, k_min, k_max, scale=None,
-                  shape_params: ShapeParams = ShapeParams(), dtype=np.float32):
+                  shape_params: ShapeParams = ShapeParams(), dtype=np.float32,
+                  features: str = "v", global_variance: bool = False, shape_id=None):
+    """The whole forward chain.  The options are the block-shape ablations of Table 9:
+    features "q" / "k" take the query / key features instead of the values for the
+    variance; global_variance takes it across all channels jointly; shape_id, when
+    given, replaces the statistics and shape assignment (random or fixed shapes, whose
+    draws are inputs).  Top-k only / Top-p only (Table 7) are plain parameter choices:
+    top_p = 1 with k_min = k_max = k, or k_min = 1 with k_max >= the live block count."""
     q, k, v, a2v = (np.asarray(a, dtype=np.float64) for a in (q, k, v, a2v))
     B, Hh, N, C = q.shape
     scale = 1.0 / math.sqrt(C) if scale is None else scale
     vol = candidate_volume(cands)
-    stats = zone_stats(v, a2v, grid, zone)
-    sid, margin = assign_shapes(stats.astype(np.float32), cands, zone, shape_params, dtype)
+    if shape_id is None:
+        feat = {"v": v, "q": q, "k": k}[features]
+        stats = zone_stats(feat, a2v, grid, zone, global_variance=global_variance)
+        sid, margin = assign_shapes(stats.astype(np.float32), cands, zone, shape_params, dtype)
+    else:
+        stats, sid = None, np.asarray(shape_id, dtype=np.int32)
+        margin = np.full(sid.shape, np.inf)
     tok = slot_map(grid, zone, cands, sid)
     bv = block_valid(tok, vol)
     qp, kp, vp = permute(q, tok), permute(k, tok), permute(v, tok)
