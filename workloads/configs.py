@@ -1,4 +1,4 @@
-"""The five synthetic workloads: sizes, candidate shapes and selection parameters.
+"""The synthetic workloads: sizes, candidate shapes and selection parameters.
 
 Every entry is a plain description of a workload.  Nothing here computes any part of
 the Prism method; the numbers are the workload recipe (grid, zone size, candidate
@@ -125,6 +125,18 @@ WORKLOADS: List[Workload] = [
         blobs=BlobRecipe(n=3, sigma_lo=3.0, sigma_hi=6.0),
         top_p=0.85, k_min=32, k_max=768,
         q_gain=1.5092, density_target=(0.09, 0.11),     # from oracle/calibrate_gain.py 4
+    ),
+    # Forward-only inference at the 2K, 10 s scale (Table 13 caption: about 870K tokens at
+    # 2K, 10 s, 24 fps, run on 4 GPUs): 61 latent frames x 90 x 160, the same 4-head share
+    # and field recipe as the 2K-like workload, audio scaled to the clip (1,500 tokens),
+    # Top-k ceiling raised so that a 10 % density is not clamped.
+    Workload(
+        name="2k-10s-inference", B=1, heads=4, d=128, grid=(61, 90, 160), zone=(4, 16, 16),
+        cands=tuple(CANDS_64), n_audio=1500, dtype="bf16",
+        field=FieldRecipe("zoned", M=8, f_lo=1 / 32, f_hi=1 / 8),
+        blobs=BlobRecipe(n=3, sigma_lo=3.0, sigma_hi=6.0),
+        top_p=0.85, k_min=32, k_max=2048,
+        q_gain=1.6818, density_target=(0.09, 0.11),     # from oracle/calibrate_gain.py 5
     ),
 ]
 
