@@ -176,17 +176,21 @@ def run_gpu(args):
     _lib.load()
     w = workload(args.workload)
     t0 = time.time()
-    x = make_inputs(w, seed=args.workload)
+    x = make_inputs(w, seed=args.workload, with_grad=not args.forward_only)
     log(f"[bench] inputs of {w.name} generated in {time.time() - t0:.1f}s")
     dev = torch.device("cuda:0")
-    q, k, v, a2v, do = (x[n].to(dev) for n in ("q", "k", "v", "a2v", "do"))
+    q, k, v, a2v = (x[n].to(dev) for n in ("q", "k", "v", "a2v"))
+    do = x["do"].to(dev) if "do" in x else None
     L = PrismLayer.for_workload(w, device=dev)
     stream = torch.cuda.current_stream()
+
+    fwd_only = args.forward_only
 
     def step(ev=None):
         if ev is None:
             L.forward(q, k, v, a2v)
-            L.backward(do)
+            if not fwd_only:
+                L.backward(do)
             return
         L.zone_stats(v, a2v)
         L.assign_shapes()
@@ -199,6 +203,8 @@ def run_gpu(args):
         L.attn_fwd()
         ev["fwd1"].record(stream)
         L.permute(L.op, L.o, inverse=True)
+        if fwd_only:
+            return
         g = L._grads()
         L.permute(do, g["dop"])
         L.attn_bwd(marks=ev["marks"])
@@ -241,15 +247,18 @@ def run_gpu(args):
 
     t_select = sum(e["select0"].elapsed_time(e["fwd0"]) for e in evs) / len(evs)
     t_fwd = sum(e["fwd0"].elapsed_time(e["fwd1"]) for e in evs) / len(evs)
-    t_pre = sum(e["marks"][0].elapsed_time(e["marks"][1]) for e in evs) / len(evs)
-    t_dkdv = sum(e["marks"][1].elapsed_time(e["marks"][2]) for e in evs) / len(evs)
-    t_dq = sum(e["marks"][2].elapsed_time(e["marks"][3]) for e in evs) / len(evs)
+    if fwd_only:
+        t_pre = t_dkdv = t_dq = 0.0
+    else:
+        t_pre = sum(e["marks"][0].elapsed_time(e["marks"][1]) for e in evs) / len(evs)
+        t_dkdv = sum(e["marks"][1].elapsed_time(e["marks"][2]) for e in evs) / len(evs)
+        t_dq = sum(e["marks"][2].elapsed_time(e["marks"][3]) for e in evs) / len(evs)
 
     sums = selection_sums(L)
     pairs = sums["tok_pairs"]
     dens = density(L)
     d = w.d
-    f_sel = 14.0 * d * pairs
+    f_sel = (4.0 if fwd_only else 14.0) * d * pairs
     value = f_sel / (ms_step * 1e-3) / 1e12
     t_attn = t_fwd + t_pre + t_dkdv + t_dq
     attn_tflops = f_sel / (t_attn * 1e-3) / 1e12
@@ -259,6 +268,8 @@ def run_gpu(args):
     # = 312 flop/B), so their roofline is HBM bandwidth on algorithmic bytes.
     kb = kernel_bytes(sums, d)
     kern = {"sparse_attn_fwd": t_fwd, "sparse_attn_bwd_dkdv": t_dkdv, "sparse_attn_bwd_dq": t_dq}
+    if fwd_only:
+        kern = {"sparse_attn_fwd": t_fwd}
     dom = max(kern, key=lambda n: kern[n])
     t_dom = kern[dom]
     achieved = kb[dom] / (t_dom * 1e-3) / 1e9
@@ -269,14 +280,17 @@ def run_gpu(args):
     stage = {}
     names = ["zone_stats", "assign_shapes", "permute_qkv", "select", "attn_fwd", "unpermute_o", "permute_do",
              "attn_bwd", "unpermute_grads"]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    g = L._grads()
     calls = [lambda: L.zone_stats(v, a2v), L.assign_shapes,
              lambda: (L.permute(q, L.qp, block_valid=L.bvalid), L.permute(k, L.kp), L.permute(v, L.vp)),
-             L.select, L.attn_fwd, lambda: L.permute(L.op, L.o, inverse=True), lambda: L.permute(do, g["dop"]),
-             L.attn_bwd,
-             lambda: (L.permute(g["dqp"], g["dq"], inverse=True), L.permute(g["dkp"], g["dk"], inverse=True),
-                      L.permute(g["dvp"], g["dv"], inverse=True))]
+             L.select, L.attn_fwd, lambda: L.permute(L.op, L.o, inverse=True)]
+    if fwd_only:
+        names = names[:len(calls)]
+    else:
+        g = L._grads()
+        calls += [lambda: L.permute(do, g["dop"]), L.attn_bwd,
+                  lambda: (L.permute(g["dqp"], g["dq"], inverse=True), L.permute(g["dkp"], g["dk"], inverse=True),
+                           L.permute(g["dvp"], g["dv"], inverse=True))]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
     ev[0].record(stream)
     for i, c in enumerate(calls):
         c()
@@ -290,14 +304,17 @@ def run_gpu(args):
     if not args.no_dense:
         o_d = torch.empty_like(q)
         lse_d = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
-        dq_d, dk_d, dv_d = (torch.empty_like(q) for _ in range(3))
-        ws = torch.empty(api.prism_dense_bwd_workspace_size(w.B, w.heads, w.N, w.d), dtype=torch.uint8, device=dev)
         wsf = torch.empty(max(1, api.prism_dense_fwd_workspace_size(w.B, w.heads, w.N, w.d)), dtype=torch.uint8,
                           device=dev)
+        if not fwd_only:
+            dq_d, dk_d, dv_d = (torch.empty_like(q) for _ in range(3))
+            ws = torch.empty(api.prism_dense_bwd_workspace_size(w.B, w.heads, w.N, w.d), dtype=torch.uint8,
+                             device=dev)
 
         def dense_step():
             api.prism_dense_attn_fwd(q, k, v, L.scale, o_d, lse_d, wsf)
-            api.prism_dense_attn_bwd(q, k, v, o_d, do, lse_d, L.scale, dq_d, dk_d, dv_d, ws)
+            if not fwd_only:
+                api.prism_dense_attn_bwd(q, k, v, o_d, do, lse_d, L.scale, dq_d, dk_d, dv_d, ws)
 
         dense_step()
         torch.cuda.synchronize()
@@ -308,13 +325,14 @@ def run_gpu(args):
         e1.record(stream)
         torch.cuda.synchronize()
         dense_ms = e0.elapsed_time(e1) / args.dense_steps
-        dflops = 14.0 * d * w.N * w.N * w.B * w.heads
+        dflops = (4.0 if fwd_only else 14.0) * d * w.N * w.N * w.B * w.heads
         dense = dict(ms=round(dense_ms, 3), tflops=round(dflops / (dense_ms * 1e-3) / 1e12, 2),
                      speedup=round(dense_ms / ms_step, 3))
         log(f"[bench] dense comparator: {dense}")
 
     res = dict(
-        metric="ms/layer & effective TFLOP/s, sparse attn fwd+bwd at 2K; speedup vs dense",
+        metric=("ms/layer & effective TFLOP/s, sparse attn fwd (inference) ; speedup vs dense" if fwd_only else
+                "ms/layer & effective TFLOP/s, sparse attn fwd+bwd at 2K; speedup vs dense"),
         value=round(value, 3), unit="TFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
         ms_per_step=round(ms_step, 3), higher_is_better=True, scaling="weak", vs_baseline=None,
         dtype="bf16" if w.dtype == "bf16" else "f32", data="synthetic",
@@ -341,10 +359,10 @@ def run_gpu(args):
     return res, (w, x)
 
 
-def cpu_baseline(w, x, budget_blocks: int):
+def cpu_baseline(w, x, budget_blocks: int, fwd_only: bool = False):
     """The oracle as it stands, on one head of the same inputs: the whole chain for that
     head with the attention restricted to `budget_blocks` query blocks (forward, and
-    the full backward of exactly those blocks' selected pairs)."""
+    unless fwd_only the full backward of exactly those blocks' selected pairs)."""
     import numpy as np
     import threadpoolctl
 
@@ -368,17 +386,18 @@ def cpu_baseline(w, x, budget_blocks: int):
                              w.k_max, rows=rows)
     blocks = [(0, 0, int(I)) for I in rows]
     op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, scale, w.vol, blocks=blocks)
-    dop = O.permute(n["do"], tok)
-    touched = sorted({(0, 0, int(J)) for s in sel.values() for J in s})
-    O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, scale, w.vol, q_blocks=blocks, k_blocks=touched)
+    if not fwd_only:
+        dop = O.permute(n["do"], tok)
+        touched = sorted({(0, 0, int(J)) for s in sel.values() for J in s})
+        O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, scale, w.vol, q_blocks=blocks, k_blocks=touched)
     dt = time.perf_counter() - t0
     pairs = sum(int(bv[0, 0, I]) * int(bv[0, 0, s].sum()) for (_, _, I), s in sel.items())
-    flops = 14.0 * w.d * pairs
+    flops = (4.0 if fwd_only else 14.0) * w.d * pairs
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
                 seconds=round(dt, 2),
                 sample=(f"head 0 of {w.name}: zone stats, shapes, permutation and pooling of the whole head, "
-                        f"selection, forward and backward of {budget_blocks} query blocks "
-                        f"({pairs} valid token pairs, 14*d flops each), float64 numpy"))
+                        f"selection, forward{'' if fwd_only else ' and backward'} of {budget_blocks} query blocks "
+                        f"({pairs} valid token pairs, {4 if fwd_only else 14}*d flops each), float64 numpy"))
 
 
 def main():
@@ -388,9 +407,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--forward-only", action="store_true",
+                    help="time the forward chain only (inference; e.g. --workload 5)")
     ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=400)
+    ap.add_argument("--cpu-blocks", type=int, default=200)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one elementwise pass y = -x over this many MiB after warm-up (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
@@ -408,7 +429,7 @@ def main():
     res, (w, x) = run_gpu(args)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle sample ...")
-        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_blocks)
+        res["cpu_baseline"] = cpu_baseline(w, x, args.cpu_blocks, args.forward_only)
         log(f"[bench] cpu baseline: {res['cpu_baseline']}")
     print(json.dumps(res), flush=True)
 

@@ -18,11 +18,39 @@ from .api import ShapeRule
 Shape = Tuple[int, int, int]
 
 
+def random_shape_ids(B: int, Hh: int, grid: Sequence[int], zone: Sequence[int], cands: Sequence[Shape],
+                     seed: int) -> torch.Tensor:
+    """Seeded uniform draw of a feasible candidate per (batch, head, zone): the random-shape
+    ablation of Table 9.  The draw happens here, on the host, and enters the layer as an
+    input (PrismLayer.forward(..., shape_id=...)).  int32 [B, Hh, nZ] on the CPU."""
+    T, H, W = grid
+    zt, zh, zw = zone
+    nZ = -(-T // zt) * -(-H // zh) * -(-W // zw)
+    ok = [i for i, (bt, bh, bw) in enumerate(cands) if zt % bt == 0 and zh % bh == 0 and zw % bw == 0]
+    if not ok:
+        raise ValueError("no candidate shape fits the zone")
+    g = torch.Generator().manual_seed(int(seed))
+    pick = torch.randint(len(ok), (B, Hh, nZ), generator=g)
+    return torch.tensor(ok, dtype=torch.int32)[pick]
+
+
 class PrismLayer:
+    """One layer's buffers and call sequence.
+
+    Ablation settings (Table 9 caption): `features` picks the tensor whose directional
+    variance guides the shapes ("v" by default, or "q" / "k"); `variance` = "global"
+    takes it across all channels jointly instead of per channel.  Fixed shapes are a
+    one-candidate set; random shapes come in through forward(shape_id=...).  Top-k only
+    and Top-p only (Table 7) are selection parameters (top_p = 1 with k_min = k_max, or
+    k_min = 1 with k_max >= the block count)."""
+
     def __init__(self, B: int, Hh: int, d: int, grid: Sequence[int], zone: Sequence[int],
                  cands: Sequence[Shape], top_p: float, k_min: int, k_max: int,
                  dtype: torch.dtype = torch.bfloat16, device="cuda", scale: Optional[float] = None,
-                 rule: ShapeRule = ShapeRule()):
+                 rule: ShapeRule = ShapeRule(), features: str = "v", variance: str = "channel"):
+        if features not in ("v", "q", "k") or variance not in ("channel", "global"):
+            raise ValueError(f"features must be v, q or k and variance channel or global, got {features}, {variance}")
+        self.features, self.variance = features, variance
         self.B, self.Hh, self.d = B, Hh, d
         self.dtype, self.device = dtype, torch.device(device)
         self.grid = api.make_grid(grid, zone)
@@ -68,8 +96,9 @@ class PrismLayer:
         return self._grad_bufs
 
     # ---- stages (each is exactly one library call)
-    def zone_stats(self, v, a2v):
-        api.prism_zone_stats(v, a2v, self.grid, self.stats)
+    def zone_stats(self, feat, a2v):
+        fn = api.prism_zone_stats_global if self.variance == "global" else api.prism_zone_stats
+        fn(feat, a2v, self.grid, self.stats)
 
     def assign_shapes(self):
         api.prism_assign_shapes(self.stats, self.grid, self.shapes, self.shape_params, self.shape_id,
@@ -94,9 +123,12 @@ class PrismLayer:
                                   g["dqp"], g["dkp"], g["dvp"], self.ws_bwd, marks)
 
     # ---- whole layer
-    def forward(self, q, k, v, a2v):
-        self.zone_stats(v, a2v)
-        self.assign_shapes()
+    def forward(self, q, k, v, a2v, shape_id: Optional[torch.Tensor] = None):
+        if shape_id is None:
+            self.zone_stats({"v": v, "q": q, "k": k}[self.features], a2v)
+            self.assign_shapes()
+        else:
+            self.shape_id.copy_(shape_id)
         self.permute(q, self.qp, block_valid=self.bvalid)
         self.permute(k, self.kp)
         self.permute(v, self.vp)
@@ -115,7 +147,10 @@ class PrismLayer:
         return g["dq"], g["dk"], g["dv"]
 
     @classmethod
-    def for_workload(cls, w, device="cuda", heads: Optional[int] = None):
+    def for_workload(cls, w, device="cuda", heads: Optional[int] = None, **kw):
+        """A layer sized for a workload; keyword arguments override its cands, top_p,
+        k_min, k_max or set the ablation options."""
         dt = torch.float32 if w.dtype == "f32" else torch.bfloat16
-        return cls(w.B, w.heads if heads is None else heads, w.d, w.grid, w.zone, list(w.cands), w.top_p,
-                   w.k_min, w.k_max, dtype=dt, device=device)
+        args = dict(cands=list(w.cands), top_p=w.top_p, k_min=w.k_min, k_max=w.k_max)
+        args.update(kw)
+        return cls(w.B, w.heads if heads is None else heads, w.d, w.grid, w.zone, dtype=dt, device=device, **args)
