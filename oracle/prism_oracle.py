@@ -231,6 +231,21 @@ def zone_stats_bruteforce(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float
     return out
 
 
+def a2v_norm(q: np.ndarray, ka: np.ndarray, va: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
+    """Per-token norm of the audio-to-video cross-attention output (abstract: the shapes
+    follow the feature norms of the A2V cross-attention output): video queries q
+    [B,Hh,N,C] attend densely to audio keys ka and values va [B,Hh,Na,C];
+    a_x = || softmax_j(q_x . ka_j * scale) va ||_2, float64 [B, Hh, N].
+    zone_stats(v, a[..., None]) then gives the statistics of the norm map (the norm of a
+    one-element row is its value)."""
+    q, ka, va = (np.asarray(x, dtype=np.float64) for x in (q, ka, va))
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    s = (q @ np.swapaxes(ka, -1, -2)) * scale
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    o = (e / e.sum(axis=-1, keepdims=True)) @ va
+    return np.sqrt((o * o).sum(axis=-1))
+
+
 # =================================================================================
 # Shape assignment (abstract: finer partitioning along axes of rapid visual variation
 # and strong audio-visual coupling; Table 9 caption: r_{v,d}, gate a-bar, v-hat_{a,d};

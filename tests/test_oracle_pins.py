@@ -121,6 +121,39 @@ def test_global_variance_share_matches_closed_form():
     assert np.array_equal(per[3:], glo[3:])           # the audio statistics do not change
 
 
+def test_a2v_norm_special_cases_and_bruteforce():
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 2, 7, 4))
+    va = rng.standard_normal((1, 2, 5, 4))
+    # one audio key: every query's output is that key's value row
+    a1 = O.a2v_norm(q, rng.standard_normal((1, 2, 1, 4)), va[:, :, :1])
+    assert np.allclose(a1, np.linalg.norm(va[:, :, 0], axis=-1)[..., None].repeat(7, axis=-1), atol=1e-12)
+    # identical keys: uniform weights, output = mean value row
+    ka = np.repeat(rng.standard_normal((1, 2, 1, 4)), 5, axis=2)
+    a2 = O.a2v_norm(q, ka, va)
+    assert np.allclose(a2, np.linalg.norm(va.mean(axis=2), axis=-1)[..., None].repeat(7, axis=-1), atol=1e-12)
+    # explicit loops
+    ka = rng.standard_normal((1, 2, 5, 4))
+    a3 = O.a2v_norm(q, ka, va, scale=0.3)
+    for h in range(2):
+        for x in range(7):
+            w = [math.exp(0.3 * float(q[0, h, x] @ ka[0, h, j])) for j in range(5)]
+            o = sum(wj * va[0, h, j] for j, wj in enumerate(w)) / sum(w)
+            assert abs(a3[0, h, x] - math.sqrt(float(o @ o))) < 1e-12
+
+
+def test_zone_stats_from_norm_map_equals_from_rows():
+    rng = np.random.default_rng(5)
+    grid, zone = (5, 6, 7), (2, 4, 4)
+    N = 5 * 6 * 7
+    V = rng.standard_normal((1, 2, N, 3))
+    A = rng.standard_normal((1, 2, N, 4))
+    a = np.linalg.norm(A, axis=-1)[..., None]
+    for gv in (False, True):
+        assert np.allclose(O.zone_stats(V, A, grid, zone, global_variance=gv),
+                           O.zone_stats(V, a, grid, zone, global_variance=gv), rtol=1e-13, atol=1e-13)
+
+
 def test_zone_stats_vectorised_equals_bruteforce_on_ragged_grid():
     rng = np.random.default_rng(7)
     grid, zone = (5, 6, 7), (2, 4, 4)
