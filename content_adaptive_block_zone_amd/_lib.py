@@ -44,6 +44,8 @@ PROTOTYPES = {
     "prism_num_blocks": (c_int64, [_GP, _SP]),
     "prism_zone_stats": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _P, _P]),
     "prism_zone_stats_global": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _P, _P]),
+    "prism_a2v_attn_norm": (c_int, [_P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_float, _P, _P, _P]),
+    "prism_zone_stats_from_norm": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, c_int, _P, _P]),
     "prism_assign_shapes": (c_int, [_P, c_int, c_int, _GP, _SP, _SHP, _P, _P, _P]),
     "prism_permute": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _SP, _P, c_int, _P, _P]),
     "prism_select_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),

@@ -143,6 +143,29 @@ def prism_zone_stats_global(v: torch.Tensor, a2v: torch.Tensor, grid: PrismGrid,
     _zone_stats("prism_zone_stats_global", v, a2v, grid, stats, stream)
 
 
+def prism_a2v_attn_norm(q: torch.Tensor, ka: torch.Tensor, va: torch.Tensor, scale: float, a2v_norm: torch.Tensor,
+                        o: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, Hh, N, d = q.shape
+    Na = ka.shape[2]
+    dt = _same_dtype(q, ka, va)
+    check(load().prism_a2v_attn_norm(_ptr(q, shape=(B, Hh, N, d), name="q"), _ptr(ka, shape=(B, Hh, Na, d), name="ka"),
+                                     _ptr(va, shape=(B, Hh, Na, d), name="va"), dt, B, Hh, N, Na, d, float(scale),
+                                     None if o is None else _ptr(o, q.dtype, (B, Hh, N, d), "o"),
+                                     _ptr(a2v_norm, torch.float32, (B, Hh, N), "a2v_norm"), _stream(stream)),
+          "prism_a2v_attn_norm")
+
+
+def prism_zone_stats_from_norm(v: torch.Tensor, a2v_norm: torch.Tensor, grid: PrismGrid, stats: torch.Tensor,
+                               global_variance: bool = False, stream=None) -> None:
+    B, Hh, N, d = v.shape
+    nZ = prism_num_zones(grid)
+    check(load().prism_zone_stats_from_norm(_ptr(v, shape=(B, Hh, N, d), name="v"),
+                                            _ptr(a2v_norm, torch.float32, (B, Hh, N), "a2v_norm"), _dt(v), B, Hh,
+                                            d, grid, int(bool(global_variance)),
+                                            _ptr(stats, torch.float32, (B, Hh, nZ, 8), "stats"), _stream(stream)),
+          "prism_zone_stats_from_norm")
+
+
 def prism_assign_shapes(stats: torch.Tensor, grid: PrismGrid, shapes: PrismShapes, params: PrismShapeParams,
                         shape_id: torch.Tensor, margin: Optional[torch.Tensor] = None, stream=None) -> None:
     B, Hh, nZ, _ = stats.shape

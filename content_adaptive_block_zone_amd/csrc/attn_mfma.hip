@@ -103,6 +103,10 @@ __device__ __forceinline__ int nrows_of(const AttnArgs& a, int bh, int I) {
 __device__ __forceinline__ size_t row0_of(const AttnArgs& a, int bh, int I) {
   return size_t(bh) * a.nrows + size_t(I) * TR;
 }
+// first row of key block J (keys may be a different sequence in a dense cross-attention)
+__device__ __forceinline__ size_t krow0_of(const AttnArgs& a, int bh, int J) {
+  return size_t(bh) * a.nkrows + size_t(J) * TR;
+}
 
 // Owner block of a workgroup.  Heads are taken in order, so that a head's K/V (or Q/dO)
 // pass through the 256 MB last-level cache one at a time.  Workgroups are dealt to the
@@ -144,11 +148,12 @@ __device__ __forceinline__ BlockList load_list(const AttnArgs& a, int bh, const 
   __syncthreads();
   return L;
 }
+// srows: rows per head of the streamed tensor (dense mode's ragged last block)
 __device__ __forceinline__ void list_at(const AttnArgs& a, int bh, const BlockList& L, const int* meta, int k, int& J,
-                                        int& n) {
+                                        int& n, int srows) {
   if (a.dense) {
     J = k;
-    n = min(TR, a.nrows - k * TR);
+    n = min(TR, srows - k * TR);
   } else if (L.in_lds) {
     const int m = meta[k];
     J = m & 0xffff;
@@ -261,7 +266,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   bf16_t* O = static_cast<bf16_t*>(a.out);
   __shared__ int sMeta[kMetaCap];
-  const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
+  const int cnt = a.dense ? a.nkb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
   const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
   const int qrow = 16 * w + l16;
   const bool qok = qrow < nI;
@@ -278,9 +283,9 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   Chunks ck, cv;
   int J = 0, nJ = 0;
   if (cnt > 0) {
-    list_at(a, bh, bl, sMeta, 0, J, nJ);
-    fetch(ck, K + row0_of(a, bh, J) * D, nJ);
-    fetch(cv, V + row0_of(a, bh, J) * D, nJ);
+    list_at(a, bh, bl, sMeta, 0, J, nJ, a.nkrows);
+    fetch(ck, K + krow0_of(a, bh, J) * D, nJ);
+    fetch(cv, V + krow0_of(a, bh, J) * D, nJ);
   }
   for (int it = 0; it < cnt; ++it) {
     __syncthreads();
@@ -289,9 +294,9 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
     __syncthreads();
     const int nJc = nJ;
     if (it + 1 < cnt) {
-      list_at(a, bh, bl, sMeta, it + 1, J, nJ);
-      fetch(ck, K + row0_of(a, bh, J) * D, nJ);
-      fetch(cv, V + row0_of(a, bh, J) * D, nJ);
+      list_at(a, bh, bl, sMeta, it + 1, J, nJ, a.nkrows);
+      fetch(ck, K + krow0_of(a, bh, J) * D, nJ);
+      fetch(cv, V + krow0_of(a, bh, J) * D, nJ);
     }
     // S^T tiles: rows = keys 16kt + 4G + i, column = this lane's query
     f32x4 st[4];
@@ -337,12 +342,25 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
       o[t] = mma(ldt8<f16x8>(sVt, 16 * t + l16, 4 + G), p1, o[t]);
     }
   }
-  // O^T tile t: rows d = 16t + 4G + i, column = query qrow
+  // O^T tile t: rows d = 16t + 4G + i, column = query qrow.  O, LSE and the row norm are
+  // each optional (the norm serves the audio-to-video cross-attention's per-token norm).
   if (qok) {
     const float inv = 1.f / l;
+    if (O) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) store4(O + (q0 + qrow) * D + 16 * t + 4 * G, o[t], inv);
-    if (G == 0) a.lse_out[q0 + qrow] = (m + log2f(l)) * 0.6931471805599453f;
+      for (int t = 0; t < 8; ++t) store4(O + (q0 + qrow) * D + 16 * t + 4 * G, o[t], inv);
+    }
+    if (a.lse_out && G == 0) a.lse_out[q0 + qrow] = (m + log2f(l)) * 0.6931471805599453f;
+    if (a.norm_out) {
+      float ss = 0.f;
+#pragma unroll
+      for (int t = 0; t < 8; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ss = fmaf(o[t][i] * inv, o[t][i] * inv, ss);
+      ss += __shfl_xor(ss, 16, 64);   // the lanes of one query (same l16) are all in this branch
+      ss += __shfl_xor(ss, 32, 64);
+      if (G == 0) a.norm_out[q0 + qrow] = sqrtf(ss);
+    }
   } else if (!a.dense) {
 #pragma unroll
     for (int t = 0; t < 8; ++t) store4(O + (q0 + qrow) * D + 16 * t + 4 * G, zero4(), 0.f);
@@ -392,7 +410,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
   Chunks ck, cv;
   int J = 0, nJ = 0;
   if (cnt > 0) {
-    list_at(a, bh, bl, sMeta, 0, J, nJ);
+    list_at(a, bh, bl, sMeta, 0, J, nJ, a.nkrows);
     fetch(ck, K + row0_of(a, bh, J) * D, nJ);
     fetch(cv, V + row0_of(a, bh, J) * D, nJ);
   }
@@ -404,7 +422,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
     __syncthreads();
     const int nJc = nJ;
     if (it + 1 < cnt) {
-      list_at(a, bh, bl, sMeta, it + 1, J, nJ);
+      list_at(a, bh, bl, sMeta, it + 1, J, nJ, a.nkrows);
       fetch(ck, K + row0_of(a, bh, J) * D, nJ);
       fetch(cv, V + row0_of(a, bh, J) * D, nJ);
     }
@@ -510,7 +528,7 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   size_t qn = 0;
   auto fetch_q = [&](int k) {
     int Ib;
-    list_at(a, bh, bl, sMeta, k, Ib, nIn);
+    list_at(a, bh, bl, sMeta, k, Ib, nIn, a.nrows);
     qn = row0_of(a, bh, Ib);
     fetch(cq, Q + qn * D, nIn);
     if (tid < TR) {

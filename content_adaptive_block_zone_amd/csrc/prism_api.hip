@@ -108,28 +108,36 @@ int64_t prism_num_blocks(const prism_grid* grid, const prism_shapes* shapes) {
   return int64_t(g.nZ) * (g.Vz / shapes->vol);
 }
 
-static prism_status zone_stats_common(const char* who, bool global_variance, const void* v, const void* a2v,
-                                      prism_dtype dtype, int B, int Hh, int d, const prism_grid* grid,
-                                      float* stats, hipStream_t stream) {
-  if (!v || !a2v || !stats) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+static prism_status zone_stats_common(const char* who, bool global_variance, bool from_norm, const void* v,
+                                      const void* aux, prism_dtype dtype, int B, int Hh, int d,
+                                      const prism_grid* grid, float* stats, hipStream_t stream) {
+  if (!v || !aux || !stats) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
   if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "%s: B and Hh must be >= 1", who);
   if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "%s: unknown dtype %d", who, int(dtype));
   if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "%s: d=%d not in {32,64,128,256}", who, d);
   Geo g;
   prism_status st = check_grid(grid, &g);
   if (st != PRISM_OK) return st;
-  return launched(launch_zone_stats(v, a2v, dtype, B * Hh, d, g, global_variance, stats, stream), who);
+  return launched(launch_zone_stats(v, aux, dtype, B * Hh, d, g, global_variance, from_norm, stats, stream), who);
 }
 
 prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
                               const prism_grid* grid, float* stats, hipStream_t stream) {
-  return zone_stats_common("prism_zone_stats", false, v, a2v, dtype, B, Hh, d, grid, stats, stream);
+  return zone_stats_common("prism_zone_stats", false, false, v, a2v, dtype, B, Hh, d, grid, stats, stream);
 }
 
 prism_status prism_zone_stats_global(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
                                      const prism_grid* grid, float* stats, hipStream_t stream) {
-  return zone_stats_common("prism_zone_stats_global", true, v, a2v, dtype, B, Hh, d, grid, stats, stream);
+  return zone_stats_common("prism_zone_stats_global", true, false, v, a2v, dtype, B, Hh, d, grid, stats, stream);
 }
+
+prism_status prism_zone_stats_from_norm(const void* v, const float* a2v_norm, prism_dtype dtype, int B, int Hh,
+                                        int d, const prism_grid* grid, int global_variance, float* stats,
+                                        hipStream_t stream) {
+  return zone_stats_common("prism_zone_stats_from_norm", global_variance != 0, true, v, a2v_norm, dtype, B, Hh,
+                           d, grid, stats, stream);
+}
+
 
 prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_grid* grid,
                                  const prism_shapes* shapes, const prism_shape_params* params,
@@ -212,6 +220,7 @@ static AttnArgs sparse_args(int B, int Hh, int nb, int vol, int d, int k_max, fl
   AttnArgs a = {};
   a.BH = B * Hh; a.nb = nb; a.vol = vol; a.k_max = k_max; a.nrows = nb * vol; a.d = d;
   a.dense = 0; a.scale = scale;
+  a.nkrows = a.nrows; a.nkb = nb;
   return a;
 }
 
@@ -220,6 +229,7 @@ static AttnArgs dense_args(int B, int Hh, int N, int d, float scale) {
   const int nb = (N + kTileRows - 1) / kTileRows;
   a.BH = B * Hh; a.nb = nb; a.vol = kTileRows; a.k_max = nb; a.nrows = N; a.d = d;
   a.dense = 1; a.scale = scale;
+  a.nkrows = N; a.nkb = nb;
   return a;
 }
 
@@ -313,6 +323,26 @@ prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, c
   a.q = q; a.k = k; a.v = v; a.o = o; a.dout = dout; a.lse_in = lse;
   a.dq = dq; a.dk = dk; a.dv = dv;
   return launched(launch_attn_bwd(a, dtype, workspace, marks, stream), "prism_dense_attn_bwd");
+}
+
+prism_status prism_a2v_attn_norm(const void* q, const void* ka, const void* va, prism_dtype dtype, int B, int Hh,
+                                 int N, int Na, int d, float scale, void* o, float* a2v_norm,
+                                 hipStream_t stream) {
+  const char* who = "prism_a2v_attn_norm";
+  if (!q || !ka || !va || !a2v_norm) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1 || N < 1 || Na < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, N, Na must be >= 1", who);
+  if (dtype != PRISM_BF16 || d != 128) return fail(PRISM_ERR_DTYPE, "%s: needs bf16 and d = 128", who);
+  if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "%s: scale must be finite", who);
+  if (int64_t(B) * Hh * N > (int64_t(1) << 31) || int64_t(B) * Hh * Na > (int64_t(1) << 31))
+    return fail(PRISM_ERR_SHAPE, "%s: too many rows", who);
+  AttnArgs a = dense_args(B, Hh, N, d, scale);
+  a.nkrows = Na;
+  a.nkb = (Na + kTileRows - 1) / kTileRows;
+  a.q = q; a.k = ka; a.v = va;
+  a.out = o;
+  a.lse_out = nullptr;
+  a.norm_out = a2v_norm;
+  return launched(launch_attn_fwd_mfma(a, stream), who);
 }
 
 }  // extern "C"

@@ -182,11 +182,16 @@ struct AttnArgs {
   int BH, nb, vol, k_max, nrows, d;
   int dense;  // 1: unpermuted [N][d] tensors, 64-row tiles, every block selected
   float scale;
+  // Key side of a dense forward: rows and 64-row blocks of K/V per head (equal to nrows
+  // and nb except for a cross-attention, whose keys are a different sequence).
+  int nkrows, nkb;
+  float* norm_out;  // forward only, nullable: L2 norm of each output row, float [BH][nrows]
 };
 
 // Launchers (each returns the first HIP error of its launches).
-hipError_t launch_zone_stats(const void* v, const void* a2v, prism_dtype dt, int BH, int d,
-                             const Geo& g, bool global_variance, float* stats, hipStream_t s);
+// aux: the A2V output rows [BH][N][d] (dtype dt), or with from_norm the norm map float [BH][N]
+hipError_t launch_zone_stats(const void* v, const void* aux, prism_dtype dt, int BH, int d, const Geo& g,
+                             bool global_variance, bool from_norm, float* stats, hipStream_t s);
 hipError_t launch_assign_shapes(const float* stats, int BH, const Geo& g, const ShapeTab& tab,
                                 const prism_shape_params& p, int32_t* shape_id, float* margin,
                                 hipStream_t s);
@@ -202,6 +207,8 @@ size_t select_ws_bytes(int BH, int nb, int d);
 // scalar kernels.  The forward needs no scratch; the backward's holds D (one float per row).
 size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
 size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);
+int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s);
 

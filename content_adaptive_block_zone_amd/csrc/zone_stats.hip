@@ -23,9 +23,13 @@ constexpr int NWAVE = NT / 64;
 // GLOBAL: instead of taking each channel's share of its semivariance per axis and
 // averaging the shares, take the per-axis semivariance averaged over all channels
 // jointly and its share (the "global variance" variant of Eq. 1, Table 9 caption).
-template <typename T, int D, bool GLOBAL>
-__global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, const T* __restrict__ a2v,
+// FROM_NORM: aux is the per-token A2V norm map, float [BH][N], instead of the A2V output
+// rows [BH][N][D] whose norms the kernel would take itself.
+template <typename T, int D, bool GLOBAL, bool FROM_NORM>
+__global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, const void* __restrict__ aux,
                                                    float* __restrict__ stats, Geo g) {
+  const T* a2v = static_cast<const T*>(aux);
+  const float* anorm = static_cast<const float*>(aux);
   constexpr int G = D / 8;      // lanes per token
   constexpr int RPP = NT / G;   // rows in flight per pass
   constexpr int U = 4;          // tokens along w per step
@@ -57,6 +61,7 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
     const size_t off = base + (size_t((t0 + lt) * g.H + h0 + lh) * g.W + w0) * D + cg * 8;
     const T* vr = v + off;
     const T* ar = a2v + off;
+    const float* nr = anorm + size_t(bh) * g.N + size_t((t0 + lt) * g.H + h0 + lh) * g.W + w0;
     const bool has_t = lt + 1 < et, has_h = lh + 1 < eh;
     // A neighbour row that does not exist is replaced by the row itself, and a token past
     // the zone's end by the last one: their increments are exactly zero (the ragged tail
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
         load8(vr + o, x[j]);
         load8(vr + o + dh, yh[j]);
         load8(vr + o + dt, yt[j]);
-        load8(ar + o, u[j]);
+        if constexpr (!FROM_NORM) load8(ar + o, u[j]);
       }
       if (lw0 == 0) {
 #pragma unroll
@@ -92,12 +97,16 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
           ssd[0][k] = fmaf(dtt, dtt, ssd[0][k]);
           prev[k] = x[j][k];
         }
-        float sq = 0.f;
+        if constexpr (FROM_NORM) {
+          if (cg == 0 && lw < ew) s_a[(lt * g.zh + lh) * g.zw + lw] = nr[lw];
+        } else {
+          float sq = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sq = fmaf(u[j][k], u[j][k], sq);
+          for (int k = 0; k < 8; ++k) sq = fmaf(u[j][k], u[j][k], sq);
 #pragma unroll
-        for (int o = G / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
-        if (cg == 0 && lw < ew) s_a[(lt * g.zh + lh) * g.zw + lw] = sqrtf(sq);
+          for (int o = G / 2; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+          if (cg == 0 && lw < ew) s_a[(lt * g.zh + lh) * g.zw + lw] = sqrtf(sq);
+        }
       }
     }
   }
@@ -181,31 +190,36 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
   }
 }
 
-template <typename T, bool GLOBAL>
-hipError_t launch_t(const void* v, const void* a2v, int BH, int d, const Geo& g, float* stats,
-                    hipStream_t s) {
+template <typename T, bool GLOBAL, bool FROM_NORM>
+hipError_t launch_t(const void* v, const void* aux, int BH, int d, const Geo& g, float* stats, hipStream_t s) {
   dim3 grid(unsigned(BH) * unsigned(g.nZ)), block(NT);
   const T* pv = static_cast<const T*>(v);
-  const T* pa = static_cast<const T*>(a2v);
   switch (d) {
-    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
-    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
-    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
-    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256, GLOBAL>), grid, block, 0, s, pv, pa, stats, g); break;
+    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
+    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
+    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
+    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t launch_dt(const void* v, const void* aux, int BH, int d, const Geo& g, bool global_variance,
+                     bool from_norm, float* stats, hipStream_t s) {
+  if (from_norm)
+    return global_variance ? launch_t<T, true, true>(v, aux, BH, d, g, stats, s)
+                           : launch_t<T, false, true>(v, aux, BH, d, g, stats, s);
+  return global_variance ? launch_t<T, true, false>(v, aux, BH, d, g, stats, s)
+                         : launch_t<T, false, false>(v, aux, BH, d, g, stats, s);
+}
+
 }  // namespace
 
-hipError_t launch_zone_stats(const void* v, const void* a2v, prism_dtype dt, int BH, int d,
-                             const Geo& g, bool global_variance, float* stats, hipStream_t s) {
-  if (dt == PRISM_BF16)
-    return global_variance ? launch_t<bf16_t, true>(v, a2v, BH, d, g, stats, s)
-                           : launch_t<bf16_t, false>(v, a2v, BH, d, g, stats, s);
-  return global_variance ? launch_t<float, true>(v, a2v, BH, d, g, stats, s)
-                         : launch_t<float, false>(v, a2v, BH, d, g, stats, s);
+hipError_t launch_zone_stats(const void* v, const void* aux, prism_dtype dt, int BH, int d, const Geo& g,
+                             bool global_variance, bool from_norm, float* stats, hipStream_t s) {
+  if (dt == PRISM_BF16) return launch_dt<bf16_t>(v, aux, BH, d, g, global_variance, from_norm, stats, s);
+  return launch_dt<float>(v, aux, BH, d, g, global_variance, from_norm, stats, s);
 }
 
 }  // namespace prism

@@ -100,6 +100,17 @@ class PrismLayer:
         fn = api.prism_zone_stats_global if self.variance == "global" else api.prism_zone_stats
         fn(feat, a2v, self.grid, self.stats)
 
+    def zone_stats_from_norm(self, feat, a2v_norm):
+        api.prism_zone_stats_from_norm(feat, a2v_norm, self.grid, self.stats, self.variance == "global")
+
+    def a2v_norm(self, q, ka, va, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Per-token norm of the audio-to-video cross-attention softmax(q ka^T/sqrt(d)) va,
+        float32 [B, Hh, N] (the layer's own dense cross-attention kernel)."""
+        if out is None:
+            out = torch.empty(q.shape[:3], dtype=torch.float32, device=self.device)
+        api.prism_a2v_attn_norm(q, ka, va, self.scale, out)
+        return out
+
     def assign_shapes(self):
         api.prism_assign_shapes(self.stats, self.grid, self.shapes, self.shape_params, self.shape_id,
                                 self.shape_margin)
@@ -123,9 +134,16 @@ class PrismLayer:
                                   g["dqp"], g["dkp"], g["dvp"], self.ws_bwd, marks)
 
     # ---- whole layer
-    def forward(self, q, k, v, a2v, shape_id: Optional[torch.Tensor] = None):
+    def forward(self, q, k, v, a2v=None, shape_id: Optional[torch.Tensor] = None,
+                a2v_norm: Optional[torch.Tensor] = None):
+        """a2v: the A2V cross-attention output [B, Hh, N, d]; or a2v_norm: its per-token
+        norm [B, Hh, N] (see a2v_norm()); or shape_id: given shapes, no statistics."""
         if shape_id is None:
-            self.zone_stats({"v": v, "q": q, "k": k}[self.features], a2v)
+            feat = {"v": v, "q": q, "k": k}[self.features]
+            if a2v_norm is not None:
+                self.zone_stats_from_norm(feat, a2v_norm)
+            else:
+                self.zone_stats(feat, a2v)
             self.assign_shapes()
         else:
             self.shape_id.copy_(shape_id)

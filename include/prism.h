@@ -112,6 +112,25 @@ prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype,
 prism_status prism_zone_stats_global(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh,
                                      int d, const prism_grid* grid, float* stats, hipStream_t stream);
 
+/* Audio-to-video cross-attention emitting the per-token norm that guides the shapes
+ * (abstract: feature norms of the A2V cross-attention output), so that the statistics
+ * need not read the A2V output back.
+ * q        [B][Hh][N][d]  video queries;  ka, va [B][Hh][Na][d] audio keys and values.
+ * o        optional out [B][Hh][N][d]: softmax(q ka^T * scale) va (NULL: not written).
+ * a2v_norm out float [B][Hh][N]: the L2 norm of each output row, from the fp32 output.
+ * Dense over all Na keys (no selection).  Requires bf16 and d = 128 (PRISM_ERR_DTYPE). */
+prism_status prism_a2v_attn_norm(const void* q, const void* ka, const void* va, prism_dtype dtype, int B,
+                                 int Hh, int N, int Na, int d, float scale, void* o, float* a2v_norm,
+                                 hipStream_t stream);
+
+/* Zone statistics from the per-token A2V norm map (float [B][Hh][N], e.g. from
+ * prism_a2v_attn_norm) instead of the A2V output rows; global_variance != 0 selects the
+ * all-channel variant of prism_zone_stats_global.  Arguments, output and errors otherwise
+ * as prism_zone_stats. */
+prism_status prism_zone_stats_from_norm(const void* v, const float* a2v_norm, prism_dtype dtype, int B,
+                                        int Hh, int d, const prism_grid* grid, int global_variance,
+                                        float* stats, hipStream_t stream);
+
 /* Shape assignment (abstract: finer blocks along fast-varying, audio-coupled axes;
  * Table 10 caption: b*_d ~ g_d^-alpha and its quantization).
  * stats    float [B][Hh][nZ][8] from prism_zone_stats.

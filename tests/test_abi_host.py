@@ -114,6 +114,12 @@ def test_calls_validate_before_launch(lib):
         ("prism_sparse_attn_bwd", (P, P, P, P, P, P, F32, P, P, P, 8, P, P, 1, 2, 16, 16, 64, 0.125, P, P, P,
                                    P, 8, None, None), E.PRISM_ERR_ARG),
         ("prism_dense_attn_fwd", (P, P, P, F32, 1, 2, 0, 64, 0.125, P, P, None, 0, None), E.PRISM_ERR_ARG),
+        ("prism_a2v_attn_norm", (P, P, P, F32, 1, 2, 64, 32, 128, 0.1, None, P, None), E.PRISM_ERR_DTYPE),
+        ("prism_a2v_attn_norm", (P, P, P, BF16, 1, 2, 64, 0, 128, 0.1, None, P, None), E.PRISM_ERR_ARG),
+        ("prism_a2v_attn_norm", (P, P, None, BF16, 1, 2, 64, 32, 128, 0.1, None, P, None), E.PRISM_ERR_ARG),
+        ("prism_zone_stats_from_norm", (P, None, BF16, 1, 2, 128, g, 0, P, None), E.PRISM_ERR_ARG),
+        ("prism_zone_stats_from_norm", (P, P, BF16, 1, 2, 48, g, 0, P, None), E.PRISM_ERR_DTYPE),
+        ("prism_zone_stats_global", (P, P, F32, 0, 2, 64, g, P, None), E.PRISM_ERR_ARG),
         ("prism_dense_attn_bwd", (P, P, P, P, P, P, F32, 1, 2, 256, 64, float("nan"), P, P, P, P, 1 << 30,
                                   None, None), E.PRISM_ERR_ARG),
     ]

@@ -1,0 +1,116 @@
+"""GPU parity of the audio-to-video path: the fused cross-attention that emits the
+per-token norm (prism_a2v_attn_norm), the zone statistics that read that norm map
+(prism_zone_stats_from_norm), and the whole layer driven from audio keys and values,
+against the oracle (a2v_norm, zone_stats on the norm map, prism_forward)."""
+
+from __future__ import annotations
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import prism_oracle as O
+from tests.parity_util import NEAR, STATS_ATOL, STATS_RTOL, assert_close_out, f64, i32, log, selection_from_arrays
+from workloads import workload
+from workloads.synth import make_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from content_adaptive_block_zone_amd import _lib
+    _lib.load()
+
+
+@functools.lru_cache(maxsize=2)
+def inputs(wl: int, heads: int):
+    """The workload's Q/K/V plus seeded audio keys and values N(0, 1) of its audio length."""
+    w = workload(wl)
+    x = make_inputs(w, seed=wl, heads=range(heads), with_grad=False)
+    g = torch.Generator().manual_seed(1000 + wl)
+    shape = (w.B, heads, w.n_audio, w.d)
+    x["ka"] = torch.randn(shape, generator=g).to(torch.bfloat16)
+    x["va"] = torch.randn(shape, generator=g).to(torch.bfloat16)
+    return w, x
+
+
+def layer(wl, heads, **kw):
+    from content_adaptive_block_zone_amd.pipeline import PrismLayer
+    return PrismLayer.for_workload(workload(wl), heads=heads, **kw)
+
+
+@pytest.mark.parametrize("wl,heads,n_sample", [(1, 2, None), (4, 4, 4096)])
+def test_a2v_attn_norm(wl, heads, n_sample):
+    """480p-like (200 audio keys: a ragged last key tile) in full; 2K-like at the
+    benchmark's size on sampled tokens."""
+    w, x = inputs(wl, heads)
+    L = layer(wl, heads)
+    q, ka, va = (x[n].cuda() for n in ("q", "ka", "va"))
+    o = torch.empty_like(q)
+    norm = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    from content_adaptive_block_zone_amd import api
+    api.prism_a2v_attn_norm(q, ka, va, L.scale, norm, o=o)
+    torch.cuda.synchronize()
+    nq, nka, nva = (x[n].float().numpy().astype(np.float64) for n in ("q", "ka", "va"))
+    if n_sample is not None:
+        idx = np.sort(np.random.default_rng(7).choice(w.N, size=n_sample, replace=False))
+        nq = nq[:, :, idx]
+    else:
+        idx = np.arange(w.N)
+    want = O.a2v_norm(nq, nka, nva, L.scale)
+    assert_close_out(f64(norm)[:, :, idx], want, "bf16", f"A2V norm {w.name}")
+    # the optional output rows: their norms are the norm map up to the bf16 rounding of O
+    s = (nq @ np.swapaxes(nka, -1, -2)) * L.scale
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    want_o = (e / e.sum(axis=-1, keepdims=True)) @ nva
+    assert_close_out(f64(o)[:, :, idx], want_o, "bf16", f"A2V output {w.name}")
+    # the norm-only call (no output rows) gives the same norms
+    norm2 = torch.empty_like(norm)
+    api.prism_a2v_attn_norm(q, ka, va, L.scale, norm2)
+    assert torch.equal(norm, norm2)
+
+
+@pytest.mark.parametrize("variance", ["channel", "global"])
+def test_zone_stats_from_norm(variance):
+    w, x = inputs(1, 2)
+    L = layer(1, 2, variance=variance)
+    nv = x["v"].float().numpy().astype(np.float64)
+    a = O.a2v_norm(x["q"].float().numpy(), x["ka"].float().numpy(), x["va"].float().numpy())
+    L.zone_stats_from_norm(x["v"].cuda(), torch.from_numpy(a.astype(np.float32)).cuda())
+    want = O.zone_stats(nv, a.astype(np.float32).astype(np.float64)[..., None], w.grid, w.zone,
+                        global_variance=(variance == "global"))
+    got = f64(L.stats)
+    assert (got[..., 7] == want[..., 7]).all()
+    assert np.allclose(got, want, rtol=STATS_RTOL, atol=STATS_ATOL)
+
+
+def test_layer_driven_from_audio():
+    """A2V norm -> statistics -> shapes -> ... -> O, all on the GPU, against the oracle
+    chain fed the oracle's norm map; compared when no near-tie decision differs."""
+    w, x = inputs(1, 2)
+    L = layer(1, 2)
+    q, k, v, ka, va = (x[n].cuda() for n in ("q", "k", "v", "ka", "va"))
+    norm = L.a2v_norm(q, ka, va)
+    o = L.forward(q, k, v, a2v_norm=norm)
+    torch.cuda.synchronize()
+    n = {k_: x[k_].float().numpy().astype(np.float64) for k_ in ("q", "k", "v", "ka", "va")}
+    a = O.a2v_norm(n["q"], n["ka"], n["va"])
+    f = O.prism_forward(n["q"], n["k"], n["v"], a[..., None], w.grid, w.zone, list(w.cands), w.top_p, w.k_min,
+                        w.k_max)
+    sid = i32(L.shape_id)
+    assert not ((sid != f["shape_id"]) & ~(f["shape_margin"] < NEAR)).any()
+    if (sid != f["shape_id"]).any():
+        pytest.skip("a near-tie zone took the other shape")
+    gsel = selection_from_arrays(i32(L.sel_idx), i32(L.sel_cnt))
+    diff = [k_ for k_ in gsel if gsel[k_].tolist() != f["sel"][k_].tolist()]
+    assert all(f["sel_near"][k_] for k_ in diff)
+    log(f"[a2v layer] {len(diff)} near-tie selection differences")
+    if diff:
+        pytest.skip("a near-tie query block took the other selection")
+    assert_close_out(f64(o), f["o"], "bf16", "layer from audio: O")
