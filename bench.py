@@ -158,6 +158,40 @@ def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
     print("\n".join(lines))
 
 
+def parse_ablation(spec: str, w):
+    """Layer settings for an ablation run (Table 7: Top-k only / Top-p only; Table 9:
+    fixed or random shapes, query/key features, global variance), comma-separated:
+    topk=F (top_p = 1, k = F * live blocks), topp=P (k_min = 1, k_max = nb),
+    fixed=BTxBHxBW, random[=SEED], features=q|k, variance=global.
+    Returns (PrismLayer keyword arguments, shape ids or None)."""
+    from content_adaptive_block_zone_amd.pipeline import random_shape_ids
+    kw, ids = {}, None
+    if not spec:
+        return kw, ids
+    T, H, W = w.grid
+    zt, zh, zw = w.zone
+    nZ = -(-T // zt) * -(-H // zh) * -(-W // zw)
+    nb = nZ * (zt * zh * zw) // w.vol
+    for item in spec.split(","):
+        key, _, val = item.partition("=")
+        if key == "topk":
+            k = max(1, int(round(float(val) * nb)))
+            kw.update(top_p=1.0, k_min=k, k_max=k)
+        elif key == "topp":
+            kw.update(top_p=float(val), k_min=1, k_max=nb)
+        elif key == "fixed":
+            kw.update(cands=[tuple(int(e) for e in val.split("x"))])
+        elif key == "random":
+            ids = random_shape_ids(w.B, w.heads, w.grid, w.zone, list(w.cands), int(val or 0))
+        elif key == "features":
+            kw.update(features=val)
+        elif key == "variance":
+            kw.update(variance=val)
+        else:
+            raise SystemExit(f"unknown ablation setting {item!r}")
+    return kw, ids
+
+
 def density(L):
     import torch
     live = (L.bvalid > 0).sum(dim=-1).double()                      # [B, Hh]
@@ -181,19 +215,29 @@ def run_gpu(args):
     dev = torch.device("cuda:0")
     q, k, v, a2v = (x[n].to(dev) for n in ("q", "k", "v", "a2v"))
     do = x["do"].to(dev) if "do" in x else None
-    L = PrismLayer.for_workload(w, device=dev)
+    kw, shape_ids = parse_ablation(args.ablation, w)
+    L = PrismLayer.for_workload(w, device=dev, **kw)
+    if shape_ids is not None:
+        shape_ids = shape_ids.to(dev)
+    feat = {"v": v, "q": q, "k": k}[L.features]
     stream = torch.cuda.current_stream()
 
     fwd_only = args.forward_only
 
+    def stats_and_shapes():
+        if shape_ids is None:
+            L.zone_stats(feat, a2v)
+            L.assign_shapes()
+        else:
+            L.shape_id.copy_(shape_ids)
+
     def step(ev=None):
         if ev is None:
-            L.forward(q, k, v, a2v)
+            L.forward(q, k, v, a2v, shape_id=shape_ids)
             if not fwd_only:
                 L.backward(do)
             return
-        L.zone_stats(v, a2v)
-        L.assign_shapes()
+        stats_and_shapes()
         L.permute(q, L.qp, block_valid=L.bvalid)
         L.permute(k, L.kp)
         L.permute(v, L.vp)
@@ -280,7 +324,8 @@ def run_gpu(args):
     stage = {}
     names = ["zone_stats", "assign_shapes", "permute_qkv", "select", "attn_fwd", "unpermute_o", "permute_do",
              "attn_bwd", "unpermute_grads"]
-    calls = [lambda: L.zone_stats(v, a2v), L.assign_shapes,
+    calls = [lambda: L.zone_stats(feat, a2v) if shape_ids is None else L.shape_id.copy_(shape_ids),
+             lambda: L.assign_shapes() if shape_ids is None else None,
              lambda: (L.permute(q, L.qp, block_valid=L.bvalid), L.permute(k, L.kp), L.permute(v, L.vp)),
              L.select, L.attn_fwd, lambda: L.permute(L.op, L.o, inverse=True)]
     if fwd_only:
@@ -340,7 +385,8 @@ def run_gpu(args):
                              f"({w.N} tokens), zone {w.zone[0]}x{w.zone[1]}x{w.zone[2]}, {len(w.cands)} shapes of "
                              f"{w.vol} tokens, top-p {w.top_p}, top-k {w.k_min}..{w.k_max}",
                     B=w.B, heads=w.heads, d=w.d, tokens=w.N, nb=L.nb, npad=L.Npad, density=round(dens, 4),
-                    selected_token_pairs=pairs, selected_block_pairs=sums["block_pairs"]),
+                    selected_token_pairs=pairs, selected_block_pairs=sums["block_pairs"],
+                    **({"ablation": args.ablation} if args.ablation else {})),
         ms_per_layer=round(ms_step, 3),
         attn_tflops=round(attn_tflops, 3),
         attn_ms=dict(fwd=round(t_fwd, 4), bwd_pre=round(t_pre, 4), bwd_dkdv=round(t_dkdv, 4), bwd_dq=round(t_dq, 4)),
@@ -407,6 +453,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=4)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--ablation", default="",
+                    help="ablation settings, e.g. topk=0.15 | topp=0.5 | fixed=4x4x4 | random=1 | features=q | "
+                         "variance=global (comma-separated)")
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward chain only (inference; e.g. --workload 5)")
     ap.add_argument("--dense-steps", type=int, default=1)
