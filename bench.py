@@ -105,7 +105,7 @@ def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
     kernel scaled by what the counters read for the plain copy (written to stdout)."""
     import csv
     import glob
-    lines = ["# Commands (run from the repository root on one MI355X)"]
+    lines = ["# Commands (one MI355X, repository at /root/repo; rocprofv3 runs from /tmp)"]
     lines += [f"#   {c}" for c in commands]
     lines.append("")
     st = glob.glob(os.path.join(stats_dir, "*kernel_stats.csv"))[0]
