@@ -72,14 +72,11 @@ COPY_MIB = 256
 
 
 def attn_source_sha256():
-    """Hash of the attention kernels' source: recorded counter traffic is reported only
-    while the kernels are the ones it was measured on."""
+    """Hash of the attention kernels' source file: recorded counter traffic is reported
+    only while the kernels are the ones it was measured on."""
     import hashlib
-    h = hashlib.sha256()
-    for f in ("attn_mfma.hip", "prism_internal.h"):
-        with open(os.path.join(ROOT, "content_adaptive_block_zone_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()
+    with open(os.path.join(ROOT, "content_adaptive_block_zone_amd", "csrc", "attn_mfma.hip"), "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
 
 
 def recorded_traffic(kernel):

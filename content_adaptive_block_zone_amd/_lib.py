@@ -49,6 +49,9 @@ PROTOTYPES = {
     "prism_assign_shapes": (c_int, [_P, c_int, c_int, _GP, _SP, _SHP, _P, _P, _P]),
     "prism_permute": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _SP, _P, c_int, _P, _P]),
     "prism_select_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "prism_tiles_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "prism_blocks_to_tiles": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, _P, _P, _P, _P, _P,
+                                      _P, c_size_t, _P]),
     "prism_select_blocks": (c_int, [_P, _P, c_int, _P, c_int, c_int, c_int, c_int, c_int, c_float, _SLP,
                                     _P, _P, _P, _P, _P, _P, c_size_t, _P]),
     "prism_fwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),

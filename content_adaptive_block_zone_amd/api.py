@@ -209,6 +209,26 @@ def prism_select_blocks(qp: torch.Tensor, kp: torch.Tensor, block_valid: torch.T
         workspace.numel(), _stream(stream)), "prism_select_blocks")
 
 
+def prism_tiles_workspace_size(B: int, Hh: int, nb: int, vol: int) -> int:
+    return int(load().prism_tiles_workspace_size(B, Hh, nb, vol))
+
+
+def prism_blocks_to_tiles(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, vol: int, tile_valid, tile_idx, tile_cnt,
+                          tile_rev_ptr, tile_rev_idx, workspace, stream=None) -> None:
+    B, Hh, nb = block_valid.shape
+    km = sel_idx.shape[-1]
+    g = vol // 64
+    nt, kt = nb * g, km * g
+    check(load().prism_blocks_to_tiles(
+        _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"), _ptr(sel_idx, torch.int32, (B, Hh, nb, km), "sel_idx"),
+        _ptr(sel_cnt, torch.int32, (B, Hh, nb), "sel_cnt"), _ptr(rev_ptr, torch.int32, (B, Hh, nb + 1), "rev_ptr"),
+        _ptr(rev_idx, torch.int32, (B, Hh, nb * km), "rev_idx"), B, Hh, nb, vol, km,
+        _ptr(tile_valid, torch.int32, (B, Hh, nt), "tile_valid"), _ptr(tile_idx, torch.int32, (B, Hh, nt, kt), "tile_idx"),
+        _ptr(tile_cnt, torch.int32, (B, Hh, nt), "tile_cnt"), _ptr(tile_rev_ptr, torch.int32, (B, Hh, nt + 1), "tile_rev_ptr"),
+        _ptr(tile_rev_idx, torch.int32, (B, Hh, nt * kt), "tile_rev_idx"), _ptr(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _stream(stream)), "prism_blocks_to_tiles")
+
+
 def prism_sparse_attn_fwd(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, scale: float, op, lse,
                           workspace=None, stream=None) -> None:
     B, Hh, npad, d = qp.shape

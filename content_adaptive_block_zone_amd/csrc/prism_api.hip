@@ -345,4 +345,30 @@ prism_status prism_a2v_attn_norm(const void* q, const void* ka, const void* va, 
   return launched(launch_attn_fwd_mfma(a, stream), who);
 }
 
+size_t prism_tiles_workspace_size(int B, int Hh, int nb, int vol) {
+  if (B < 1 || Hh < 1 || nb < 1 || vol < kTileRows || vol % kTileRows != 0) return 0;
+  return tiles_ws_bytes(B * Hh, nb, vol);
+}
+
+prism_status prism_blocks_to_tiles(const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   const int32_t* rev_ptr, const int32_t* rev_idx, int B, int Hh, int nb, int vol,
+                                   int k_max, int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt,
+                                   int32_t* tile_rev_ptr, int32_t* tile_rev_idx, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream) {
+  const char* who = "prism_blocks_to_tiles";
+  if (!block_valid || !sel_idx || !sel_cnt || !rev_ptr || !rev_idx || !tile_valid || !tile_idx || !tile_cnt ||
+      !tile_rev_ptr || !tile_rev_idx || !workspace)
+    return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1 || nb < 1 || k_max < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, nb, k_max must be >= 1", who);
+  if (vol < kTileRows || vol % kTileRows != 0 || vol > 4096)
+    return fail(PRISM_ERR_SHAPE, "%s: vol=%d must be a multiple of %d in [%d, 4096]", who, vol, kTileRows, kTileRows);
+  const int g = vol / kTileRows;
+  if (int64_t(B) * Hh * nb * g * int64_t(k_max) * g > (int64_t(1) << 31))
+    return fail(PRISM_ERR_SHAPE, "%s: tile lists exceed 2^31 entries", who);
+  if (ws_bytes < tiles_ws_bytes(B * Hh, nb, vol)) return fail(PRISM_ERR_ARG, "%s: workspace too small", who);
+  return launched(launch_blocks_to_tiles(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, B * Hh, nb, vol, k_max,
+                                         tile_valid, tile_idx, tile_cnt, tile_rev_ptr, tile_rev_idx, workspace, stream),
+                  who);
+}
+
 }  // extern "C"

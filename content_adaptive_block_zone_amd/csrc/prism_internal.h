@@ -207,6 +207,11 @@ size_t select_ws_bytes(int BH, int nb, int d);
 // scalar kernels.  The forward needs no scratch; the backward's holds D (one float per row).
 size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
 size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
+size_t tiles_ws_bytes(int BH, int nb, int vol);
+hipError_t launch_blocks_to_tiles(const int32_t* bvalid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                  const int32_t* rev_ptr, const int32_t* rev_idx, int BH, int nb, int vol, int k_max,
+                                  int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt, int32_t* tile_rev_ptr,
+                                  int32_t* tile_rev_idx, void* ws, hipStream_t s);
 hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);

@@ -1,0 +1,158 @@
+// Blocks of 128 or 256 tokens (the C_128 / C_256 candidate sets of Tables 9 and 11) run
+// through the 64-row attention kernels as runs of 2 or 4 consecutive 64-row tiles.  The
+// selection stays at block level (pooling, scores and the Top-k/Top-p cut are per block);
+// these kernels expand it, and its reverse index, to tile level:
+//   query tile (I, u) lists every live tile of every block J that block I selected;
+//   key tile (J, v) lists every live tile of every block I that selected block J.
+// A block's valid rows come first (then its padding), so its live tiles are the first
+// ceil(n/64); fully padded tiles appear in no list.  Lists stay ascending because the
+// block lists are ascending.
+#include "prism_internal.h"
+
+namespace prism {
+namespace {
+
+constexpr int NT = 256;
+constexpr int TT = 64;  // rows per tile
+
+__device__ __forceinline__ int live_tiles(int n) { return (n + TT - 1) / TT; }
+
+__global__ void k_tile_valid(const int32_t* __restrict__ bvalid, size_t total_tiles, int g,
+                             int32_t* __restrict__ tvalid) {
+  const size_t t = blockIdx.x * size_t(blockDim.x) + threadIdx.x;
+  if (t >= total_tiles) return;
+  const int n = bvalid[t / g] - TT * int(t % g);
+  tvalid[t] = n < 0 ? 0 : (n > TT ? TT : n);
+}
+
+// One workgroup per (block, head): the expanded list of `cnt` blocks taken from `lst`,
+// written to every live tile of the block (or, for a dead tile, an empty list).
+// Offsets come from an exclusive scan of the listed blocks' live-tile counts, taken in
+// chunks of NT with a running carry.
+__device__ void expand_rows(const int32_t* __restrict__ lst, int cnt, const int32_t* __restrict__ bv_head,
+                            int own_live, int g, int cap, int32_t* __restrict__ out_rows,
+                            int32_t* __restrict__ out_cnt, int* red) {
+  int carry = 0;
+  for (int k0 = 0; k0 < cnt; k0 += NT) {
+    const int k = k0 + int(threadIdx.x);
+    const int J = k < cnt ? lst[k] : 0;
+    const int c = k < cnt ? live_tiles(bv_head[J]) : 0;
+    int tot;
+    const int off = carry + block_excl_scan<NT>(c, red, &tot);
+    for (int u = 0; u < own_live; ++u)
+      for (int v = 0; v < c; ++v) out_rows[size_t(u) * cap + off + v] = J * g + v;
+    carry += tot;
+    __syncthreads();
+  }
+  // empty slots and dead tiles
+  for (int u = 0; u < g; ++u) {
+    const int used = u < own_live ? carry : 0;
+    for (int s = used + int(threadIdx.x); s < cap; s += NT) out_rows[size_t(u) * cap + s] = -1;
+    if (threadIdx.x == 0) out_cnt[u] = used;
+  }
+}
+
+__global__ __launch_bounds__(NT) void k_tile_lists(const int32_t* __restrict__ bvalid,
+                                                   const int32_t* __restrict__ sel_idx,
+                                                   const int32_t* __restrict__ sel_cnt, int nb, int g, int k_max,
+                                                   int32_t* __restrict__ tile_idx, int32_t* __restrict__ tile_cnt) {
+  __shared__ int red[8];
+  const int I = blockIdx.x, bh = blockIdx.y;
+  const int32_t* bv = bvalid + size_t(bh) * nb;
+  const int own_live = live_tiles(bv[I]);
+  const int cnt = own_live > 0 ? sel_cnt[size_t(bh) * nb + I] : 0;
+  const int cap = k_max * g;
+  const size_t t0 = size_t(bh) * nb * g + size_t(I) * g;
+  expand_rows(sel_idx + (size_t(bh) * nb + I) * k_max, cnt, bv, own_live, g, cap, tile_idx + t0 * cap,
+              tile_cnt + t0, red);
+}
+
+// Reverse counts: key tile (J, v) is listed by every live tile of every block that selected J.
+__global__ __launch_bounds__(64) void k_tile_rev_count(const int32_t* __restrict__ bvalid,
+                                                       const int32_t* __restrict__ rev_ptr,
+                                                       const int32_t* __restrict__ rev_idx, int nb, int g, int k_max,
+                                                       int32_t* __restrict__ rcnt) {
+  const int J = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
+  const int32_t* bv = bvalid + size_t(bh) * nb;
+  const int32_t* rp = rev_ptr + size_t(bh) * (nb + 1);
+  const int32_t* ri = rev_idx + size_t(bh) * nb * k_max;
+  int c = 0;
+  for (int k = rp[J] + lane; k < rp[J + 1]; k += 64) c += live_tiles(bv[ri[k]]);
+  c = wave_sum_i(c);
+  const int live = live_tiles(bv[J]);
+  if (lane < g) rcnt[(size_t(bh) * nb + J) * g + lane] = lane < live ? c : 0;
+}
+
+__global__ __launch_bounds__(1024) void k_tile_rev_scan(const int32_t* __restrict__ rcnt, int nt,
+                                                        int32_t* __restrict__ tile_rev_ptr) {
+  __shared__ int red[20];
+  const int bh = blockIdx.x;
+  const int R = (nt + 1023) / 1024;
+  const int t0 = min(nt, int(threadIdx.x) * R), t1 = min(nt, t0 + R);
+  const int32_t* c = rcnt + size_t(bh) * nt;
+  int s = 0;
+  for (int t = t0; t < t1; ++t) s += c[t];
+  int tot;
+  int off = block_excl_scan<1024>(s, red, &tot);
+  int32_t* rp = tile_rev_ptr + size_t(bh) * (nt + 1);
+  for (int t = t0; t < t1; ++t) {
+    rp[t] = off;
+    off += c[t];
+  }
+  if (threadIdx.x == 0) rp[nt] = tot;
+}
+
+__global__ __launch_bounds__(NT) void k_tile_rev_fill(const int32_t* __restrict__ bvalid,
+                                                      const int32_t* __restrict__ rev_ptr,
+                                                      const int32_t* __restrict__ rev_idx, int nb, int g, int k_max,
+                                                      const int32_t* __restrict__ tile_rev_ptr,
+                                                      int32_t* __restrict__ tile_rev_idx) {
+  __shared__ int red[8];
+  const int J = blockIdx.x, bh = blockIdx.y;
+  const int32_t* bv = bvalid + size_t(bh) * nb;
+  const int32_t* rp = rev_ptr + size_t(bh) * (nb + 1);
+  const int32_t* ri = rev_idx + size_t(bh) * nb * k_max;
+  const int nt = nb * g;
+  const int32_t* trp = tile_rev_ptr + size_t(bh) * (nt + 1);
+  int32_t* out = tile_rev_idx + size_t(bh) * nt * (size_t(k_max) * g);
+  const int live = live_tiles(bv[J]);
+  const int k_beg = rp[J], cnt = rp[J + 1] - rp[J];
+  int carry = 0;
+  for (int k0 = 0; k0 < cnt; k0 += NT) {
+    const int k = k0 + int(threadIdx.x);
+    const int I = k < cnt ? ri[k_beg + k] : 0;
+    const int c = k < cnt ? live_tiles(bv[I]) : 0;
+    int tot;
+    const int off = carry + block_excl_scan<NT>(c, red, &tot);
+    for (int v = 0; v < live; ++v) {
+      const int base = trp[J * g + v];
+      for (int u = 0; u < c; ++u) out[base + off + u] = I * g + u;
+    }
+    carry += tot;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+size_t tiles_ws_bytes(int BH, int nb, int vol) { return align256(size_t(BH) * nb * (vol / TT) * 4); }
+
+hipError_t launch_blocks_to_tiles(const int32_t* bvalid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                  const int32_t* rev_ptr, const int32_t* rev_idx, int BH, int nb, int vol, int k_max,
+                                  int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt, int32_t* tile_rev_ptr,
+                                  int32_t* tile_rev_idx, void* ws, hipStream_t s) {
+  const int g = vol / TT;
+  const int nt = nb * g;
+  const size_t total = size_t(BH) * nt;
+  int32_t* rcnt = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(k_tile_valid, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, bvalid, total, g, tile_valid);
+  hipLaunchKernelGGL(k_tile_lists, dim3(nb, BH), dim3(NT), 0, s, bvalid, sel_idx, sel_cnt, nb, g, k_max, tile_idx,
+                     tile_cnt);
+  hipLaunchKernelGGL(k_tile_rev_count, dim3(nb, BH), dim3(64), 0, s, bvalid, rev_ptr, rev_idx, nb, g, k_max, rcnt);
+  hipLaunchKernelGGL(k_tile_rev_scan, dim3(BH), dim3(1024), 0, s, rcnt, nt, tile_rev_ptr);
+  hipLaunchKernelGGL(k_tile_rev_fill, dim3(nb, BH), dim3(NT), 0, s, bvalid, rev_ptr, rev_idx, nb, g, k_max,
+                     tile_rev_ptr, tile_rev_idx);
+  return hipGetLastError();
+}
+
+}  // namespace prism

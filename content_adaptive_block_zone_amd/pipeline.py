@@ -86,6 +86,20 @@ class PrismLayer:
         self.ws_bwd = e(api.prism_bwd_workspace_size(B, Hh, self.nb, self.vol, d, dtype), dt=torch.uint8)
         self.o = e(B_, H_, self.N, d)
         self._grad_bufs = None
+        # Blocks of more than 64 tokens run the attention on 64-row tiles (vol/64 per block).
+        self.g = self.vol // 64 if self.vol > 64 else 1
+        if self.vol > 64:
+            if self.vol % 64:
+                raise ValueError(f"block volume {self.vol} above 64 must be a multiple of 64")
+            nt, kt = self.nb * self.g, self.k_max * self.g
+            self.tile_valid = e(B_, H_, nt, dt=i32)
+            self.tile_idx = e(B_, H_, nt, kt, dt=i32)
+            self.tile_cnt = e(B_, H_, nt, dt=i32)
+            self.tile_rev_ptr = e(B_, H_, nt + 1, dt=i32)
+            self.tile_rev_idx = e(B_, H_, nt * kt, dt=i32)
+            self.ws_tiles = e(api.prism_tiles_workspace_size(B, Hh, self.nb, self.vol), dt=torch.uint8)
+            self.ws_fwd = e(max(1, api.prism_fwd_workspace_size(B, Hh, nt, 64, d, dtype)), dt=torch.uint8)
+            self.ws_bwd = e(api.prism_bwd_workspace_size(B, Hh, nt, 64, d, dtype), dt=torch.uint8)
 
     def _grads(self):
         if self._grad_bufs is None:
@@ -122,16 +136,28 @@ class PrismLayer:
         api.prism_select_blocks(self.qp, self.kp, self.bvalid, self.vol, self.scale, self.sel_params,
                                 self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.ws_sel,
                                 self.sel_margin)
+        if self.vol > 64:
+            api.prism_blocks_to_tiles(self.bvalid, self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.vol,
+                                      self.tile_valid, self.tile_idx, self.tile_cnt, self.tile_rev_ptr,
+                                      self.tile_rev_idx, self.ws_tiles)
+
+    def _attn_lists(self):
+        """(valid counts, lists, counts, reverse pointers, reverse lists, rows per unit) the
+        attention runs on: the blocks themselves, or their 64-row tiles."""
+        if self.vol > 64:
+            return (self.tile_valid, self.tile_idx, self.tile_cnt, self.tile_rev_ptr, self.tile_rev_idx, 64)
+        return (self.bvalid, self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.vol)
 
     def attn_fwd(self):
-        api.prism_sparse_attn_fwd(self.qp, self.kp, self.vp, self.bvalid, self.sel_idx, self.sel_cnt,
-                                  self.vol, self.scale, self.op, self.lse, self.ws_fwd)
+        bv, idx, cnt, _, _, vol = self._attn_lists()
+        api.prism_sparse_attn_fwd(self.qp, self.kp, self.vp, bv, idx, cnt, vol, self.scale, self.op, self.lse,
+                                  self.ws_fwd)
 
     def attn_bwd(self, marks=None):
         g = self._grads()
-        api.prism_sparse_attn_bwd(self.qp, self.kp, self.vp, self.op, g["dop"], self.lse, self.bvalid,
-                                  self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.vol, self.scale,
-                                  g["dqp"], g["dkp"], g["dvp"], self.ws_bwd, marks)
+        bv, idx, cnt, rp, ri, vol = self._attn_lists()
+        api.prism_sparse_attn_bwd(self.qp, self.kp, self.vp, self.op, g["dop"], self.lse, bv, idx, cnt, rp, ri, vol,
+                                  self.scale, g["dqp"], g["dkp"], g["dvp"], self.ws_bwd, marks)
 
     # ---- whole layer
     def forward(self, q, k, v, a2v=None, shape_id: Optional[torch.Tensor] = None,

@@ -176,6 +176,27 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
                                  float* sel_margin, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* Blocks of 128 or 256 tokens (the C_128 / C_256 candidate sets, Tables 9 and 11) run
+ * through the attention as runs of vol/64 consecutive 64-row tiles.  This call expands a
+ * block-level selection (from prism_select_blocks with that vol) and its reverse index to
+ * tile level, for prism_sparse_attn_fwd / _bwd called with vol = 64, nb_t = nb*vol/64
+ * tiles and k_max_t = k_max*vol/64:
+ *   tile_valid   out int32 [B][Hh][nb_t]: valid rows of each tile (a block's valid rows
+ *                come first, so its live tiles are the first ceil(n/64));
+ *   tile_idx     out int32 [B][Hh][nb_t][k_max_t], ascending, -1 padded; tile_cnt [B][Hh][nb_t]:
+ *                query tile (I,u) lists every live tile of every block I selected
+ *                (nothing for a tile with no valid row);
+ *   tile_rev_ptr out int32 [B][Hh][nb_t+1], tile_rev_idx out [B][Hh][nb_t*k_max_t]: the
+ *                transpose of tile_idx, ascending per key tile.
+ * vol must be a multiple of 64 in [64, 4096] (PRISM_ERR_SHAPE); workspace:
+ * prism_tiles_workspace_size() bytes of device scratch. */
+size_t prism_tiles_workspace_size(int B, int Hh, int nb, int vol);
+prism_status prism_blocks_to_tiles(const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                   const int32_t* rev_ptr, const int32_t* rev_idx, int B, int Hh, int nb, int vol,
+                                   int k_max, int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt,
+                                   int32_t* tile_rev_ptr, int32_t* tile_rev_idx, void* workspace, size_t ws_bytes,
+                                   hipStream_t stream);
+
 /* Block-sparse attention forward (Figure 2 caption).  Query row i of block I attends
  * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:
  *   O_i = softmax_j(scale q_i.k_j) v_j,  lse_i = ln sum_j exp(scale q_i.k_j).

@@ -120,6 +120,12 @@ def test_calls_validate_before_launch(lib):
         ("prism_zone_stats_from_norm", (P, None, BF16, 1, 2, 128, g, 0, P, None), E.PRISM_ERR_ARG),
         ("prism_zone_stats_from_norm", (P, P, BF16, 1, 2, 48, g, 0, P, None), E.PRISM_ERR_DTYPE),
         ("prism_zone_stats_global", (P, P, F32, 0, 2, 64, g, P, None), E.PRISM_ERR_ARG),
+        ("prism_blocks_to_tiles", (P, P, P, P, P, 1, 2, 16, 96, 4, P, P, P, P, P, P, 1 << 20, None),
+         E.PRISM_ERR_SHAPE),                                                           # vol not a multiple of 64
+        ("prism_blocks_to_tiles", (P, P, P, P, P, 1, 2, 16, 128, 4, P, P, P, P, P, P, 4, None),
+         E.PRISM_ERR_ARG),                                                             # workspace too small
+        ("prism_blocks_to_tiles", (P, None, P, P, P, 1, 2, 16, 128, 4, P, P, P, P, P, P, 1 << 20, None),
+         E.PRISM_ERR_ARG),
         ("prism_dense_attn_bwd", (P, P, P, P, P, P, F32, 1, 2, 256, 64, float("nan"), P, P, P, P, 1 << 30,
                                   None, None), E.PRISM_ERR_ARG),
     ]

@@ -54,6 +54,9 @@ def test_table11_shape_codes_have_equal_volume_per_set():
     for r in rows:
         assert abs(sum(r) - 100.0) < 1e-9
     assert O.candidate_volume(CANDS_64) == 64 and O.candidate_volume(CANDS_16) == 16
+    # the 128- and 256-token workload sets are exactly the table's codes, in its order
+    from workloads import CANDS_128, CANDS_256
+    assert CANDS_128 == sets["C_128"][1] and CANDS_256 == sets["C_256"][1]
 
 
 # ------------------------------------------------------------------ zones
@@ -458,6 +461,24 @@ def test_all_blocks_selected_equals_textbook_dense_attention():
     assert np.allclose(O.unpermute(lse[..., None], tok, N)[..., 0], lse_want, atol=1e-12)
     od, ld = O.dense_attn_fwd(q, k, v, 0.3)
     assert np.allclose(od, want, atol=1e-12) and np.allclose(ld, lse_want, atol=1e-12)
+
+
+@pytest.mark.parametrize("cands", [[(2, 8, 8), (4, 4, 8), (4, 8, 4)], [(4, 8, 8)]])
+def test_large_blocks_all_selected_equal_dense_attention(cands):
+    """128- and 256-token blocks (cut by the grid edge, so with padding) through the whole
+    chain with every live block selected reproduce dense attention over the real tokens."""
+    rng = np.random.default_rng(21)
+    grid, zone = (6, 10, 12), (4, 16, 16)
+    N = 6 * 10 * 12
+    q, k, v = (rng.standard_normal((1, 2, N, 8)) for _ in range(3))
+    a2v = rng.standard_normal((1, 2, N, 8))
+    vol = O.candidate_volume(cands)
+    f = O.prism_forward(q, k, v, a2v, grid, zone, cands, 1.0, 10 ** 6, 10 ** 6, scale=0.4, dtype=np.float64)
+    assert f["vol"] == vol and f["bvalid"].max() <= vol
+    tok = f["tok"]
+    assert sorted(tok[0, 0][tok[0, 0] >= 0].tolist()) == list(range(N))
+    want, _ = O.dense_attn_fwd(q, k, v, 0.4)
+    assert np.allclose(f["o"], want, atol=1e-12)
 
 
 def test_single_selected_block_is_attention_inside_that_block():

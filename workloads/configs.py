@@ -26,6 +26,13 @@ CANDS_64: List[Shape] = [
 ]
 
 
+# The 128- and 256-token candidate sets of the block-shape proportion table (Table 11
+# codes b_T b_H b_W, list order = the table's column order).  In the 4x16x16 zones of the
+# bf16 workloads only shapes with b_T <= 4 tile a zone: 288, 448, 484 and 488.
+CANDS_128: List[Shape] = [(2, 8, 8), (8, 2, 8), (8, 8, 2), (4, 4, 8), (4, 8, 4), (8, 4, 4)]
+CANDS_256: List[Shape] = [(4, 8, 8), (8, 4, 8), (8, 8, 4)]
+
+
 @dataclass(frozen=True)
 class FieldRecipe:
     """Recipe of the smooth Q/K/V fields: a sum of M sinusoids per (b, h, channel).
