@@ -231,6 +231,21 @@ def zone_stats_bruteforce(v: np.ndarray, a2v: np.ndarray, grid, zone, eps: float
     return out
 
 
+def zone_activity(v: np.ndarray, grid, zone) -> np.ndarray:
+    """Video activity of every zone, float64 [B, Hh, nZ]: the channel-mean lag-one
+    semivariance summed over the three axes, sum_d mean_c gamma_{d,c} (the magnitude that
+    the per-axis shares of zone_stats normalise away).  Used by the multi-volume reading
+    (assign_shapes_multi)."""
+    v = np.asarray(v, dtype=np.float64)
+    B, Hh, N, C = v.shape
+    out = np.zeros((B, Hh, num_zones(grid, zone)))
+    for b in range(B):
+        for h in range(Hh):
+            Vz, mask = zone_view(v[b, h], grid, zone)
+            out[b, h] = directional_semivariance(Vz, mask).mean(axis=2).sum(axis=1)
+    return out
+
+
 def a2v_norm(q: np.ndarray, ka: np.ndarray, va: np.ndarray, scale: Optional[float] = None) -> np.ndarray:
     """Per-token norm of the audio-to-video cross-attention output (abstract: the shapes
     follow the feature norms of the A2V cross-attention output): video queries q
@@ -318,6 +333,60 @@ def assign_shapes(stats: np.ndarray, cands: Sequence[Shape], zone, p: ShapeParam
     return quantize_shape(lam, cands, zone, dtype)
 
 
+TAU_128 = 1.0      # zones with activity below this take 128-token blocks ...
+TAU_256 = 0.5      # ... and below this 256-token blocks
+
+
+def assign_shapes_multi(stats: np.ndarray, vact: np.ndarray, cands: Sequence[Shape], zone,
+                        p: ShapeParams = ShapeParams(), tau_128: float = TAU_128, tau_256: float = TAU_256,
+                        dtype=np.float32):
+    """Shapes from a candidate list that mixes 64-, 128- and 256-token shapes (Tables 9 and
+    11: sets C_64, C_128, C_256; Table 10 caption: thresholds tau_128 / tau_256 of the block
+    shape assignment).  The pages give no rule for the volume; reading:
+        rho_z = vact_z / (mean of vact over the head's zones)   (0 if that mean is 0)
+        act_z = rho_z + a-bar_z                                  (a-bar: the audio gate)
+        volume 256 if act_z < tau_256, 128 if act_z < tau_128, else 64,
+    falling back to the next smaller volume when no shape of the chosen volume tiles the
+    zone; the shape is then the Eq. 7 choice (quantize_shape) among the candidates of that
+    volume, with lambda built for that volume.  Smooth zones without audio coupling take
+    the largest blocks.  Returns (shape id into cands, margin), the margin being the
+    smaller of the shape margin and the relative distance |act - tau| / tau to each
+    threshold, so that a near-threshold zone counts as a near-tie."""
+    abar, _, g = shape_guidance(stats, p, dtype)
+    vact = np.asarray(vact).astype(dtype)
+    n = np.asarray(stats)[..., 7]
+    live = n > 0
+    cntz = np.maximum(live.sum(axis=-1), 1).astype(dtype)
+    mean = (np.where(live, vact, dtype(0)).sum(axis=-1, dtype=dtype) / cntz).astype(dtype)   # [B, Hh]
+    with np.errstate(invalid="ignore", divide="ignore"):
+        rho = np.where(mean[..., None] > 0, vact / mean[..., None], dtype(0)).astype(dtype)
+    act = (rho + abar).astype(dtype)
+    vols = sorted({bt * bh * bw for (bt, bh, bw) in cands})
+    if 64 not in vols:
+        raise ValueError("the candidate list needs 64-token shapes")
+
+    def has_feasible(vol):
+        return any(feasible(c, zone) and c[0] * c[1] * c[2] == vol for c in cands)
+
+    B, Hh, nZ = act.shape
+    sid = np.zeros((B, Hh, nZ), dtype=np.int32)
+    margin = np.zeros((B, Hh, nZ))
+    for b in range(B):
+        for h in range(Hh):
+            for z in range(nZ):
+                a = act[b, h, z]
+                want = 256 if a < dtype(tau_256) else (128 if a < dtype(tau_128) else 64)
+                while want > 64 and not (want in vols and has_feasible(want)):
+                    want //= 2
+                idx = [i for i, c in enumerate(cands) if c[0] * c[1] * c[2] == want]
+                lam = ideal_log_extents(g[b, h, z][None], want, p.alpha, dtype)
+                j, m = quantize_shape(lam, [cands[i] for i in idx], zone, dtype)
+                sid[b, h, z] = idx[int(j[0])]
+                thr = [abs(float(a) - t) / t for t in (tau_128, tau_256)]
+                margin[b, h, z] = min([float(m[0])] + thr)
+    return sid, margin
+
+
 # =================================================================================
 # Permutation into blocks (abstract: tokens within each block stay coherent, so each
 # block must be a contiguous run; Figure 2 caption).
@@ -333,9 +402,7 @@ def slot_map(grid, zone, cands: Sequence[Shape], shape_id: np.ndarray) -> np.nda
     T, H, W = grid
     zt, zh, zw = zone
     nzt, nzh, nzw = zone_counts(grid, zone)
-    S = candidate_volume(cands)
     Vz = zt * zh * zw
-    nbz = Vz // S
     sid = np.asarray(shape_id)
     B, Hh, nZ = sid.shape
     out = np.full((B, Hh, nZ * Vz), -1, dtype=np.int64)
@@ -344,6 +411,8 @@ def slot_map(grid, zone, cands: Sequence[Shape], shape_id: np.ndarray) -> np.nda
         for b in range(B):
             for h in range(Hh):
                 bt, bh, bw = cands[int(sid[b, h, z])]
+                S = bt * bh * bw                      # this zone's block volume
+                nbz = Vz // S
                 nbh, nbw = zh // bh, zw // bw
                 for blk in range(nbz):
                     t0 = it * zt + (blk // (nbh * nbw)) * bt
@@ -365,6 +434,27 @@ def block_valid(tok: np.ndarray, vol: int) -> np.ndarray:
     """Valid-slot count of every block, int32 [B, Hh, nb] (0 marks a dead block)."""
     B, Hh, Np = tok.shape
     return (tok >= 0).reshape(B, Hh, Np // vol, vol).sum(axis=-1).astype(np.int32)
+
+
+def block_heads(tok: np.ndarray, shape_id: np.ndarray, cands: Sequence[Shape], zone, unit: int = 64) -> np.ndarray:
+    """Block-level valid counts for zones of different block volumes, int32
+    [B, Hh, Npad/unit]: a block is identified by its first unit (a run of `unit` slots),
+    which holds the whole block's valid count; its other units hold 0.  Because a block's
+    valid slots come first, its valid rows are the n rows from its first unit on, so
+    pool_blocks, the selection and sparse attention take these counts with vol = unit."""
+    B, Hh, Np = tok.shape
+    Vz = zone[0] * zone[1] * zone[2]
+    per_unit = block_valid(tok, unit)
+    out = np.zeros_like(per_unit)
+    upz = Vz // unit
+    for b in range(B):
+        for h in range(Hh):
+            for z in range(Np // Vz):
+                bt, bh, bw = cands[int(shape_id[b, h, z])]
+                g = bt * bh * bw // unit
+                for u0 in range(z * upz, (z + 1) * upz, g):
+                    out[b, h, u0] = per_unit[b, h, u0:u0 + g].sum()
+    return out
 
 
 def permute(x: np.ndarray, tok: np.ndarray) -> np.ndarray:
@@ -705,26 +795,33 @@ def dense_attn_bwd(q, k, v, o, do, lse, scale: float):
 
 def prism_forward(q, k, v, a2v, grid, zone, cands, top_p, k_min, k_max, scale=None,
                   shape_params: ShapeParams = ShapeParams(), dtype=np.float32,
-                  features: str = "v", global_variance: bool = False, shape_id=None):
+                  features: str = "v", global_variance: bool = False, shape_id=None, mixed=None):
     """The whole forward chain.  The options are the block-shape ablations of Table 9:
     features "q" / "k" take the query / key features instead of the values for the
     variance; global_variance takes it across all channels jointly; shape_id, when
     given, replaces the statistics and shape assignment (random or fixed shapes, whose
     draws are inputs).  Top-k only / Top-p only (Table 7) are plain parameter choices:
-    top_p = 1 with k_min = k_max = k, or k_min = 1 with k_max >= the live block count."""
+    top_p = 1 with k_min = k_max = k, or k_min = 1 with k_max >= the live block count.
+    mixed = (tau_128, tau_256): cands mixes block volumes; shapes by assign_shapes_multi,
+    blocks identified by their first 64-slot unit (block_heads) and everything downstream
+    run with vol = 64."""
     q, k, v, a2v = (np.asarray(a, dtype=np.float64) for a in (q, k, v, a2v))
     B, Hh, N, C = q.shape
     scale = 1.0 / math.sqrt(C) if scale is None else scale
-    vol = candidate_volume(cands)
+    vol = 64 if mixed is not None else candidate_volume(cands)
     if shape_id is None:
         feat = {"v": v, "q": q, "k": k}[features]
         stats = zone_stats(feat, a2v, grid, zone, global_variance=global_variance)
-        sid, margin = assign_shapes(stats.astype(np.float32), cands, zone, shape_params, dtype)
+        if mixed is not None:
+            sid, margin = assign_shapes_multi(stats.astype(np.float32), zone_activity(feat, grid, zone), cands, zone,
+                                              shape_params, mixed[0], mixed[1], dtype)
+        else:
+            sid, margin = assign_shapes(stats.astype(np.float32), cands, zone, shape_params, dtype)
     else:
         stats, sid = None, np.asarray(shape_id, dtype=np.int32)
         margin = np.full(sid.shape, np.inf)
     tok = slot_map(grid, zone, cands, sid)
-    bv = block_valid(tok, vol)
+    bv = block_heads(tok, sid, cands, zone) if mixed is not None else block_valid(tok, vol)
     qp, kp, vp = permute(q, tok), permute(k, tok), permute(v, tok)
     qbar, kbar = pool_blocks(qp, bv, vol), pool_blocks(kp, bv, vol)
     sel, near = select_blocks(qbar.astype(np.float32), kbar.astype(np.float32), bv, scale,

@@ -157,6 +157,77 @@ def test_zone_stats_from_norm_map_equals_from_rows():
                            O.zone_stats(V, a, grid, zone, global_variance=gv), rtol=1e-13, atol=1e-13)
 
 
+def test_zone_activity_closed_form():
+    # channel 0 varies along t (amplitude 2, period 3), channel 1 along h (amplitude 0.5,
+    # period 5): activity = mean over the 2 channels of each axis's semivariance, summed
+    grid = zone = (4, 16, 16)
+    w1, w2 = 2 * math.pi / 3, 2 * math.pi / 5
+    V = _grid_field(grid, lambda t, h, w, c: 2.0 * np.sin(w1 * t + 0.2) if c == 0 else 0.5 * np.sin(w2 * h + 0.9),
+                    C=2)
+    act = O.zone_activity(V, grid, zone)[0, 0, 0]
+    want = (4.0 * math.sin(w1 / 2) ** 2 + 0.25 * math.sin(w2 / 2) ** 2) / 2
+    assert abs(act - want) < 1e-12
+    assert O.zone_activity(np.ones_like(V), grid, zone)[0, 0, 0] == 0.0
+
+
+def _multi_stats(rows):
+    """stats rows [r_t, r_h, r_w, g_t, g_h, g_w, m, n] for one head, as [1, 1, nZ, 8]."""
+    return np.array(rows, dtype=np.float64)[None, None]
+
+
+def test_assign_multi_volume_classes_and_fallback():
+    from workloads import CANDS_128, CANDS_256
+    cands = CANDS_64 + CANDS_128 + CANDS_256
+    zone = (4, 16, 16)
+    iso = [1 / 3, 1 / 3, 1 / 3, 1.0, 1.0, 1.0]
+    # four zones, equal audio norm (gate 0): activities 0.2, 0.75, 1.5, 1.55 of a mean 1
+    st = _multi_stats([iso + [1.0, 1024]] * 4)
+    vact = np.array([[[0.2, 0.75, 1.5, 1.55]]])
+    sid, margin = O.assign_shapes_multi(st, vact, cands, zone)
+    vols = [int(np.prod(cands[i])) for i in sid[0, 0]]
+    assert vols == [256, 128, 64, 64]
+    # isotropic guidance picks the most cubic shape of each volume that tiles the zone
+    assert cands[sid[0, 0, 0]] == (4, 8, 8) and cands[sid[0, 0, 2]] == (4, 4, 4)
+    # the audio gate lifts a smooth zone to the finest blocks: m_z = 2x the head mean
+    st2 = _multi_stats([iso + [3.0, 1024], iso + [1.0, 1024], iso + [1.0, 1024], iso + [1.0, 1024]])
+    sid2, _ = O.assign_shapes_multi(st2, vact, cands, zone)
+    assert int(np.prod(cands[sid2[0, 0, 0]])) == 64            # act = 0.2 + 1
+    # no 256-token shape tiles the zone -> 128 (and without 128 shapes -> 64)
+    sid3, _ = O.assign_shapes_multi(st, vact, CANDS_64 + CANDS_128 + [(8, 4, 8)], zone)
+    assert int(np.prod((CANDS_64 + CANDS_128 + [(8, 4, 8)])[sid3[0, 0, 0]])) == 128
+    sid4, _ = O.assign_shapes_multi(st, vact, CANDS_64 + [(8, 4, 8)], zone)
+    assert int(np.prod((CANDS_64 + [(8, 4, 8)])[sid4[0, 0, 0]])) == 64
+    # an activity on a threshold is a near-tie
+    _, m5 = O.assign_shapes_multi(st, np.array([[[0.5, 1.0, 1.5, 1.0]]]), cands, zone)
+    assert m5[0, 0, 0] < O.NEAR_TIE and m5[0, 0, 1] < O.NEAR_TIE
+
+
+def test_mixed_volume_slot_map_and_dense_equivalence():
+    """Zones with 64-, 128- and 256-token blocks on a ragged grid: every token in exactly
+    one slot, block heads carry whole-block counts, and with every block selected the chain
+    reproduces dense attention."""
+    from workloads import CANDS_128, CANDS_256
+    cands = CANDS_64 + CANDS_128 + CANDS_256
+    rng = np.random.default_rng(4)
+    grid, zone = (6, 20, 18), (4, 16, 16)
+    N = 6 * 20 * 18
+    nZ = O.num_zones(grid, zone)
+    sid = np.array([[[3, 11, 14, 8, 0, 14, 12, 1]]], dtype=np.int32)[:, :, :nZ]      # 64/128/256 mixed
+    tok = O.slot_map(grid, zone, cands, sid)
+    assert sorted(tok[0, 0][tok[0, 0] >= 0].tolist()) == list(range(N))
+    bv = O.block_heads(tok, sid, cands, zone)
+    assert bv.sum() == N and bv.max() <= 256
+    for z in range(nZ):
+        g = int(np.prod(cands[sid[0, 0, z]])) // 64
+        heads = bv[0, 0, z * 16:(z + 1) * 16]
+        assert (heads.reshape(-1, g)[:, 1:] == 0).all()
+    q, k, v, a2v = (rng.standard_normal((1, 1, N, 8)) for _ in range(4))
+    f = O.prism_forward(q, k, v, a2v, grid, zone, cands, 1.0, 10 ** 6, 10 ** 6, scale=0.4, dtype=np.float64,
+                        shape_id=sid, mixed=(O.TAU_128, O.TAU_256))
+    want, _ = O.dense_attn_fwd(q, k, v, 0.4)
+    assert np.allclose(f["o"], want, atol=1e-12)
+
+
 def test_zone_stats_vectorised_equals_bruteforce_on_ragged_grid():
     rng = np.random.default_rng(7)
     grid, zone = (5, 6, 7), (2, 4, 4)
