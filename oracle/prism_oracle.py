@@ -491,9 +491,12 @@ def pool_blocks(xp: np.ndarray, bvalid: np.ndarray, vol: int) -> np.ndarray:
     Valid rows of a block are its first bvalid slots (see slot_map)."""
     B, Hh, Np, C = xp.shape
     nb = Np // vol
-    x = xp.astype(np.float64).reshape(B, Hh, nb, vol, C)
-    rows = np.arange(vol)[None, None, None, :] < bvalid[..., None]
-    s = (x * rows[..., None]).sum(axis=3)
+    # rows I*vol .. I*vol + n - 1; with mixed volumes a block identified by its first unit
+    # runs past that unit, so the sum is a difference of prefix sums, not a per-unit sum
+    cs = np.concatenate([np.zeros((B, Hh, 1, C)), np.cumsum(xp.astype(np.float64), axis=2)], axis=2)
+    start = (np.arange(nb) * vol)[None, None, :]
+    end = start + np.asarray(bvalid)
+    s = np.take_along_axis(cs, end[..., None], axis=2) - np.take_along_axis(cs, np.broadcast_to(start, end.shape)[..., None], axis=2)
     return s / np.maximum(bvalid, 1)[..., None]
 
 

@@ -415,6 +415,15 @@ def test_pooling_bruteforce():
             n = bv[0, h, I]
             want = np.zeros(3) if n == 0 else sum(xp[0, h, I * 16 + r] for r in range(n)) / n
             assert np.allclose(got[0, h, I], want, atol=1e-14)
+    # blocks identified by their first 16-row unit that run past it (mixed volumes): a
+    # 48-row block at unit 0 with 40 valid rows, a 16-row block at unit 3
+    bv2 = np.array([[[40, 0, 0, 9], [33, 0, 0, 16]]], dtype=np.int32)
+    got2 = O.pool_blocks(xp, bv2, 16)
+    for h in range(2):
+        for I in range(4):
+            n = bv2[0, h, I]
+            want = np.zeros(3) if n == 0 else sum(xp[0, h, I * 16 + r] for r in range(n)) / n
+            assert np.allclose(got2[0, h, I], want, atol=1e-14)
 
 
 # ------------------------------------------------------------------ selection
