@@ -159,7 +159,9 @@ def parse_ablation(spec: str, w):
     """Layer settings for an ablation run (Table 7: Top-k only / Top-p only; Table 9:
     fixed or random shapes, query/key features, global variance), comma-separated:
     topk=F (top_p = 1, k = F * live blocks), topp=P (k_min = 1, k_max = nb),
-    fixed=BTxBHxBW, random[=SEED], features=q|k, variance=global.
+    fixed=BTxBHxBW, random[=SEED], features=q|k, variance=global; block volumes (Tables 9
+    and 11): sets=C128 | C256 (one larger set), mixed[=TAU128:TAU256] (C_64 + C_128 +
+    C_256 chosen per zone by the activity thresholds).
     Returns (PrismLayer keyword arguments, shape ids or None)."""
     from content_adaptive_block_zone_amd.pipeline import random_shape_ids
     kw, ids = {}, None
@@ -180,6 +182,13 @@ def parse_ablation(spec: str, w):
             kw.update(cands=[tuple(int(e) for e in val.split("x"))])
         elif key == "random":
             ids = random_shape_ids(w.B, w.heads, w.grid, w.zone, list(w.cands), int(val or 0))
+        elif key == "sets":
+            from workloads import CANDS_128, CANDS_256
+            kw.update(cands={"C128": CANDS_128, "C256": CANDS_256}[val])
+        elif key == "mixed":
+            from workloads import CANDS_128, CANDS_256
+            t128, t256 = (float(t) for t in val.split(":")) if val else (1.0, 0.5)
+            kw.update(cands=list(w.cands) + CANDS_128 + CANDS_256, mixed=(t128, t256))
         elif key == "features":
             kw.update(features=val)
         elif key == "variance":
@@ -235,9 +244,7 @@ def run_gpu(args):
                 L.backward(do)
             return
         stats_and_shapes()
-        L.permute(q, L.qp, block_valid=L.bvalid)
-        L.permute(k, L.kp)
-        L.permute(v, L.vp)
+        L.permute_qkv(q, k, v)
         ev["select0"].record(stream)
         L.select()
         ev["fwd0"].record(stream)
@@ -323,7 +330,7 @@ def run_gpu(args):
              "attn_bwd", "unpermute_grads"]
     calls = [lambda: L.zone_stats(feat, a2v) if shape_ids is None else L.shape_id.copy_(shape_ids),
              lambda: L.assign_shapes() if shape_ids is None else None,
-             lambda: (L.permute(q, L.qp, block_valid=L.bvalid), L.permute(k, L.kp), L.permute(v, L.vp)),
+             lambda: L.permute_qkv(q, k, v),
              L.select, L.attn_fwd, lambda: L.permute(L.op, L.o, inverse=True)]
     if fwd_only:
         names = names[:len(calls)]

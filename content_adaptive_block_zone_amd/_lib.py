@@ -10,7 +10,7 @@ from ctypes import POINTER, c_float, c_int, c_int32, c_int64, c_size_t, c_void_p
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libprism.so")
-MAX_SHAPES = 16
+MAX_SHAPES = 32
 
 PRISM_OK, PRISM_ERR_ARG, PRISM_ERR_DTYPE, PRISM_ERR_SHAPE, PRISM_ERR_LAUNCH = range(5)
 PRISM_F32, PRISM_BF16 = 0, 1
@@ -46,6 +46,12 @@ PROTOTYPES = {
     "prism_zone_stats_global": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _P, _P]),
     "prism_a2v_attn_norm": (c_int, [_P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, c_float, _P, _P, _P]),
     "prism_zone_stats_from_norm": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, c_int, _P, _P]),
+    "prism_zone_stats_ex": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, c_int, _P, _P, _P]),
+    "prism_assign_shapes_multi": (c_int, [_P, _P, c_int, c_int, _GP, _SP, _SHP, c_float, c_float, _P, _P, _P]),
+    "prism_block_heads": (c_int, [_P, _P, c_int, c_int, _GP, _SP, _P, _P]),
+    "prism_tiles_mixed_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "prism_blocks_to_tiles_mixed": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, _P, _P, _P, _P,
+                                            _P, c_size_t, _P]),
     "prism_assign_shapes": (c_int, [_P, c_int, c_int, _GP, _SP, _SHP, _P, _P, _P]),
     "prism_permute": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _SP, _P, c_int, _P, _P]),
     "prism_select_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),

@@ -33,10 +33,12 @@ def make_grid(grid: Sequence[int], zone: Sequence[int]) -> PrismGrid:
     return PrismGrid(*[int(x) for x in grid], *[int(x) for x in zone])
 
 
-def make_shapes(cands: Sequence[Shape]) -> PrismShapes:
+def make_shapes(cands: Sequence[Shape], unit: Optional[int] = None) -> PrismShapes:
+    """Candidate table.  vol is the first candidate's volume, or `unit` for a list that
+    mixes volumes (each a multiple of the unit)."""
     s = PrismShapes()
     s.n = len(cands)
-    s.vol = int(cands[0][0] * cands[0][1] * cands[0][2]) if cands else 0
+    s.vol = int(unit) if unit is not None else (int(cands[0][0] * cands[0][1] * cands[0][2]) if cands else 0)
     for i, (bt, bh, bw) in enumerate(cands):
         s.bt[i], s.bh[i], s.bw[i] = int(bt), int(bh), int(bw)
     return s
@@ -166,6 +168,45 @@ def prism_zone_stats_from_norm(v: torch.Tensor, a2v_norm: torch.Tensor, grid: Pr
           "prism_zone_stats_from_norm")
 
 
+STATS_GLOBAL_VARIANCE, STATS_FROM_NORM = 1, 2
+
+
+def prism_zone_stats_ex(v: torch.Tensor, aux: torch.Tensor, grid: PrismGrid, stats: torch.Tensor, flags: int = 0,
+                        vact: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, Hh, N, d = v.shape
+    nZ = prism_num_zones(grid)
+    if flags & STATS_FROM_NORM:
+        a = _ptr(aux, torch.float32, (B, Hh, N), "a2v_norm")
+    else:
+        _same_dtype(v, aux)
+        a = _ptr(aux, shape=(B, Hh, N, d), name="a2v")
+    check(load().prism_zone_stats_ex(_ptr(v, shape=(B, Hh, N, d), name="v"), a, _dt(v), B, Hh, d, grid, int(flags),
+                                     _ptr(stats, torch.float32, (B, Hh, nZ, 8), "stats"),
+                                     _ptr(vact, torch.float32, (B, Hh, nZ), "vact"), _stream(stream)),
+          "prism_zone_stats_ex")
+
+
+def prism_assign_shapes_multi(stats: torch.Tensor, vact: torch.Tensor, grid: PrismGrid, shapes: PrismShapes,
+                              params: PrismShapeParams, tau_128: float, tau_256: float, shape_id: torch.Tensor,
+                              margin: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, Hh, nZ, _ = stats.shape
+    check(load().prism_assign_shapes_multi(_ptr(stats, torch.float32, name="stats"),
+                                           _ptr(vact, torch.float32, (B, Hh, nZ), "vact"), B, Hh, grid, shapes, params,
+                                           float(tau_128), float(tau_256),
+                                           _ptr(shape_id, torch.int32, (B, Hh, nZ), "shape_id"),
+                                           _ptr(margin, torch.float32, (B, Hh, nZ), "margin"), _stream(stream)),
+          "prism_assign_shapes_multi")
+
+
+def prism_block_heads(unit_valid: torch.Tensor, shape_id: torch.Tensor, grid: PrismGrid, shapes: PrismShapes,
+                      block_valid: torch.Tensor, stream=None) -> None:
+    B, Hh, nb = unit_valid.shape
+    check(load().prism_block_heads(_ptr(unit_valid, torch.int32, name="unit_valid"),
+                                   _ptr(shape_id, torch.int32, name="shape_id"), B, Hh, grid, shapes,
+                                   _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"), _stream(stream)),
+          "prism_block_heads")
+
+
 def prism_assign_shapes(stats: torch.Tensor, grid: PrismGrid, shapes: PrismShapes, params: PrismShapeParams,
                         shape_id: torch.Tensor, margin: Optional[torch.Tensor] = None, stream=None) -> None:
     B, Hh, nZ, _ = stats.shape
@@ -227,6 +268,25 @@ def prism_blocks_to_tiles(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, vol: 
         _ptr(tile_cnt, torch.int32, (B, Hh, nt), "tile_cnt"), _ptr(tile_rev_ptr, torch.int32, (B, Hh, nt + 1), "tile_rev_ptr"),
         _ptr(tile_rev_idx, torch.int32, (B, Hh, nt * kt), "tile_rev_idx"), _ptr(workspace, torch.uint8, name="workspace"),
         workspace.numel(), _stream(stream)), "prism_blocks_to_tiles")
+
+
+def prism_tiles_mixed_workspace_size(B: int, Hh: int, nb: int) -> int:
+    return int(load().prism_tiles_mixed_workspace_size(B, Hh, nb))
+
+
+def prism_blocks_to_tiles_mixed(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, max_units: int, tile_idx, tile_cnt,
+                                tile_rev_ptr, tile_rev_idx, workspace, stream=None) -> None:
+    B, Hh, nb = block_valid.shape
+    km = sel_idx.shape[-1]
+    kt = km * max_units
+    check(load().prism_blocks_to_tiles_mixed(
+        _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"), _ptr(sel_idx, torch.int32, (B, Hh, nb, km), "sel_idx"),
+        _ptr(sel_cnt, torch.int32, (B, Hh, nb), "sel_cnt"), _ptr(rev_ptr, torch.int32, (B, Hh, nb + 1), "rev_ptr"),
+        _ptr(rev_idx, torch.int32, (B, Hh, nb * km), "rev_idx"), B, Hh, nb, km, int(max_units),
+        _ptr(tile_idx, torch.int32, (B, Hh, nb, kt), "tile_idx"), _ptr(tile_cnt, torch.int32, (B, Hh, nb), "tile_cnt"),
+        _ptr(tile_rev_ptr, torch.int32, (B, Hh, nb + 1), "tile_rev_ptr"),
+        _ptr(tile_rev_idx, torch.int32, (B, Hh, nb * kt), "tile_rev_idx"), _ptr(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _stream(stream)), "prism_blocks_to_tiles_mixed")
 
 
 def prism_sparse_attn_fwd(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, scale: float, op, lse,

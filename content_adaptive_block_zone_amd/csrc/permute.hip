@@ -16,12 +16,15 @@ __global__ __launch_bounds__(NT) void k_permute(const uint4* __restrict__ x, uin
                                                 int32_t* __restrict__ block_valid) {
   const int I = blockIdx.x;
   const int bh = blockIdx.y;
-  const int vol = tab.vol;
+  const int vol = tab.vol;          // slots handled by this workgroup (the unit)
   const int slot0 = I * vol;
   const int z = slot0 / g.Vz;
-  const int blk = (slot0 % g.Vz) / vol;
   const int c = shape_id[size_t(bh) * g.nZ + z];
   const int bt = tab.bt[c], bhh = tab.bh[c], bw = tab.bw[c];
+  // the zone's blocks hold S = cvol tokens, a multiple of the unit: this unit is the part
+  // j0 .. j0 + vol - 1 of block blk
+  const int S = tab.cvol[c];
+  const int blk = (slot0 % g.Vz) / S, j0 = (slot0 % g.Vz) % S;
   const int nbh = g.zh / bhh, nbw = g.zw / bw;
   const int iw = z % g.nzw, ih = (z / g.nzw) % g.nzh, it = z / (g.nzw * g.nzh);
   const int t0 = it * g.zt + (blk / (nbh * nbw)) * bt;
@@ -33,8 +36,9 @@ __global__ __launch_bounds__(NT) void k_permute(const uint4* __restrict__ x, uin
   const size_t tok_base = size_t(bh) * g.N;
   const int total = vol * chunks;
   for (int e = threadIdx.x; e < total; e += NT) {
-    const int j = e / chunks, ch = e - j * chunks;
-    const size_t srow = (slot_base + j) * chunks + ch;
+    const int r = e / chunks, ch = e - r * chunks;
+    const int j = j0 + r;           // position inside the block
+    const size_t srow = (slot_base + r) * chunks + ch;
     if (j < nval) {
       const int tok = ((t0 + j / (eh * ew)) * g.H + h0 + (j / ew) % eh) * g.W + w0 + j % ew;
       const size_t trow = (tok_base + tok) * chunks + ch;
@@ -46,7 +50,7 @@ __global__ __launch_bounds__(NT) void k_permute(const uint4* __restrict__ x, uin
       y[srow] = make_uint4(0u, 0u, 0u, 0u);
     }
   }
-  if (threadIdx.x == 0 && block_valid) block_valid[size_t(bh) * nb + I] = nval;
+  if (threadIdx.x == 0 && block_valid) block_valid[size_t(bh) * nb + I] = max(0, min(vol, nval - j0));
 }
 
 }  // namespace

@@ -67,11 +67,17 @@ prism_status check_shapes(const prism_shapes* s, const Geo& g, ShapeTab* out) {
   ShapeTab t = {};
   t.n = s->n;
   t.vol = s->vol;
+  t.uniform = 1;
   int nfeas = 0;
   for (int c = 0; c < s->n; ++c) {
     if (s->bt[c] < 1 || s->bh[c] < 1 || s->bw[c] < 1) return fail(PRISM_ERR_ARG, "shape %d has an extent < 1", c);
-    if (int64_t(s->bt[c]) * s->bh[c] * s->bw[c] != s->vol)
-      return fail(PRISM_ERR_SHAPE, "shape %d (%dx%dx%d) does not hold vol=%d tokens", c, s->bt[c], s->bh[c], s->bw[c], s->vol);
+    const int64_t cv = int64_t(s->bt[c]) * s->bh[c] * s->bw[c];
+    // a candidate holds vol tokens, or (mixed sets) a multiple of vol that divides the zone
+    if (cv % s->vol != 0 || cv > g.Vz || g.Vz % cv != 0)
+      return fail(PRISM_ERR_SHAPE, "shape %d (%dx%dx%d) holds %lld tokens: not a multiple of vol=%d dividing the zone",
+                  c, s->bt[c], s->bh[c], s->bw[c], (long long)cv, s->vol);
+    t.cvol[c] = int(cv);
+    if (cv != s->vol) t.uniform = 0;
     t.bt[c] = s->bt[c];
     t.bh[c] = s->bh[c];
     t.bw[c] = s->bw[c];
@@ -110,7 +116,8 @@ int64_t prism_num_blocks(const prism_grid* grid, const prism_shapes* shapes) {
 
 static prism_status zone_stats_common(const char* who, bool global_variance, bool from_norm, const void* v,
                                       const void* aux, prism_dtype dtype, int B, int Hh, int d,
-                                      const prism_grid* grid, float* stats, hipStream_t stream) {
+                                      const prism_grid* grid, float* stats, hipStream_t stream,
+                                      float* vact = nullptr) {
   if (!v || !aux || !stats) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
   if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "%s: B and Hh must be >= 1", who);
   if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "%s: unknown dtype %d", who, int(dtype));
@@ -118,7 +125,8 @@ static prism_status zone_stats_common(const char* who, bool global_variance, boo
   Geo g;
   prism_status st = check_grid(grid, &g);
   if (st != PRISM_OK) return st;
-  return launched(launch_zone_stats(v, aux, dtype, B * Hh, d, g, global_variance, from_norm, stats, stream), who);
+  return launched(launch_zone_stats(v, aux, dtype, B * Hh, d, g, global_variance, from_norm, stats, vact, stream),
+                  who);
 }
 
 prism_status prism_zone_stats(const void* v, const void* a2v, prism_dtype dtype, int B, int Hh, int d,
@@ -139,6 +147,14 @@ prism_status prism_zone_stats_from_norm(const void* v, const float* a2v_norm, pr
 }
 
 
+prism_status prism_zone_stats_ex(const void* v, const void* aux, prism_dtype dtype, int B, int Hh, int d,
+                                 const prism_grid* grid, int flags, float* stats, float* vact, hipStream_t stream) {
+  if (flags & ~(PRISM_STATS_GLOBAL_VARIANCE | PRISM_STATS_FROM_NORM))
+    return fail(PRISM_ERR_ARG, "prism_zone_stats_ex: unknown flags 0x%x", unsigned(flags));
+  return zone_stats_common("prism_zone_stats_ex", (flags & PRISM_STATS_GLOBAL_VARIANCE) != 0,
+                           (flags & PRISM_STATS_FROM_NORM) != 0, v, aux, dtype, B, Hh, d, grid, stats, stream, vact);
+}
+
 prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_grid* grid,
                                  const prism_shapes* shapes, const prism_shape_params* params,
                                  int32_t* shape_id, float* margin, hipStream_t stream) {
@@ -150,11 +166,56 @@ prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_
   ShapeTab t;
   st = check_shapes(shapes, g, &t);
   if (st != PRISM_OK) return st;
+  if (!t.uniform) return fail(PRISM_ERR_SHAPE, "prism_assign_shapes: candidates of several volumes (use prism_assign_shapes_multi)");
   const prism_shape_params p = *params;
   if (!std::isfinite(p.alpha) || !std::isfinite(p.tau_lo) || !std::isfinite(p.tau_hi) || !(p.tau_hi > p.tau_lo))
     return fail(PRISM_ERR_ARG, "prism_assign_shapes: need finite alpha and tau_hi > tau_lo");
   if (!(p.g_min > 0.f) || !(p.eps >= 0.f)) return fail(PRISM_ERR_ARG, "prism_assign_shapes: need g_min > 0, eps >= 0");
   return launched(launch_assign_shapes(stats, B * Hh, g, t, p, shape_id, margin, stream), "prism_assign_shapes");
+}
+
+prism_status prism_assign_shapes_multi(const float* stats, const float* vact, int B, int Hh, const prism_grid* grid,
+                                       const prism_shapes* shapes, const prism_shape_params* params, float tau_128,
+                                       float tau_256, int32_t* shape_id, float* margin, hipStream_t stream) {
+  const char* who = "prism_assign_shapes_multi";
+  if (!stats || !vact || !shape_id || !params) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "%s: B and Hh must be >= 1", who);
+  Geo g;
+  prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  ShapeTab t;
+  st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  bool unit_feasible = false;
+  for (int c = 0; c < t.n; ++c) {
+    if (t.cvol[c] != t.vol && t.cvol[c] != 2 * t.vol && t.cvol[c] != 4 * t.vol)
+      return fail(PRISM_ERR_SHAPE, "%s: candidate %d holds %d tokens, not 1, 2 or 4 units of %d", who, c, t.cvol[c], t.vol);
+    unit_feasible |= t.feasible[c] && t.cvol[c] == t.vol;
+  }
+  if (!unit_feasible) return fail(PRISM_ERR_SHAPE, "%s: no candidate of the unit volume %d tiles the zone", who, t.vol);
+  const prism_shape_params p = *params;
+  if (!std::isfinite(p.alpha) || !std::isfinite(p.tau_lo) || !std::isfinite(p.tau_hi) || !(p.tau_hi > p.tau_lo))
+    return fail(PRISM_ERR_ARG, "%s: need finite alpha and tau_hi > tau_lo", who);
+  if (!(p.g_min > 0.f) || !(p.eps >= 0.f)) return fail(PRISM_ERR_ARG, "%s: need g_min > 0, eps >= 0", who);
+  if (!(tau_256 > 0.f) || !(tau_128 >= tau_256) || !std::isfinite(tau_128))
+    return fail(PRISM_ERR_ARG, "%s: need 0 < tau_256 <= tau_128 < inf", who);
+  return launched(launch_assign_shapes_multi(stats, vact, B * Hh, g, t, p, tau_128, tau_256, shape_id, margin, stream),
+                  who);
+}
+
+prism_status prism_block_heads(const int32_t* unit_valid, const int32_t* shape_id, int B, int Hh,
+                               const prism_grid* grid, const prism_shapes* shapes, int32_t* block_valid,
+                               hipStream_t stream) {
+  const char* who = "prism_block_heads";
+  if (!unit_valid || !shape_id || !block_valid) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1) return fail(PRISM_ERR_ARG, "%s: B and Hh must be >= 1", who);
+  Geo g;
+  prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  ShapeTab t;
+  st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  return launched(launch_block_heads(unit_valid, shape_id, B * Hh, g, t, block_valid, stream), who);
 }
 
 prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int Hh, int d,
@@ -368,6 +429,31 @@ prism_status prism_blocks_to_tiles(const int32_t* block_valid, const int32_t* se
   if (ws_bytes < tiles_ws_bytes(B * Hh, nb, vol)) return fail(PRISM_ERR_ARG, "%s: workspace too small", who);
   return launched(launch_blocks_to_tiles(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, B * Hh, nb, vol, k_max,
                                          tile_valid, tile_idx, tile_cnt, tile_rev_ptr, tile_rev_idx, workspace, stream),
+                  who);
+}
+
+size_t prism_tiles_mixed_workspace_size(int B, int Hh, int nb) {
+  if (B < 1 || Hh < 1 || nb < 1) return 0;
+  return tiles_mixed_ws_bytes(B * Hh, nb);
+}
+
+prism_status prism_blocks_to_tiles_mixed(const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                         const int32_t* rev_ptr, const int32_t* rev_idx, int B, int Hh, int nb,
+                                         int k_max, int max_units, int32_t* tile_idx, int32_t* tile_cnt,
+                                         int32_t* tile_rev_ptr, int32_t* tile_rev_idx, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream) {
+  const char* who = "prism_blocks_to_tiles_mixed";
+  if (!block_valid || !sel_idx || !sel_cnt || !rev_ptr || !rev_idx || !tile_idx || !tile_cnt || !tile_rev_ptr ||
+      !tile_rev_idx || !workspace)
+    return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1 || nb < 1 || k_max < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, nb, k_max must be >= 1", who);
+  if (max_units < 1 || max_units > 64) return fail(PRISM_ERR_ARG, "%s: max_units must be in [1, 64]", who);
+  if (int64_t(B) * Hh * nb * int64_t(k_max) * max_units > (int64_t(1) << 31))
+    return fail(PRISM_ERR_SHAPE, "%s: tile lists exceed 2^31 entries", who);
+  if (ws_bytes < tiles_mixed_ws_bytes(B * Hh, nb)) return fail(PRISM_ERR_ARG, "%s: workspace too small", who);
+  return launched(launch_blocks_to_tiles_mixed(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, B * Hh, nb, k_max,
+                                               max_units, tile_idx, tile_cnt, tile_rev_ptr, tile_rev_idx, workspace,
+                                               stream),
                   who);
 }
 

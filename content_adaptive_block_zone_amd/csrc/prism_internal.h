@@ -155,10 +155,12 @@ struct Geo {
 };
 
 struct ShapeTab {
-  int n, vol;
+  int n, vol;  // vol: the slot unit (every candidate's volume when uniform)
   int bt[PRISM_MAX_SHAPES], bh[PRISM_MAX_SHAPES], bw[PRISM_MAX_SHAPES];
   float lg[PRISM_MAX_SHAPES][3];  // log2 of each extent
   int feasible[PRISM_MAX_SHAPES];
+  int cvol[PRISM_MAX_SHAPES];     // each candidate's own volume (a multiple of vol)
+  int uniform;                    // every candidate holds vol tokens
 };
 
 struct AttnArgs {
@@ -191,10 +193,17 @@ struct AttnArgs {
 // Launchers (each returns the first HIP error of its launches).
 // aux: the A2V output rows [BH][N][d] (dtype dt), or with from_norm the norm map float [BH][N]
 hipError_t launch_zone_stats(const void* v, const void* aux, prism_dtype dt, int BH, int d, const Geo& g,
-                             bool global_variance, bool from_norm, float* stats, hipStream_t s);
+                             bool global_variance, bool from_norm, float* stats, float* vact, hipStream_t s);
 hipError_t launch_assign_shapes(const float* stats, int BH, const Geo& g, const ShapeTab& tab,
                                 const prism_shape_params& p, int32_t* shape_id, float* margin,
                                 hipStream_t s);
+// mixed volumes (unit 64, candidates of 64, 128 and 256 tokens) chosen by thresholds on
+// the zone activity vact
+hipError_t launch_assign_shapes_multi(const float* stats, const float* vact, int BH, const Geo& g,
+                                      const ShapeTab& tab, const prism_shape_params& p, float tau_128,
+                                      float tau_256, int32_t* shape_id, float* margin, hipStream_t s);
+hipError_t launch_block_heads(const int32_t* unit_valid, const int32_t* shape_id, int BH, const Geo& g,
+                              const ShapeTab& tab, int32_t* block_valid, hipStream_t s);
 hipError_t launch_permute(const void* x, void* y, prism_dtype dt, int BH, int d, const Geo& g,
                           const ShapeTab& tab, const int32_t* shape_id, int inverse,
                           int32_t* block_valid, hipStream_t s);
@@ -208,6 +217,11 @@ size_t select_ws_bytes(int BH, int nb, int d);
 size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
 size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt);
 size_t tiles_ws_bytes(int BH, int nb, int vol);
+size_t tiles_mixed_ws_bytes(int BH, int nb);
+hipError_t launch_blocks_to_tiles_mixed(const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                        const int32_t* rev_ptr, const int32_t* rev_idx, int BH, int nb, int k_max,
+                                        int max_units, int32_t* tile_idx, int32_t* tile_cnt, int32_t* tile_rev_ptr,
+                                        int32_t* tile_rev_idx, void* ws, hipStream_t s);
 hipError_t launch_blocks_to_tiles(const int32_t* bvalid, const int32_t* sel_idx, const int32_t* sel_cnt,
                                   const int32_t* rev_ptr, const int32_t* rev_idx, int BH, int nb, int vol, int k_max,
                                   int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt, int32_t* tile_rev_ptr,

@@ -27,7 +27,7 @@ constexpr int NWAVE = NT / 64;
 // rows [BH][N][D] whose norms the kernel would take itself.
 template <typename T, int D, bool GLOBAL, bool FROM_NORM>
 __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, const void* __restrict__ aux,
-                                                   float* __restrict__ stats, Geo g) {
+                                                   float* __restrict__ stats, float* __restrict__ vact, Geo g) {
   const T* a2v = static_cast<const T*>(aux);
   const float* anorm = static_cast<const float*>(aux);
   constexpr int G = D / 8;      // lanes per token
@@ -126,6 +126,7 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
   const float np_h = float(et * max(eh - 1, 0) * ew);
   const float np_w = float(et * eh * max(ew - 1, 0));
   const float npair[3] = {np_t, np_h, np_w};
+  float vs = 0.f;  // channel sum of the per-axis semivariances (zone activity)
   for (int c = tid; c < D; c += NT) {
     float gam[3];
 #pragma unroll
@@ -135,6 +136,7 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
       for (int r = 0; r < NWAVE; ++r) s += s_red[r][a][c];
       gam[a] = npair[a] > 0.f ? 0.5f * s / npair[a] : 0.f;
     }
+    vs += gam[0] + gam[1] + gam[2];
     if (GLOBAL) {
 #pragma unroll
       for (int a = 0; a < 3; ++a) s_share[a][c] = gam[a];
@@ -170,6 +172,10 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
 #pragma unroll
   for (int a = 0; a < 3; ++a) res[3 + a] = block_sum<NT>(sa[a], s_tmp);
   res[6] = block_sum<NT>(asum, s_tmp);
+  if (vact) {  // uniform over the workgroup
+    vs = block_sum<NT>(vs, s_tmp);
+    if (tid == 0) vact[size_t(bh) * g.nZ + z] = vs / float(D);
+  }
   if (tid == 0) {
     float* out = stats + (size_t(bh) * g.nZ + z) * 8;
     if (GLOBAL) {  // shares of the channel-mean semivariances
@@ -191,14 +197,15 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
 }
 
 template <typename T, bool GLOBAL, bool FROM_NORM>
-hipError_t launch_t(const void* v, const void* aux, int BH, int d, const Geo& g, float* stats, hipStream_t s) {
+hipError_t launch_t(const void* v, const void* aux, int BH, int d, const Geo& g, float* stats, float* vact,
+                    hipStream_t s) {
   dim3 grid(unsigned(BH) * unsigned(g.nZ)), block(NT);
   const T* pv = static_cast<const T*>(v);
   switch (d) {
-    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
-    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
-    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
-    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, g); break;
+    case 32: hipLaunchKernelGGL((k_zone_stats<T, 32, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, vact, g); break;
+    case 64: hipLaunchKernelGGL((k_zone_stats<T, 64, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, vact, g); break;
+    case 128: hipLaunchKernelGGL((k_zone_stats<T, 128, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, vact, g); break;
+    case 256: hipLaunchKernelGGL((k_zone_stats<T, 256, GLOBAL, FROM_NORM>), grid, block, 0, s, pv, aux, stats, vact, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -206,20 +213,20 @@ hipError_t launch_t(const void* v, const void* aux, int BH, int d, const Geo& g,
 
 template <typename T>
 hipError_t launch_dt(const void* v, const void* aux, int BH, int d, const Geo& g, bool global_variance,
-                     bool from_norm, float* stats, hipStream_t s) {
+                     bool from_norm, float* stats, float* vact, hipStream_t s) {
   if (from_norm)
-    return global_variance ? launch_t<T, true, true>(v, aux, BH, d, g, stats, s)
-                           : launch_t<T, false, true>(v, aux, BH, d, g, stats, s);
-  return global_variance ? launch_t<T, true, false>(v, aux, BH, d, g, stats, s)
-                         : launch_t<T, false, false>(v, aux, BH, d, g, stats, s);
+    return global_variance ? launch_t<T, true, true>(v, aux, BH, d, g, stats, vact, s)
+                           : launch_t<T, false, true>(v, aux, BH, d, g, stats, vact, s);
+  return global_variance ? launch_t<T, true, false>(v, aux, BH, d, g, stats, vact, s)
+                         : launch_t<T, false, false>(v, aux, BH, d, g, stats, vact, s);
 }
 
 }  // namespace
 
 hipError_t launch_zone_stats(const void* v, const void* aux, prism_dtype dt, int BH, int d, const Geo& g,
-                             bool global_variance, bool from_norm, float* stats, hipStream_t s) {
-  if (dt == PRISM_BF16) return launch_dt<bf16_t>(v, aux, BH, d, g, global_variance, from_norm, stats, s);
-  return launch_dt<float>(v, aux, BH, d, g, global_variance, from_norm, stats, s);
+                             bool global_variance, bool from_norm, float* stats, float* vact, hipStream_t s) {
+  if (dt == PRISM_BF16) return launch_dt<bf16_t>(v, aux, BH, d, g, global_variance, from_norm, stats, vact, s);
+  return launch_dt<float>(v, aux, BH, d, g, global_variance, from_norm, stats, vact, s);
 }
 
 }  // namespace prism

@@ -42,19 +42,26 @@ class PrismLayer:
     takes it across all channels jointly instead of per channel.  Fixed shapes are a
     one-candidate set; random shapes come in through forward(shape_id=...).  Top-k only
     and Top-p only (Table 7) are selection parameters (top_p = 1 with k_min = k_max, or
-    k_min = 1 with k_max >= the block count)."""
+    k_min = 1 with k_max >= the block count).
+
+    mixed = (tau_128, tau_256) takes a candidate list that mixes 64-, 128- and 256-token
+    shapes (Tables 9 and 11: C_64, C_128, C_256) and picks each zone's volume by those
+    thresholds on its activity (prism_assign_shapes_multi); blocks are then identified by
+    their first 64-row unit and the attention runs on 64-row tiles."""
 
     def __init__(self, B: int, Hh: int, d: int, grid: Sequence[int], zone: Sequence[int],
                  cands: Sequence[Shape], top_p: float, k_min: int, k_max: int,
                  dtype: torch.dtype = torch.bfloat16, device="cuda", scale: Optional[float] = None,
-                 rule: ShapeRule = ShapeRule(), features: str = "v", variance: str = "channel"):
+                 rule: ShapeRule = ShapeRule(), features: str = "v", variance: str = "channel",
+                 mixed: Optional[Tuple[float, float]] = None):
         if features not in ("v", "q", "k") or variance not in ("channel", "global"):
             raise ValueError(f"features must be v, q or k and variance channel or global, got {features}, {variance}")
         self.features, self.variance = features, variance
+        self.mixed = None if mixed is None else (float(mixed[0]), float(mixed[1]))
         self.B, self.Hh, self.d = B, Hh, d
         self.dtype, self.device = dtype, torch.device(device)
         self.grid = api.make_grid(grid, zone)
-        self.shapes = api.make_shapes(cands)
+        self.shapes = api.make_shapes(cands, unit=64 if mixed is not None else None)
         self.shape_params = api.make_shape_params(rule)
         self.sel_params = api.make_select_params(top_p, k_min, k_max)
         self.scale = api.default_scale(d) if scale is None else float(scale)
@@ -88,7 +95,18 @@ class PrismLayer:
         self._grad_bufs = None
         # Blocks of more than 64 tokens run the attention on 64-row tiles (vol/64 per block).
         self.g = self.vol // 64 if self.vol > 64 else 1
-        if self.vol > 64:
+        if self.mixed is not None:
+            # blocks identified by their first 64-row unit; units are the attention tiles
+            self.max_units = max(bt * bh * bw for (bt, bh, bw) in cands) // 64
+            kt = self.k_max * self.max_units
+            self.vact = e(B_, H_, self.nZ, dt=f32)
+            self.unit_valid = e(B_, H_, self.nb, dt=i32)
+            self.tile_idx = e(B_, H_, self.nb, kt, dt=i32)
+            self.tile_cnt = e(B_, H_, self.nb, dt=i32)
+            self.tile_rev_ptr = e(B_, H_, self.nb + 1, dt=i32)
+            self.tile_rev_idx = e(B_, H_, self.nb * kt, dt=i32)
+            self.ws_tiles = e(api.prism_tiles_mixed_workspace_size(B, Hh, self.nb), dt=torch.uint8)
+        elif self.vol > 64:
             if self.vol % 64:
                 raise ValueError(f"block volume {self.vol} above 64 must be a multiple of 64")
             nt, kt = self.nb * self.g, self.k_max * self.g
@@ -110,11 +128,21 @@ class PrismLayer:
         return self._grad_bufs
 
     # ---- stages (each is exactly one library call)
+    def _stats_flags(self, from_norm: bool) -> int:
+        return ((api.STATS_GLOBAL_VARIANCE if self.variance == "global" else 0) |
+                (api.STATS_FROM_NORM if from_norm else 0))
+
     def zone_stats(self, feat, a2v):
+        if self.mixed is not None:
+            api.prism_zone_stats_ex(feat, a2v, self.grid, self.stats, self._stats_flags(False), self.vact)
+            return
         fn = api.prism_zone_stats_global if self.variance == "global" else api.prism_zone_stats
         fn(feat, a2v, self.grid, self.stats)
 
     def zone_stats_from_norm(self, feat, a2v_norm):
+        if self.mixed is not None:
+            api.prism_zone_stats_ex(feat, a2v_norm, self.grid, self.stats, self._stats_flags(True), self.vact)
+            return
         api.prism_zone_stats_from_norm(feat, a2v_norm, self.grid, self.stats, self.variance == "global")
 
     def a2v_norm(self, q, ka, va, out: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -126,8 +154,22 @@ class PrismLayer:
         return out
 
     def assign_shapes(self):
+        if self.mixed is not None:
+            api.prism_assign_shapes_multi(self.stats, self.vact, self.grid, self.shapes, self.shape_params,
+                                          self.mixed[0], self.mixed[1], self.shape_id, self.shape_margin)
+            return
         api.prism_assign_shapes(self.stats, self.grid, self.shapes, self.shape_params, self.shape_id,
                                 self.shape_margin)
+
+    def permute_qkv(self, q, k, v):
+        """Q, K, V into slot order; block_valid (block heads, when volumes are mixed) from Q's pass."""
+        if self.mixed is not None:
+            self.permute(q, self.qp, block_valid=self.unit_valid)
+            api.prism_block_heads(self.unit_valid, self.shape_id, self.grid, self.shapes, self.bvalid)
+        else:
+            self.permute(q, self.qp, block_valid=self.bvalid)
+        self.permute(k, self.kp)
+        self.permute(v, self.vp)
 
     def permute(self, x, y, inverse=False, block_valid=None):
         api.prism_permute(x, y, self.grid, self.shapes, self.shape_id, inverse, block_valid)
@@ -136,7 +178,11 @@ class PrismLayer:
         api.prism_select_blocks(self.qp, self.kp, self.bvalid, self.vol, self.scale, self.sel_params,
                                 self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.ws_sel,
                                 self.sel_margin)
-        if self.vol > 64:
+        if self.mixed is not None:
+            api.prism_blocks_to_tiles_mixed(self.bvalid, self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx,
+                                            self.max_units, self.tile_idx, self.tile_cnt, self.tile_rev_ptr,
+                                            self.tile_rev_idx, self.ws_tiles)
+        elif self.vol > 64:
             api.prism_blocks_to_tiles(self.bvalid, self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.vol,
                                       self.tile_valid, self.tile_idx, self.tile_cnt, self.tile_rev_ptr,
                                       self.tile_rev_idx, self.ws_tiles)
@@ -144,6 +190,8 @@ class PrismLayer:
     def _attn_lists(self):
         """(valid counts, lists, counts, reverse pointers, reverse lists, rows per unit) the
         attention runs on: the blocks themselves, or their 64-row tiles."""
+        if self.mixed is not None:
+            return (self.unit_valid, self.tile_idx, self.tile_cnt, self.tile_rev_ptr, self.tile_rev_idx, 64)
         if self.vol > 64:
             return (self.tile_valid, self.tile_idx, self.tile_cnt, self.tile_rev_ptr, self.tile_rev_idx, 64)
         return (self.bvalid, self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.vol)
@@ -173,9 +221,7 @@ class PrismLayer:
             self.assign_shapes()
         else:
             self.shape_id.copy_(shape_id)
-        self.permute(q, self.qp, block_valid=self.bvalid)
-        self.permute(k, self.kp)
-        self.permute(v, self.vp)
+        self.permute_qkv(q, k, v)
         self.select()
         self.attn_fwd()
         self.permute(self.op, self.o, inverse=True)

@@ -52,6 +52,9 @@ typedef enum {
 
 typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
 
+/* Flags of prism_zone_stats_ex. */
+enum { PRISM_STATS_GLOBAL_VARIANCE = 1, PRISM_STATS_FROM_NORM = 2 };
+
 /* Video latent grid (T, H, W) and macro-zone extents (zt, zh, zw).  Zones tile the grid
  * from the origin in t-major raster order; the grid is padded at its far edges up to a
  * multiple of the zone (abstract: spatiotemporal macro-zones). */
@@ -60,7 +63,7 @@ typedef struct {
   int32_t zt, zh, zw;
 } prism_grid;
 
-#define PRISM_MAX_SHAPES 16
+#define PRISM_MAX_SHAPES 32
 
 /* Candidate block shapes (b_T, b_H, b_W), all holding `vol` tokens (Table 11 caption:
  * shapes b_T b_H b_W; one candidate set holds a single volume).  A candidate can be
@@ -131,6 +134,16 @@ prism_status prism_zone_stats_from_norm(const void* v, const float* a2v_norm, pr
                                         int Hh, int d, const prism_grid* grid, int global_variance,
                                         float* stats, hipStream_t stream);
 
+/* The zone statistics with every option: flags PRISM_STATS_GLOBAL_VARIANCE (as
+ * prism_zone_stats_global) and PRISM_STATS_FROM_NORM (aux is the norm map float
+ * [B][Hh][N], as prism_zone_stats_from_norm; otherwise the A2V output rows).
+ * vact     optional out float [B][Hh][nZ]: the zone's video activity, the channel-mean
+ *          lag-one semivariance of v summed over t, h and w (the magnitude the shares
+ *          normalise away; input of prism_assign_shapes_multi).
+ * Unknown flags: PRISM_ERR_ARG.  Arguments, output and errors otherwise as prism_zone_stats. */
+prism_status prism_zone_stats_ex(const void* v, const void* aux, prism_dtype dtype, int B, int Hh, int d,
+                                 const prism_grid* grid, int flags, float* stats, float* vact, hipStream_t stream);
+
 /* Shape assignment (abstract: finer blocks along fast-varying, audio-coupled axes;
  * Table 10 caption: b*_d ~ g_d^-alpha and its quantization).
  * stats    float [B][Hh][nZ][8] from prism_zone_stats.
@@ -142,6 +155,32 @@ prism_status prism_zone_stats_from_norm(const void* v, const float* a2v_norm, pr
 prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_grid* grid,
                                  const prism_shapes* shapes, const prism_shape_params* params,
                                  int32_t* shape_id, float* margin, hipStream_t stream);
+
+/* Shapes from a candidate table that mixes volumes: unit = shapes->vol (64), candidates
+ * of 1, 2 or 4 units (the C_64 / C_128 / C_256 sets of Tables 9 and 11; Table 10 caption:
+ * thresholds tau_128 / tau_256 of the assignment).  Per zone, activity = vact_z / (mean of
+ * vact over the head's zones) + the audio gate; the block volume is 4 units if activity <
+ * tau_256, 2 units if < tau_128, else 1 unit (a smaller one when no shape of the chosen
+ * volume tiles the zone), and the shape is the Eq. 7 choice among that volume's
+ * candidates, as in prism_assign_shapes.
+ * vact     float [B][Hh][nZ] from prism_zone_stats_ex.
+ * margin   optional out: the smaller of the shape margin and |activity - tau| / tau.
+ * Errors: a candidate not of 1, 2 or 4 units or no unit-volume shape tiling the zone ->
+ * PRISM_ERR_SHAPE; not 0 < tau_256 <= tau_128 -> PRISM_ERR_ARG. */
+prism_status prism_assign_shapes_multi(const float* stats, const float* vact, int B, int Hh, const prism_grid* grid,
+                                       const prism_shapes* shapes, const prism_shape_params* params, float tau_128,
+                                       float tau_256, int32_t* shape_id, float* margin, hipStream_t stream);
+
+/* Block-level valid counts for a mixed-volume assignment: each block is identified by
+ * its first unit (shapes->vol slots), which receives the whole block's valid count; its
+ * other units receive 0.
+ * unit_valid  int32 [B][Hh][nb] per-unit counts from prism_permute(..., block_valid) with the
+ *             same mixed table (nb = zones * zone volume / unit).
+ * block_valid out int32 [B][Hh][nb]: the input of prism_select_blocks with vol = unit (a
+ *             block's valid rows are contiguous from its first unit). */
+prism_status prism_block_heads(const int32_t* unit_valid, const int32_t* shape_id, int B, int Hh,
+                               const prism_grid* grid, const prism_shapes* shapes, int32_t* block_valid,
+                               hipStream_t stream);
 
 /* Token permutation into blocks (abstract: each block's tokens are contiguous).
  * Slot order: zones in raster order; a zone's blocks in raster order over its block grid;
@@ -196,6 +235,19 @@ prism_status prism_blocks_to_tiles(const int32_t* block_valid, const int32_t* se
                                    int k_max, int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt,
                                    int32_t* tile_rev_ptr, int32_t* tile_rev_idx, void* workspace, size_t ws_bytes,
                                    hipStream_t stream);
+
+/* prism_blocks_to_tiles for a mixed-volume assignment, where blocks are identified by
+ * their first 64-row unit (prism_block_heads) and own the following live units: tile
+ * numbering is the unit numbering (nb tiles), tile_valid is the per-unit count from
+ * prism_permute, and lists hold up to k_max * max_units tiles (max_units = the largest
+ * block volume / 64).  Output layouts otherwise as prism_blocks_to_tiles; workspace:
+ * prism_tiles_mixed_workspace_size() bytes. */
+size_t prism_tiles_mixed_workspace_size(int B, int Hh, int nb);
+prism_status prism_blocks_to_tiles_mixed(const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                         const int32_t* rev_ptr, const int32_t* rev_idx, int B, int Hh, int nb,
+                                         int k_max, int max_units, int32_t* tile_idx, int32_t* tile_cnt,
+                                         int32_t* tile_rev_ptr, int32_t* tile_rev_idx, void* workspace,
+                                         size_t ws_bytes, hipStream_t stream);
 
 /* Block-sparse attention forward (Figure 2 caption).  Query row i of block I attends
  * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:

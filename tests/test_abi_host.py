@@ -41,6 +41,14 @@ def test_every_declared_symbol_is_exported(lib):
     assert set(_lib.PROTOTYPES) == set(names)
 
 
+def test_struct_sizes_match_the_header():
+    """The ctypes mirrors of the header's structs have the header's array sizes."""
+    from content_adaptive_block_zone_amd import _lib
+    m = re.search(r"#define\s+PRISM_MAX_SHAPES\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == _lib.MAX_SHAPES
+    assert ctypes.sizeof(_lib.PrismShapes) == 4 * (2 + 3 * _lib.MAX_SHAPES)
+
+
 def test_zone_and_block_counts_match_the_oracle(lib):
     from content_adaptive_block_zone_amd import api
     for w in WORKLOADS:
