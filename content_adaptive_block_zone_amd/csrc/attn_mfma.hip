@@ -55,6 +55,9 @@ __device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+// 2^x by the hardware instruction; results below 2^-126 (probabilities too small to register
+// in a bf16 or fp32 sum of terms up to 1) flush to zero
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ u32x4 zero_u4() { return u32x4{0u, 0u, 0u, 0u}; }
 
 template <typename V>
@@ -130,16 +133,17 @@ __device__ __forceinline__ void owner_of(const AttnArgs& a, int& I, int& bh) {
 
 // The streamed block list of a workgroup, with each block's valid-row count, is copied to
 // LDS once (packed as J | n << 16), so that finding the next block to prefetch costs an
-// LDS read instead of two dependent global loads.  Lists longer than kMetaCap (or block
-// indices past 16 bits) fall back to reading global memory per step.
+// LDS read instead of two dependent global loads.  Lists longer than the kernel's capacity
+// (or block indices past 16 bits) fall back to reading global memory per step.
 constexpr int kMetaCap = 2048;
 struct BlockList {
   const int32_t* lst;  // nullptr in dense mode (block k is k)
   int cnt;
   bool in_lds;
 };
+template <int CAP = kMetaCap>
 __device__ __forceinline__ BlockList load_list(const AttnArgs& a, int bh, const int32_t* lst, int cnt, int* meta) {
-  BlockList L{lst, cnt, !a.dense && cnt <= kMetaCap && a.nb < 65536};
+  BlockList L{lst, cnt, !a.dense && cnt <= CAP && a.nb < 65536};
   if (L.in_lds)
     for (int k = threadIdx.x; k < cnt; k += NT) {
       const int J = lst[k];
@@ -235,18 +239,54 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[8 * s + e];
   return r;
 }
-// transposed copy in kappa32 order: tt[c][tpos32(r)]
-__device__ __forceinline__ void put_cols32(const Chunks& c, uint16_t* tt) {
-  const int rq = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;
-  const int p0 = tpos32(4 * rq);  // rows 4rq..4rq+3 sit at p0..p0+3
+// ---- direct-to-LDS staging (backward kernels).  A streamed 64x128 bf16 tile is copied by
+// global_load_lds (16 bytes per lane, written to LDS in lane order, no registers involved)
+// into an unpadded tile of 256-byte rows whose 16-byte chunks are permuted by an XOR with
+// sw(r) = 4(r%4) + (r/4)%4.  Reads of one chunk from 16 consecutive rows (the row operands)
+// and transposing reads of an aligned 64-byte span from 4 consecutive rows both land on 16
+// distinct chunk positions, i.e. on all 64 banks once.
+constexpr int TB = TR * D * 2;  // bytes of a tile
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
+__device__ __forceinline__ int sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// element offset of (row r, column c) in a tile
+__device__ __forceinline__ int tofs(int r, int c) { return r * D + ((((c >> 3) ^ sw(r)) & 15) << 3) + (c & 7); }
+// tile <- rows 0..63 of src; rows past n repeat row n-1 (their products are masked).  Wave w
+// writes rows 16w..16w+15, 4 rows (1 KB) per instruction.
+// The copy is written as inline assembly so that the compiler, which would otherwise make
+// the next LDS read of any stage wait for it, leaves its completion to the kernel: the
+// kernels wait for their own copies (wait_loads) before the barrier that opens a stage,
+// and no LDS location is read while a copy into it can be in flight.  M0 holds the LDS
+// destination; one wait state separates its write from the copy.
+__device__ __forceinline__ void copy16_to_lds(const void* gsrc, const void* lds_dst) {
+  const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds_dst);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m));
+}
+__device__ __forceinline__ void load_tile(const bf16_t* src, int n, uint16_t* tile) {
+  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = (c.v[i][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-    *reinterpret_cast<u32x2*>(tt + tswz(c8 + j, p0)) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * i + (l >> 4);
+    copy16_to_lds(src + size_t(max(min(r, n - 1), 0)) * D + (((l & 15) ^ sw(r)) << 3), tile + (16 * w + 4 * i) * D);
   }
 }
+// A operand of a 32x32x16 product whose rows are tile columns 32t.. (d) and whose 16 k are
+// tile rows 16j.. in kappa32 order, by two transposing reads (ds_read_b64_tr_b16).  Within
+// each 16 lanes such a read returns to lane i element i%4 of the 4-element pieces that lanes
+// 4k + i/4 address (k = 0..3); so lane 16b + 4q + c of half g addresses row
+// 16j + 8h + 4g + q, columns 32t + 16b + 4c.., and receives column 32t + 16b + 4q + c of
+// rows 16j + 8h + 4g + 0..3, which are kappa32 positions 8g + 4h + 0..3.
+__device__ __forceinline__ bf16x8 ldtr(const uint16_t* tile, int t, int j) {
+  const int l = threadIdx.x & 63;
+  const int c = 32 * t + 16 * ((l >> 4) & 1) + 4 * (l & 3);
+  const int r = 16 * j + 4 * (l >> 5) + ((l & 15) >> 2);
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + tofs(r, c)));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + tofs(r + 8, c)));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// vmcnt(0): the direct-to-LDS copies this wave issued have landed
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 // rows 8j+4g .. +3 of column `col` of a 32x32 accumulator tile, times s, as 4 bf16
 __device__ __forceinline__ void store4_32(bf16_t* p, const f32x16& c, int j, float s) {
   *reinterpret_cast<u32x2*>(p) = u32x2{pk2(c[4 * j] * s, c[4 * j + 1] * s), pk2(c[4 * j + 2] * s, c[4 * j + 3] * s)};
@@ -371,14 +411,12 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
 // ------------------------------------------------------------------ dQ (32x32x16)
 // Owner: query block I.  Wave w = (qh = w&1, kh = w>>1) handles queries 32qh.. against
 // keys 32kh.. of every streamed key block and accumulates a partial dQ^T over its key
-// half; the two halves are summed through LDS at the end.
+// half; the two halves are summed through LDS at the end.  K and V tiles stream through
+// two LDS stages: the copy of the next pair is issued right after the barrier that opens
+// the current one.
 __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
-  constexpr int B_K = TR * LP * 2, B_KT = D * LPT * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * B_K + B_KT];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
   __shared__ int sMeta[kMetaCap];
-  uint16_t* sK = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* sV = reinterpret_cast<uint16_t*>(smem + B_K);
-  uint16_t* sKt = reinterpret_cast<uint16_t*>(smem + 2 * B_K);
   int I, bh;
   owner_of<16>(a, I, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -407,43 +445,41 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
   for (int t = 0; t < 4; ++t) dq[t] = zero16();
   const float sl2 = a.scale * LOG2E;
 
-  Chunks ck, cv;
-  int J = 0, nJ = 0;
-  if (cnt > 0) {
-    list_at(a, bh, bl, sMeta, 0, J, nJ, a.nkrows);
-    fetch(ck, K + row0_of(a, bh, J) * D, nJ);
-    fetch(cv, V + row0_of(a, bh, J) * D, nJ);
-  }
+  // stage st: K tile at 2st, V tile at 2st+1
+  auto issue = [&](int k, int st) {
+    int J, n;
+    list_at(a, bh, bl, sMeta, k, J, n, a.nkrows);
+    const size_t r0 = row0_of(a, bh, J);
+    load_tile(K + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
+    load_tile(V + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
+    return n;
+  };
+  int n_next = cnt > 0 ? issue(0, 0) : 0;
   for (int it = 0; it < cnt; ++it) {
+    const int st = it & 1, nJ = n_next;
+    wait_loads();
     __syncthreads();
-    put_rows(ck, sK);
-    put_rows(cv, sV);
-    put_cols32(ck, sKt);
-    __syncthreads();
-    const int nJc = nJ;
-    if (it + 1 < cnt) {
-      list_at(a, bh, bl, sMeta, it + 1, J, nJ, a.nkrows);
-      fetch(ck, K + row0_of(a, bh, J) * D, nJ);
-      fetch(cv, V + row0_of(a, bh, J) * D, nJ);
-    }
+    if (it + 1 < cnt) n_next = issue(it + 1, st ^ 1);
+    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + 2 * st * TB);
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (2 * st + 1) * TB);
     // S^T, dP^T: rows = keys 32kh + acc_row32(e, g), column = query qrow
-    f32x16 st = zero16(), dp = zero16();
+    f32x16 st_ = zero16(), dp = zero16();
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      st = mma32(lds8<bf16x8>(sK + (32 * kh + l32) * LP + 16 * s + 8 * g), qf[s], st);
-      dp = mma32(lds8<bf16x8>(sV + (32 * kh + l32) * LP + 16 * s + 8 * g), gf[s], dp);
+      st_ = mma32(lds8<bf16x8>(sK + tofs(32 * kh + l32, 16 * s + 8 * g)), qf[s], st_);
+      dp = mma32(lds8<bf16x8>(sV + tofs(32 * kh + l32, 16 * s + 8 * g)), gf[s], dp);
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const bool ok = 32 * kh + acc_row32(e, g) < nJc;
-      const float p = ok ? exp2f(st[e] * sl2 - lse2) : 0.f;
+      const bool ok = 32 * kh + acc_row32(e, g) < nJ;
+      const float p = ok ? exp2_fast(st_[e] * sl2 - lse2) : 0.f;
       dp[e] = p * (dp[e] - Dq);
     }
     const bf16x8 s0 = pack8(dp, 0), s1 = pack8(dp, 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      dq[t] = mma32(ldt8<bf16x8>(sKt, 32 * t + l32, 4 * kh + g), s0, dq[t]);
-      dq[t] = mma32(ldt8<bf16x8>(sKt, 32 * t + l32, 4 * kh + 2 + g), s1, dq[t]);
+      dq[t] = mma32(ldtr(sK, t, 2 * kh), s0, dq[t]);
+      dq[t] = mma32(ldtr(sK, t, 2 * kh + 1), s1, dq[t]);
     }
   }
   // sum the two key halves: waves with kh = 1 hand their partials to kh = 0 through LDS
@@ -473,18 +509,14 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
 // queries 32x.. of each streamed query block for S and dP.  Wave (kh, 0) accumulates dV^T
 // and wave (kh, 1) dK^T of those 32 keys over all 64 queries: after the softmax step the
 // pair swaps halves through LDS (x = 0 hands over its dS, x = 1 its P), so neither keeps a
-// partial sum of the other's output and no reduction is left for the end.
+// partial sum of the other's output and no reduction is left for the end.  Q, dO, LSE and
+// D stream through two LDS stages, copied without passing through registers.
+constexpr int kMetaCapKV = 1280;  // keeps two workgroups per CU within 160 KB of LDS
 __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
-  constexpr int B_Q = TR * LP * 2, B_QT = D * LPT * 2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * B_Q + 2 * B_QT];
-  __shared__ float sL[TR], sD[TR];
-  __shared__ int sMeta[kMetaCap];
-  uint16_t* sQ = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* sG = reinterpret_cast<uint16_t*>(smem + B_Q);
-  uint16_t* sQt = reinterpret_cast<uint16_t*>(smem + 2 * B_Q);
-  uint16_t* sGt = reinterpret_cast<uint16_t*>(smem + 2 * B_Q + B_QT);
-  // swap area (2 KB per wave) over sQ, which is dead once S and dP are formed
-  bf16x8* xbuf = reinterpret_cast<bf16x8*>(smem);
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB + 4 * 2048];
+  __shared__ __attribute__((aligned(16))) float sLD[2][4][TR];  // [stage][LSE*log2(e), D, .., ..][row]
+  __shared__ int sMeta[kMetaCapKV];
+  bf16x8* xbuf = reinterpret_cast<bf16x8*>(smem + 4 * TB);  // 2 KB per wave
   int J, bh;
   owner_of<64>(a, J, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
@@ -504,7 +536,7 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
     cnt = rp[J + 1] - rp[J];
     lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rp[J];
   }
-  const BlockList bl = load_list(a, bh, lst, cnt, sMeta);
+  const BlockList bl = load_list<kMetaCapKV>(a, bh, lst, cnt, sMeta);
   const int key = 32 * kh + l32;
   const bool kok = key < nJ;
   bf16x8 kf[8], vf[8];
@@ -517,62 +549,56 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) acc[t] = zero16();
   const float sl2 = a.scale * LOG2E;
-  const uint16_t* At = x == 0 ? sGt : sQt;  // dO^T for dV, Q^T for dK
 
-  // The next query block's Q (with its LSE and D) is fetched right after the barrier and
-  // its dO after the swap, so that the two staging sets are never live together with the
-  // S and dP accumulators.
-  Chunks cq, cg;
-  float pl = 0.f, pd = 0.f;
-  int nIn = 0;
-  size_t qn = 0;
-  auto fetch_q = [&](int k) {
-    int Ib;
-    list_at(a, bh, bl, sMeta, k, Ib, nIn, a.nrows);
-    qn = row0_of(a, bh, Ib);
-    fetch(cq, Q + qn * D, nIn);
-    if (tid < TR) {
-      const size_t r = qn + min(tid, nIn - 1);
-      pl = a.lse_in[r];
-      pd = a.Dbuf[r];
-    }
+  // stage st: Q tile at 2st, dO tile at 2st+1 (copied to LDS directly); the LSE or D value
+  // of row `lane` comes through a register (odd waves D, even waves LSE) and is written to
+  // sLD[st][w] before the barrier that opens the stage.
+  float ld = 0.f;
+  auto issue = [&](int k, int st) {
+    int Ib, n;
+    list_at(a, bh, bl, sMeta, k, Ib, n, a.nrows);
+    const size_t r0 = row0_of(a, bh, Ib);
+    load_tile(Q + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
+    load_tile(Gd + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
+    ld = ((w & 1) ? a.Dbuf : a.lse_in)[r0 + max(min(lane, n - 1), 0)];
+    return n;
   };
-  if (cnt > 0) {
-    fetch_q(0);
-    fetch(cg, Gd + qn * D, nIn);
-  }
+  int n_next = cnt > 0 ? issue(0, 0) : 0;
   for (int it = 0; it < cnt; ++it) {
+    const int st = it & 1, nIn = n_next;
+    wait_loads();
+    sLD[st][w][lane] = (w & 1) ? ld : ld * LOG2E;
     __syncthreads();
-    put_rows(cq, sQ);
-    put_rows(cg, sG);
-    put_cols32(cq, sQt);
-    put_cols32(cg, sGt);
-    if (tid < TR) {
-      sL[tid] = tid < nIn ? pl * LOG2E : INFINITY;
-      sD[tid] = tid < nIn ? pd : 0.f;
+    if (it + 1 < cnt) n_next = issue(it + 1, st ^ 1);
+    const uint16_t* sQ = reinterpret_cast<const uint16_t*>(smem + 2 * st * TB);
+    const uint16_t* sG = reinterpret_cast<const uint16_t*>(smem + (2 * st + 1) * TB);
+    // LSE and D of this lane's 16 rows (4 runs of 4), read before the products
+    f32x4 lr[4], dr[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lr[q] = *reinterpret_cast<const f32x4*>(&sLD[st][0][32 * x + 8 * q + 4 * g]);
+      dr[q] = *reinterpret_cast<const f32x4*>(&sLD[st][1][32 * x + 8 * q + 4 * g]);
     }
-    __syncthreads();
-    const bool more = it + 1 < cnt;
-    if (more) fetch_q(it + 1);
     // S, dP: rows = queries 32x + acc_row32(e, g), column = key
     f32x16 s_ = zero16(), dp = zero16();
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      s_ = mma32(lds8<bf16x8>(sQ + (32 * x + l32) * LP + 16 * s + 8 * g), kf[s], s_);
-      dp = mma32(lds8<bf16x8>(sG + (32 * x + l32) * LP + 16 * s + 8 * g), vf[s], dp);
+      s_ = mma32(lds8<bf16x8>(sQ + tofs(32 * x + l32, 16 * s + 8 * g)), kf[s], s_);
+      dp = mma32(lds8<bf16x8>(sG + tofs(32 * x + l32, 16 * s + 8 * g)), vf[s], dp);
     }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
+      // rows past nIn repeat row nIn-1 (finite); their p is set to 0
       const int r = 32 * x + acc_row32(e, g);
-      const float p = exp2f(s_[e] * sl2 - sL[r]);
+      const float p0 = exp2_fast(s_[e] * sl2 - lr[e >> 2][e & 3]);
+      const float p = r < nIn ? p0 : 0.f;
       s_[e] = p;
-      dp[e] = p * (dp[e] - sD[r]);
+      dp[e] = p * (dp[e] - dr[e >> 2][e & 3]);
     }
     // own: the operand this wave keeps; give: the one its partner (w ^ 2) needs
     const bf16x8 P0 = pack8(s_, 0), P1 = pack8(s_, 1), S0 = pack8(dp, 0), S1 = pack8(dp, 1);
     const bf16x8 own0 = x == 0 ? P0 : S0, own1 = x == 0 ? P1 : S1;
     const bf16x8 give0 = x == 0 ? S0 : P0, give1 = x == 0 ? S1 : P1;
-    __syncthreads();  // every wave is done with sQ
     xbuf[w * 128 + lane] = give0;
     xbuf[w * 128 + 64 + lane] = give1;
     __syncthreads();
@@ -580,13 +606,13 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
     // query half 0 comes from wave x = 0, half 1 from x = 1
     const bf16x8 lo0 = x == 0 ? own0 : got0, lo1 = x == 0 ? own1 : got1;
     const bf16x8 hi0 = x == 0 ? got0 : own0, hi1 = x == 0 ? got1 : own1;
-    if (more) fetch(cg, Gd + qn * D, nIn);
+    const uint16_t* At = x == 0 ? sG : sQ;  // dO^T for dV, Q^T for dK
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, g), lo0, acc[t]);
-      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, 2 + g), lo1, acc[t]);
-      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, 4 + g), hi0, acc[t]);
-      acc[t] = mma32(ldt8<bf16x8>(At, 32 * t + l32, 6 + g), hi1, acc[t]);
+      acc[t] = mma32(ldtr(At, t, 0), lo0, acc[t]);
+      acc[t] = mma32(ldtr(At, t, 1), lo1, acc[t]);
+      acc[t] = mma32(ldtr(At, t, 2), hi0, acc[t]);
+      acc[t] = mma32(ldtr(At, t, 3), hi1, acc[t]);
     }
   }
   if (kok || (!a.dense && key < TR)) {
