@@ -9,8 +9,9 @@
 //   * a workgroup of 4 wavefronts owns one 64-row block (the query block in the forward
 //     and dQ kernels, the key block in the dK/dV kernel);
 //   * the streamed block (K/V, or Q/dO) is staged in LDS once per pair and shared by the
-//     four waves; the next pair's tiles are fetched into registers while the current one
-//     is computed.
+//     four waves, and the next pair's tiles are in flight while the current one is
+//     computed: the forward fetches them into registers and writes them to LDS; the
+//     backward kernels copy them straight into a second LDS stage (global_load_lds).
 // Forward: wave w owns rows 16w..16w+15 and uses v_mfma_f32_16x16x32 {bf16, f16}
 // (A = 16 rows x 32 k, lane l: row l%16, k = 8(l/16)..+7; B likewise with columns;
 // C = 4 registers, lane l register i at row 4(l/16)+i, column l%16).
@@ -18,11 +19,15 @@
 // does twice the work per LDS operand byte; the dQ waves sum their two key halves once at
 // the end, the dK/dV waves swap P and dS halves through LDS each pair.
 // Products whose contraction runs over the streamed block's rows (P V, Q^T dS, dO^T P,
-// K^T dS) take accumulator registers directly as the B operand.  The matching A operand
-// is a transposed tile that the staging writes into LDS with its rows in the order of
-// those registers ("kappa16" for the 16x16 tiles, "kappa32" for the 32x32 tiles; see
-// tpos and tpos32), so that operand is one 16-byte LDS read as well.  kappa16: within
-// each 32-row group, position 8G+e holds row 4G + e%4 + 16*(e/4).
+// K^T dS) take accumulator registers directly as the B operand, whose k index then runs
+// over the rows in the accumulator's order ("kappa16" for the 16x16 tiles, "kappa32" for
+// the 32x32 tiles).  The matching A operand is the streamed tile
+// transposed with its rows in that order: the forward writes such a transposed copy of V
+// into LDS (one 16-byte read per operand); the backward kernels read it from the
+// row-major tile with gfx950's transposing LDS read (ds_read_b64_tr_b16), two 8-byte
+// reads per operand.  kappa16 (tpos): within each 32-row group, position 8G+e holds row
+// 4G + e%4 + 16*(e/4).  kappa32: within each 16-row group, position p holds row p with
+// bits 2 and 3 swapped.
 // The forward's P V product runs in fp16 (probabilities in [0, 1] keep 11 bits; bf16 V
 // values are exact in fp16 within its range), the rest in bf16; all accumulation is fp32.
 #include "prism_internal.h"
@@ -159,12 +164,12 @@ __device__ __forceinline__ void list_at(const AttnArgs& a, int bh, const BlockLi
     J = k;
     n = min(TR, srows - k * TR);
   } else if (L.in_lds) {
-    const int m = meta[k];
+    const int m = __builtin_amdgcn_readfirstlane(meta[k]);  // the same for every lane
     J = m & 0xffff;
     n = m >> 16;
   } else {
-    J = L.lst[k];
-    n = nrows_of(a, bh, J);
+    J = __builtin_amdgcn_readfirstlane(L.lst[k]);
+    n = __builtin_amdgcn_readfirstlane(nrows_of(a, bh, J));
   }
 }
 
@@ -232,7 +237,6 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 __device__ __forceinline__ int acc_row32(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
-__device__ __forceinline__ int tpos32(int r) { return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1); }
 __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   bf16x8 r;
 #pragma unroll
@@ -252,23 +256,25 @@ typedef __attribute__((address_space(3))) v4i16 lds_v4i16_t;
 __device__ __forceinline__ int sw(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
 // element offset of (row r, column c) in a tile
 __device__ __forceinline__ int tofs(int r, int c) { return r * D + ((((c >> 3) ^ sw(r)) & 15) << 3) + (c & 7); }
-// tile <- rows 0..63 of src; rows past n repeat row n-1 (their products are masked).  Wave w
-// writes rows 16w..16w+15, 4 rows (1 KB) per instruction.
-// The copy is written as inline assembly so that the compiler, which would otherwise make
+// One 16-byte-per-lane copy, global memory -> LDS.  It is written as inline assembly so that the compiler, which would otherwise make
 // the next LDS read of any stage wait for it, leaves its completion to the kernel: the
 // kernels wait for their own copies (wait_loads) before the barrier that opens a stage,
 // and no LDS location is read while a copy into it can be in flight.  M0 holds the LDS
-// destination; one wait state separates its write from the copy.
-__device__ __forceinline__ void copy16_to_lds(const void* gsrc, const void* lds_dst) {
+// destination; one wait state separates its write from the copy.  The source is a
+// wave-uniform base (SGPRs) plus a 32-bit byte offset per lane.
+__device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, const void* lds_dst) {
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds_dst);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gsrc), "{m0}"(m));
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m));
 }
+// tile <- rows 0..63 of src (wave-uniform); rows past n repeat row n-1 (their products are
+// masked).  Wave w writes rows 16w..16w+15, 4 rows (1 KB) per instruction.
 __device__ __forceinline__ void load_tile(const bf16_t* src, int n, uint16_t* tile) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * i + (l >> 4);
-    copy16_to_lds(src + size_t(max(min(r, n - 1), 0)) * D + (((l & 15) ^ sw(r)) << 3), tile + (16 * w + 4 * i) * D);
+    const uint32_t off = uint32_t(max(min(r, n - 1), 0)) * (D * 2) + uint32_t(((l & 15) ^ sw(r)) << 4);
+    copy16_to_lds(src, off, tile + (16 * w + 4 * i) * D);
   }
 }
 // A operand of a 32x32x16 product whose rows are tile columns 32t.. (d) and whose 16 k are
