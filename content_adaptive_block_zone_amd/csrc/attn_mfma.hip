@@ -4,32 +4,27 @@
 // Shape of the work.  Every (query block, key block) pair costs 2 MFLOP per product but
 // needs a whole 64x128 tile pair from memory, and the key lists of neighbouring query
 // blocks barely overlap, so these kernels are bound by how fast tiles arrive, not by the
-// matrix cores.  The design therefore spends registers on occupancy and prefetch and
-// reads each streamed tile from memory exactly once per pair:
+// matrix cores.  Each streamed tile is read from memory exactly once per pair:
 //   * a workgroup of 4 wavefronts owns one 64-row block (the query block in the forward
-//     and dQ kernels, the key block in the dK/dV kernel);
-//   * the streamed block (K/V, or Q/dO) is staged in LDS once per pair and shared by the
-//     four waves, and the next pair's tiles are in flight while the current one is
-//     computed: the forward fetches them into registers and writes them to LDS; the
-//     backward kernels copy them straight into a second LDS stage (global_load_lds).
-// Forward: wave w owns rows 16w..16w+15 and uses v_mfma_f32_16x16x32 {bf16, f16}
-// (A = 16 rows x 32 k, lane l: row l%16, k = 8(l/16)..+7; B likewise with columns;
-// C = 4 registers, lane l register i at row 4(l/16)+i, column l%16).
-// Backward: the waves split the 64x64 pair 2x2 and use v_mfma_f32_32x32x16_bf16, which
-// does twice the work per LDS operand byte; the dQ waves sum their two key halves once at
-// the end, the dK/dV waves swap P and dS halves through LDS each pair.
+//     and dQ kernels, the key block in the dK/dV kernel), whose own operands stay in
+//     registers for the whole list;
+//   * the streamed block (K/V, or Q/dO) is copied straight from memory into LDS
+//     (global_load_lds, no registers involved) and shared by the four waves; there are two
+//     LDS stages, and the next pair's copy is in flight while the current one is computed.
+// All three kernels split the 64x64 pair 2x2 over the waves and use
+// v_mfma_f32_32x32x16_bf16 (A = 32 rows x 16 k, lane l: row l%32, k = 8(l/32)..+7; B
+// likewise with columns; C = 16 registers, lane l register e at row 8(e/4) + 4(l/32) + e%4,
+// column l%32).  The forward and dQ waves each cover one key half and merge the halves
+// once at the end; the dK/dV waves swap P and dS halves through LDS each pair.
 // Products whose contraction runs over the streamed block's rows (P V, Q^T dS, dO^T P,
 // K^T dS) take accumulator registers directly as the B operand, whose k index then runs
-// over the rows in the accumulator's order ("kappa16" for the 16x16 tiles, "kappa32" for
-// the 32x32 tiles).  The matching A operand is the streamed tile
-// transposed with its rows in that order: the forward writes such a transposed copy of V
-// into LDS (one 16-byte read per operand); the backward kernels read it from the
-// row-major tile with gfx950's transposing LDS read (ds_read_b64_tr_b16), two 8-byte
-// reads per operand.  kappa16 (tpos): within each 32-row group, position 8G+e holds row
-// 4G + e%4 + 16*(e/4).  kappa32: within each 16-row group, position p holds row p with
-// bits 2 and 3 swapped.
-// The forward's P V product runs in fp16 (probabilities in [0, 1] keep 11 bits; bf16 V
-// values are exact in fp16 within its range), the rest in bf16; all accumulation is fp32.
+// over the rows in the accumulator's order, "kappa32": within each 16-row group, position
+// p holds row p with bits 2 and 3 swapped.  The matching A operand is the streamed tile
+// transposed with its rows in that order, read from the row-major tile with gfx950's
+// transposing LDS read (ds_read_b64_tr_b16), two 8-byte reads per operand.
+// All accumulation is fp32; the forward's P V product takes P as a bf16 head plus a bf16
+// remainder.
+
 #include "prism_internal.h"
 
 namespace prism {
@@ -43,23 +38,13 @@ namespace {
 constexpr int D = 128;        // head dimension
 constexpr int TR = 64;        // rows per block
 constexpr int NT = 256;       // 4 wavefronts
-constexpr int LP = D + 8;     // LDS pitch (elements) of a row-major [64][128] tile
-constexpr int LPT = TR + 8;   // LDS pitch (elements) of a transposed [128][64] tile
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ f32x4 mma(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mma(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // 2^x by the hardware instruction; results below 2^-126 (probabilities too small to register
 // in a bf16 or fp32 sum of terms up to 1) flush to zero
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -73,38 +58,9 @@ __device__ __forceinline__ V lds8(const uint16_t* p) {
 __device__ __forceinline__ bf16x8 gld8(const bf16_t* p, bool ok) {
   return __builtin_bit_cast(bf16x8, ok ? *reinterpret_cast<const u32x4*>(p) : zero_u4());
 }
-// B operand from two 16-row accumulator tiles (rows 4G+i of each): k-values 0-3 from the
-// first, 4-7 from the second.
-__device__ __forceinline__ bf16x8 pack_bf16(const f32x4& x, const f32x4& y) {
-  bf16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (__bf16)x[i];
-    r[4 + i] = (__bf16)y[i];
-  }
-  return r;
-}
-__device__ __forceinline__ f16x8 pack_f16(const f32x4& x, const f32x4& y) {
-  f16x8 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[i] = (_Float16)x[i];
-    r[4 + i] = (_Float16)y[i];
-  }
-  return r;
-}
 __device__ __forceinline__ uint32_t pk2(float a, float b) {
   return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) | (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
 }
-__device__ __forceinline__ void store4(bf16_t* p, const f32x4& c, float s) {
-  *reinterpret_cast<u32x2*>(p) = u32x2{pk2(c[0] * s, c[1] * s), pk2(c[2] * s, c[3] * s)};
-}
-// position of block row r inside a transposed tile (inverse of kappa16)
-__device__ __forceinline__ int tpos(int r) {
-  const int kk = r & 31;
-  return (r & 32) | (((kk & 15) >> 2) << 3) | ((kk >> 4) << 2) | (kk & 3);
-}
-
 __device__ __forceinline__ int nrows_of(const AttnArgs& a, int bh, int I) {
   return a.dense ? min(TR, a.nrows - I * TR) : a.bvalid[size_t(bh) * a.nb + I];
 }
@@ -173,55 +129,7 @@ __device__ __forceinline__ void list_at(const AttnArgs& a, int bh, const BlockLi
   }
 }
 
-// ---- staging: a 64x128 bf16 tile = 1024 chunks of 16 bytes, 4 per thread.  Thread t
-// fetches rows 4*(t/16)+i (i = 0..3) of column chunk 8*(t%16): every load instruction of a
-// wave reads whole 256-byte rows, and the thread holds the 4 consecutive rows of each of its
-// 8 columns, which the transposed copy writes as one 8-byte run.
-struct Chunks {
-  u32x4 v[4];
-};
-__device__ __forceinline__ void fetch(Chunks& c, const bf16_t* src, int nrows) {
-  const int rq = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * rq + i;
-    c.v[i] = r < nrows ? *reinterpret_cast<const u32x4*>(src + size_t(r) * D + c8) : zero_u4();
-  }
-}
-// row-major copy: tile[r][c]
-__device__ __forceinline__ void put_rows(const Chunks& c, uint16_t* t) {
-  const int rq = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4*>(t + (4 * rq + i) * LP + c8) = c.v[i];
-}
-// Offset of position p of transposed row c: the 8-element group of p is XOR-swizzled with
-// (c / 16) % 8, so that the 8-byte writes of 16 column chunks and the 16-byte operand reads
-// of 16 consecutive rows each fall on distinct LDS banks.
-__device__ __forceinline__ int tswz(int c, int p) { return c * LPT + ((((p >> 3) ^ (c >> 4)) & 7) << 3) + (p & 7); }
-// transposed copy: tt[c][tpos(r)], optionally converted to fp16
-template <bool F16>
-__device__ __forceinline__ void put_cols(const Chunks& c, uint16_t* tt) {
-  const int rq = threadIdx.x >> 4, c8 = (threadIdx.x & 15) * 8;
-  const int p0 = tpos(4 * rq);  // rows 4rq..4rq+3 sit at p0..p0+3
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint32_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t x = (c.v[i][j >> 1] >> ((j & 1) * 16)) & 0xffffu;
-      if (F16) x = __builtin_bit_cast(uint16_t, (_Float16)__uint_as_float(x << 16));
-      h[i] = x;
-    }
-    *reinterpret_cast<u32x2*>(tt + tswz(c8 + j, p0)) = u32x2{h[0] | (h[1] << 16), h[2] | (h[3] << 16)};
-  }
-}
-// A operand from a transposed tile: row c, positions 8g..8g+7 (g = group index 0..7)
-template <typename V>
-__device__ __forceinline__ V ldt8(const uint16_t* tt, int c, int g) {
-  return lds8<V>(tt + c * LPT + (((g ^ (c >> 4)) & 7) << 3));
-}
-
-// ---- 32x32x16 products (backward kernels).  A = 32 rows x 16 k (lane l: row l%32,
+// ---- 32x32x16 products.  A = 32 rows x 16 k (lane l: row l%32,
 // k = 8(l/32)..+7), B likewise with columns, C = 16 registers: lane l register e at row
 // 8(e/4) + 4(l/32) + e%4, column l%32.  Registers 8s..8s+7 of an accumulator are the B
 // operand of a product contracting over its rows when the A operand lists those rows in
@@ -229,6 +137,11 @@ __device__ __forceinline__ V ldt8(const uint16_t* tt, int c, int g) {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+// value of lane l ^ 32 (v_permlane32_swap: a VALU exchange of the two 32-lane halves)
+__device__ __forceinline__ float xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
 }
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -243,7 +156,7 @@ __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   for (int e = 0; e < 8; ++e) r[e] = (__bf16)c[8 * s + e];
   return r;
 }
-// ---- direct-to-LDS staging (backward kernels).  A streamed 64x128 bf16 tile is copied by
+// ---- direct-to-LDS staging.  A streamed 64x128 bf16 tile is copied by
 // global_load_lds (16 bytes per lane, written to LDS in lane order, no registers involved)
 // into an unpadded tile of 256-byte rows whose 16-byte chunks are permuted by an XOR with
 // sw(r) = 4(r%4) + (r/4)%4.  Reads of one chunk from 16 consecutive rows (the row operands)
@@ -266,8 +179,9 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, co
   const uint32_t m = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds_dst);
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m));
 }
-// tile <- rows 0..63 of src (wave-uniform); rows past n repeat row n-1 (their products are
-// masked).  Wave w writes rows 16w..16w+15, 4 rows (1 KB) per instruction.
+// tile <- rows 0..63 of src (wave-uniform); rows past n repeat row n-1 (finite; their
+// products are masked).  Wave w writes rows 16w..16w+15, 4 rows (1 KB) per instruction.
+// (Copying only the valid rows, with the other lanes inactive, measured 2-3 % slower.)
 __device__ __forceinline__ void load_tile(const bf16_t* src, int n, uint16_t* tile) {
   const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
@@ -298,119 +212,162 @@ __device__ __forceinline__ void store4_32(bf16_t* p, const f32x16& c, int j, flo
   *reinterpret_cast<u32x2*>(p) = u32x2{pk2(c[4 * j] * s, c[4 * j + 1] * s), pk2(c[4 * j + 2] * s, c[4 * j + 3] * s)};
 }
 
-// ------------------------------------------------------------------ forward
+// ------------------------------------------------------------------ forward (32x32x16)
+// Owner: query block I.  Wave w = (qh = w&1, kh = w>>1) takes queries 32qh.. against keys
+// 32kh.. of every streamed key block and keeps its own online softmax (running max m, sum
+// l and O^T) over its key half; the two halves are merged once at the end through LDS.
+// K and V tiles stream through two LDS stages as in the backward kernels.  The P V product
+// runs in bf16 on P split into a bf16 head and a bf16 remainder (P = hi + lo to about 16
+// bits), i.e. two products, which keeps the probabilities' rounding well below the
+// output's own bf16 rounding.
+// P split into bf16 head and remainder, accumulator registers 8s..8s+7
+__device__ __forceinline__ void split8(const f32x16& c, int s, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const __bf16 h = (__bf16)c[8 * s + e];
+    hi[e] = h;
+    lo[e] = (__bf16)(c[8 * s + e] - (float)h);
+  }
+}
 __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[TR * LP];
-  __shared__ __attribute__((aligned(16))) uint16_t sVt[D * LPT];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
+  __shared__ int sMeta[kMetaCap];
   int I, bh;
   owner_of<16>(a, I, bh);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l16 = lane & 15, G = lane >> 4;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int qh = w & 1, kh = w >> 1;
   const int nI = nrows_of(a, bh, I);
   const size_t q0 = row0_of(a, bh, I);
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   const bf16_t* K = static_cast<const bf16_t*>(a.k);
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   bf16_t* O = static_cast<bf16_t*>(a.out);
-  __shared__ int sMeta[kMetaCap];
   const int cnt = a.dense ? a.nkb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
   const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
-  const int qrow = 16 * w + l16;
+  const int qrow = 32 * qh + l32;
   const bool qok = qrow < nI;
-
-  bf16x8 qf[4];
+  bf16x8 qf[8];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) qf[s] = gld8(Q + (q0 + qrow) * D + 32 * s + 8 * G, qok);
-  f32x4 o[8];
+  for (int s = 0; s < 8; ++s) qf[s] = gld8(Q + (q0 + qrow) * D + 16 * s + 8 * g, qok);
+  f32x16 o[4];  // O^T: rows d = 32t + acc_row32(e, g), column = query qrow
 #pragma unroll
-  for (int t = 0; t < 8; ++t) o[t] = zero4();
-  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < 4; ++t) o[t] = zero16();
+  float m = -INFINITY, l = 0.f;  // over this wave's key half, log2 units
   const float sl2 = a.scale * LOG2E;
 
-  Chunks ck, cv;
-  int J = 0, nJ = 0;
-  if (cnt > 0) {
-    list_at(a, bh, bl, sMeta, 0, J, nJ, a.nkrows);
-    fetch(ck, K + krow0_of(a, bh, J) * D, nJ);
-    fetch(cv, V + krow0_of(a, bh, J) * D, nJ);
-  }
+  // stage st: K tile at 2st, V tile at 2st+1
+  auto issue = [&](int k, int st) {
+    int J, n;
+    list_at(a, bh, bl, sMeta, k, J, n, a.nkrows);
+    const size_t r0 = krow0_of(a, bh, J);
+    load_tile(K + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
+    load_tile(V + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
+    return n;
+  };
+  int n_next = cnt > 0 ? issue(0, 0) : 0;
   for (int it = 0; it < cnt; ++it) {
+    const int st = it & 1, nJ = n_next;
+    wait_loads();
     __syncthreads();
-    put_rows(ck, sK);
-    put_cols<true>(cv, sVt);
-    __syncthreads();
-    const int nJc = nJ;
-    if (it + 1 < cnt) {
-      list_at(a, bh, bl, sMeta, it + 1, J, nJ, a.nkrows);
-      fetch(ck, K + krow0_of(a, bh, J) * D, nJ);
-      fetch(cv, V + krow0_of(a, bh, J) * D, nJ);
+    if (it + 1 < cnt) n_next = issue(it + 1, st ^ 1);
+    const uint16_t* sK = reinterpret_cast<const uint16_t*>(smem + 2 * st * TB);
+    const uint16_t* sV = reinterpret_cast<const uint16_t*>(smem + (2 * st + 1) * TB);
+    // S^T: rows = keys 32kh + acc_row32(e, g), column = query qrow
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) sc = mma32(lds8<bf16x8>(sK + tofs(32 * kh + l32, 16 * s + 8 * g)), qf[s], sc);
+    // V^T operands of this wave's key half, read while the softmax runs
+    bf16x8 vt[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      vt[t][0] = ldtr(sV, t, 2 * kh);
+      vt[t][1] = ldtr(sV, t, 2 * kh + 1);
     }
-    // S^T tiles: rows = keys 16kt + 4G + i, column = this lane's query
-    f32x4 st[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) st[kt] = zero4();
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        st[kt] = mma(lds8<bf16x8>(sK + (16 * kt + l16) * LP + 32 * s + 8 * G), qf[s], st[kt]);
     float mx = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float v = (16 * kt + 4 * G + i < nJc) ? st[kt][i] * sl2 : -INFINITY;
-        st[kt][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    for (int e = 0; e < 16; ++e) {
+      const float v = 32 * kh + acc_row32(e, g) < nJ ? sc[e] * sl2 : -INFINITY;
+      sc[e] = v;
+      mx = fmaxf(mx, v);
+    }
+    mx = fmaxf(mx, xor32(mx));  // lane l^32 holds the other rows of the column
     const float mn = fmaxf(m, mx);
-    const float alpha = exp2f(m - mn);
+    const float mref = mn == -INFINITY ? 0.f : mn;  // no valid key yet in this half
+    const float alpha = exp2_fast(m - mref);
     float rs = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = exp2f(st[kt][i] - mn);
-        st[kt][i] = p;
-        rs += p;
-      }
-    rs += __shfl_xor(rs, 16, 64);
-    rs += __shfl_xor(rs, 32, 64);
+    for (int e = 0; e < 16; ++e) {
+      const float p = exp2_fast(sc[e] - mref);
+      sc[e] = p;
+      rs += p;
+    }
+    rs += xor32(rs);
     l = l * alpha + rs;
     m = mn;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) o[t] *= alpha;
-    const f16x8 p0 = pack_f16(st[0], st[1]), p1 = pack_f16(st[2], st[3]);
+    for (int t = 0; t < 4; ++t) o[t] *= alpha;
+    bf16x8 h0, r0_, h1, r1_;
+    split8(sc, 0, h0, r0_);
+    split8(sc, 1, h1, r1_);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      o[t] = mma(ldt8<f16x8>(sVt, 16 * t + l16, G), p0, o[t]);
-      o[t] = mma(ldt8<f16x8>(sVt, 16 * t + l16, 4 + G), p1, o[t]);
+    for (int t = 0; t < 4; ++t) {
+      o[t] = mma32(vt[t][0], h0, o[t]);
+      o[t] = mma32(vt[t][0], r0_, o[t]);
+      o[t] = mma32(vt[t][1], h1, o[t]);
+      o[t] = mma32(vt[t][1], r1_, o[t]);
     }
   }
-  // O^T tile t: rows d = 16t + 4G + i, column = query qrow.  O, LSE and the row norm are
-  // each optional (the norm serves the audio-to-video cross-attention's per-token norm).
+  // merge the key halves: waves with kh = 1 hand (m, l, O^T) to kh = 0 through LDS
+  __syncthreads();
+  float* red = reinterpret_cast<float*>(smem) + qh * (4 * 16 * 64 + 2 * 64);
+  if (kh == 1) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[(t * 16 + e) * 64 + lane] = o[t][e];
+    red[4 * 16 * 64 + lane] = m;
+    red[4 * 16 * 64 + 64 + lane] = l;
+  }
+  __syncthreads();
+  if (kh == 1) return;
+  {
+    const float m1 = red[4 * 16 * 64 + lane], l1 = red[4 * 16 * 64 + 64 + lane];
+    const float mm = fmaxf(m, m1);
+    const float mref = mm == -INFINITY ? 0.f : mm;
+    const float a0 = exp2_fast(m - mref), a1 = exp2_fast(m1 - mref);
+    l = l * a0 + l1 * a1;
+    m = mm;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[t][e] = o[t][e] * a0 + red[(t * 16 + e) * 64 + lane] * a1;
+  }
+  // O, LSE and the row norm are each optional (the norm serves the audio-to-video
+  // cross-attention's per-token norm)
   if (qok) {
     const float inv = 1.f / l;
     if (O) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) store4(O + (q0 + qrow) * D + 16 * t + 4 * G, o[t], inv);
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store4_32(O + (q0 + qrow) * D + 32 * t + 8 * j + 4 * g, o[t], j, inv);
     }
-    if (a.lse_out && G == 0) a.lse_out[q0 + qrow] = (m + log2f(l)) * 0.6931471805599453f;
+    if (a.lse_out && g == 0) a.lse_out[q0 + qrow] = (m + log2f(l)) * 0.6931471805599453f;
     if (a.norm_out) {
       float ss = 0.f;
 #pragma unroll
-      for (int t = 0; t < 8; ++t)
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ss = fmaf(o[t][i] * inv, o[t][i] * inv, ss);
-      ss += __shfl_xor(ss, 16, 64);   // the lanes of one query (same l16) are all in this branch
-      ss += __shfl_xor(ss, 32, 64);
-      if (G == 0) a.norm_out[q0 + qrow] = sqrtf(ss);
+        for (int e = 0; e < 16; ++e) ss = fmaf(o[t][e] * inv, o[t][e] * inv, ss);
+      ss += xor32(ss);  // both lanes of the query are in this branch
+      if (g == 0) a.norm_out[q0 + qrow] = sqrtf(ss);
     }
-  } else if (!a.dense) {
+  } else if (!a.dense && qrow < TR) {
 #pragma unroll
-    for (int t = 0; t < 8; ++t) store4(O + (q0 + qrow) * D + 16 * t + 4 * G, zero4(), 0.f);
-    if (G == 0) a.lse_out[q0 + qrow] = 0.f;
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) store4_32(O + (q0 + qrow) * D + 32 * t + 8 * j + 4 * g, o[t], j, 0.f);
+    if (g == 0) a.lse_out[q0 + qrow] = 0.f;
   }
 }
 
