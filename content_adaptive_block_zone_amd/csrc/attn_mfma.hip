@@ -128,6 +128,23 @@ __device__ __forceinline__ void list_at(const AttnArgs& a, int bh, const BlockLi
     n = __builtin_amdgcn_readfirstlane(nrows_of(a, bh, J));
   }
 }
+// The kernels walk their list in order.  In LDS mode the entry after the one being used is
+// read one step ahead (`pre`), so that its LDS latency overlaps a whole iteration instead of
+// delaying the next copy.
+__device__ __forceinline__ int list_first(const BlockList& L, const int* meta) {
+  return L.in_lds && L.cnt > 0 ? meta[0] : 0;
+}
+__device__ __forceinline__ void list_next(const AttnArgs& a, int bh, const BlockList& L, const int* meta, int k,
+                                          int& pre, int& J, int& n, int srows) {
+  if (L.in_lds) {
+    const int m = __builtin_amdgcn_readfirstlane(pre);
+    J = m & 0xffff;
+    n = m >> 16;
+    pre = meta[min(k + 1, L.cnt - 1)];
+  } else {
+    list_at(a, bh, L, meta, k, J, n, srows);
+  }
+}
 
 // ---- 32x32x16 products.  A = 32 rows x 16 k (lane l: row l%32,
 // k = 8(l/32)..+7), B likewise with columns, C = 16 registers: lane l register e at row
@@ -256,9 +273,10 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   const float sl2 = a.scale * LOG2E;
 
   // stage st: K tile at 2st, V tile at 2st+1
+  int pre = list_first(bl, sMeta);
   auto issue = [&](int k, int st) {
     int J, n;
-    list_at(a, bh, bl, sMeta, k, J, n, a.nkrows);
+    list_next(a, bh, bl, sMeta, k, pre, J, n, a.nkrows);
     const size_t r0 = krow0_of(a, bh, J);
     load_tile(K + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
     load_tile(V + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
@@ -409,9 +427,10 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
   const float sl2 = a.scale * LOG2E;
 
   // stage st: K tile at 2st, V tile at 2st+1
+  int pre = list_first(bl, sMeta);
   auto issue = [&](int k, int st) {
     int J, n;
-    list_at(a, bh, bl, sMeta, k, J, n, a.nkrows);
+    list_next(a, bh, bl, sMeta, k, pre, J, n, a.nkrows);
     const size_t r0 = row0_of(a, bh, J);
     load_tile(K + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
     load_tile(V + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
@@ -517,9 +536,10 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   // of row `lane` comes through a register (odd waves D, even waves LSE) and is written to
   // sLD[st][w] before the barrier that opens the stage.
   float ld = 0.f;
+  int pre = list_first(bl, sMeta);
   auto issue = [&](int k, int st) {
     int Ib, n;
-    list_at(a, bh, bl, sMeta, k, Ib, n, a.nrows);
+    list_next(a, bh, bl, sMeta, k, pre, Ib, n, a.nrows);
     const size_t r0 = row0_of(a, bh, Ib);
     load_tile(Q + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
     load_tile(Gd + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
