@@ -114,3 +114,24 @@ def test_layer_driven_from_audio():
     if diff:
         pytest.skip("a near-tie query block took the other selection")
     assert_close_out(f64(o), f["o"], "bf16", "layer from audio: O")
+
+
+@pytest.mark.parametrize("n_audio", [1, 7, 65])
+def test_a2v_short_audio(n_audio):
+    """Audio sequences shorter than or just past one 64-key tile (the key tile is copied
+    with its missing rows repeating the last key, then masked), with a ragged query tail
+    (300 queries)."""
+    g = torch.Generator().manual_seed(2000 + n_audio)
+    q, ka, va = (torch.randn(shape, generator=g).to(torch.bfloat16)
+                 for shape in ((1, 2, 300, 128), (1, 2, n_audio, 128), (1, 2, n_audio, 128)))
+    from content_adaptive_block_zone_amd import api
+    scale = 1.0 / math.sqrt(128)
+    o = torch.empty_like(q, device="cuda")
+    norm = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    api.prism_a2v_attn_norm(q.cuda(), ka.cuda(), va.cuda(), scale, norm, o=o)
+    torch.cuda.synchronize()
+    nq, nka, nva = (x.float().numpy().astype(np.float64) for x in (q, ka, va))
+    assert_close_out(f64(norm), O.a2v_norm(nq, nka, nva, scale), "bf16", f"A2V norm, {n_audio} audio keys")
+    s = (nq @ np.swapaxes(nka, -1, -2)) * scale
+    e = np.exp(s - s.max(axis=-1, keepdims=True))
+    assert_close_out(f64(o), (e / e.sum(axis=-1, keepdims=True)) @ nva, "bf16", f"A2V output, {n_audio} audio keys")
