@@ -246,6 +246,7 @@ __device__ __forceinline__ void split8(const f32x16& c, int s, bf16x8& hi, bf16x
     lo[e] = (__bf16)(c[8 * s + e] - (float)h);
   }
 }
+constexpr float kLazy = 8.f;  // log2 units
 __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
   __shared__ int sMeta[kMetaCap];
@@ -309,9 +310,19 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
       mx = fmaxf(mx, v);
     }
     mx = fmaxf(mx, xor32(mx));  // lane l^32 holds the other rows of the column
-    const float mn = fmaxf(m, mx);
-    const float mref = mn == -INFINITY ? 0.f : mn;  // no valid key yet in this half
-    const float alpha = exp2_fast(m - mref);
+    // The reference m moves only when some query's max exceeds it by more than kLazy (or
+    // on its first valid key): the probabilities exp2(s - m) then stay below 2^kLazy, which
+    // fp32 sums and the split bf16 P carry without loss, and O^T is rescaled (which waits
+    // for the previous products) only on those rare steps.
+    if (__builtin_amdgcn_ballot_w64(mx > m + kLazy) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = mn == -INFINITY ? 1.f : exp2_fast(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) o[t] *= alpha;
+      m = mn;
+    }
+    const float mref = m == -INFINITY ? 0.f : m;  // no valid key yet in this half
     float rs = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
@@ -320,10 +331,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
       rs += p;
     }
     rs += xor32(rs);
-    l = l * alpha + rs;
-    m = mn;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) o[t] *= alpha;
+    l += rs;
     bf16x8 h0, r0_, h1, r1_;
     split8(sc, 0, h0, r0_);
     split8(sc, 1, h1, r1_);
