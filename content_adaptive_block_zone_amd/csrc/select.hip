@@ -5,12 +5,12 @@
 //
 //   k_pool    mean of each block's valid rows (float32)           HBM-bound
 //   k_scores  scale * Qbar Kbar^T per head, 64x64 register tiles  fp32 ALU
-//   k_select  per query block: softmax over live key blocks, then the hybrid count found
-//             by bitwise search on the float bits of the probabilities (no sort): the
-//             Top-p threshold is the largest probability v whose "sum of probabilities
-//             >= v" still exceeds p; the Top-k clamp is a count search.  The kept set is
-//             emitted in ascending block order and marked in a bitmap for the reverse
-//             index.
+//   k_select_reg  per query block, the row of scores in registers: softmax over live
+//             key blocks, then the hybrid count found by bitwise search on the float bits
+//             of the probabilities (no sort): the Top-p threshold is the largest
+//             probability v whose "sum of probabilities >= v" still exceeds p; the Top-k
+//             clamp is a count search.  The kept set is emitted in ascending block order
+//             and marked in a bitmap for the reverse index.
 //   k_rev_*   deterministic transpose of the selection via that bitmap: count, scan, fill.
 #include "prism_internal.h"
 
@@ -113,8 +113,10 @@ void launch_pool(const void* qp, const void* kp, const int32_t* bvalid, int BH, 
 }
 
 // scores[bh][I][J] = scale * sum_c qbar[bh][I][c] kbar[bh][J][c]
+// Dead key blocks (no valid token) get the score -inf.
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
-                                                int nb, int d, float scale, float* __restrict__ scores) {
+                                                const int32_t* __restrict__ bvalid, int nb, int d, float scale,
+                                                float* __restrict__ scores) {
   __shared__ float As[16][64];
   __shared__ float Bs[16][64];
   const int bh = blockIdx.z;
@@ -150,25 +152,58 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int J = J0 + tx * 4 + j;
-      if (J < nb) scores[(size_t(bh) * nb + I) * nb + J] = acc[i][j] * scale;
+      if (J < nb) scores[(size_t(bh) * nb + I) * nb + J] = bvalid[size_t(bh) * nb + J] > 0 ? acc[i][j] * scale : -INFINITY;
     }
   }
 }
 
 __device__ __forceinline__ uint32_t key_of(float p) { return __float_as_uint(p); }
 
-__global__ __launch_bounds__(NT) void k_select(const float* __restrict__ scores, const int32_t* __restrict__ bvalid,
-                                               int nb, prism_select_params prm, int k_max,
-                                               int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
-                                               float* __restrict__ sel_margin, uint32_t* __restrict__ bitmap) {
-  extern __shared__ float sP[];  // nb probabilities (-1 for dead key blocks)
-  __shared__ float redf[8];
-  __shared__ int redi[8];
-  const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x;
+// One workgroup per query block, the row held in registers: thread t of a TPB-thread
+// workgroup keeps key blocks t, t + TPB, t + 2 TPB, ... (VPT of them), so that the 31-step
+// searches are register passes.  Sums run over each thread's blocks in that order, then
+// across the workgroup, so results are deterministic.  Ascending emission uses wave
+// ballots per round of TPB blocks.  Used for nb <= TPB * VPT (at most 512 * 32).
+__device__ __forceinline__ int below(uint64_t mask) {  // set bits of mask below this lane
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
+}
+template <int TPB, int VPT>
+__global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ scores, const int32_t* __restrict__ bvalid,
+                                                   int nb, prism_select_params prm, int k_max,
+                                                   int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
+                                                   float* __restrict__ sel_margin, uint32_t* __restrict__ bitmap) {
+  constexpr int NW = TPB / 64;
+  __shared__ float redf[NW];
+  __shared__ int redi[NW];
+  __shared__ float pf[2][NW];  // the search passes alternate between two slots, so one
+  __shared__ int pi[2][NW];    // barrier per pass orders each write after the last reads
+  int par = 0;
+  auto pass_sum = [&](float v) {
+    v = wave_sum(v);
+    if ((threadIdx.x & 63) == 0) pf[par][threadIdx.x >> 6] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) t += pf[par][w2];
+    par ^= 1;
+    return t;
+  };
+  auto pass_sum_i = [&](int v) {
+    v = wave_sum_i(v);
+    if ((threadIdx.x & 63) == 0) pi[par][threadIdx.x >> 6] = v;
+    __syncthreads();
+    int t = 0;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) t += pi[par][w2];
+    par ^= 1;
+    return t;
+  };
+  __shared__ int wcnt[2][NW][VPT];  // per wave and round: equal-key count, taken count
+  const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* bv = bvalid + size_t(bh) * nb;
   int32_t* out = sel_idx + (size_t(bh) * nb + I) * k_max;
   if (bv[I] == 0) {
-    for (int s = tid; s < k_max; s += NT) out[s] = -1;
+    for (int s = tid; s < k_max; s += TPB) out[s] = -1;
     if (tid == 0) {
       sel_cnt[size_t(bh) * nb + I] = 0;
       if (sel_margin) sel_margin[size_t(bh) * nb + I] = 1.f;
@@ -176,36 +211,50 @@ __global__ __launch_bounds__(NT) void k_select(const float* __restrict__ scores,
     return;
   }
   const float* row = scores + (size_t(bh) * nb + I) * nb;
+  float q[VPT];  // logit, then exp, then probability; -1 for dead (or absent) key blocks
   float mx = -INFINITY;
   int nl = 0;
-  for (int J = tid; J < nb; J += NT) {
-    const bool live = bv[J] > 0;
-    const float l = live ? row[J] : -INFINITY;
-    sP[J] = l;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int J = tid + TPB * i;
+    const float l = J < nb ? row[J] : -INFINITY;  // -inf: dead key block (k_scores)
+    q[i] = l;
     mx = fmaxf(mx, l);
-    nl += live;
+    nl += l != -INFINITY;
   }
-  mx = block_max<NT>(mx, redf);
-  const int nlive = block_sum_i<NT>(nl, redi);
+  mx = block_max<TPB>(mx, redf);
+  const int nlive = block_sum_i<TPB>(nl, redi);
   float se = 0.f;
-  for (int J = tid; J < nb; J += NT) {
-    const float l = sP[J];
-    const float e = l == -INFINITY ? -1.f : expf(l - mx);
-    sP[J] = e;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const float e = q[i] == -INFINITY ? -1.f : expf(q[i] - mx);
+    q[i] = e;
     if (e >= 0.f) se += e;
   }
-  se = block_sum<NT>(se, redf);
+  se = block_sum<TPB>(se, redf);
   float tot = 0.f;
-  for (int J = tid; J < nb; J += NT) {
-    const float e = sP[J];
-    if (e >= 0.f) {
-      const float p = e / se;
-      sP[J] = p;
-      tot += p;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i)
+    if (q[i] >= 0.f) {
+      q[i] = q[i] / se;
+      tot += q[i];
     }
-  }
   const float p = prm.top_p;
-  tot = block_sum<NT>(tot, redf);  // also orders the writes above before the passes below
+  tot = block_sum<TPB>(tot, redf);
+  // kk = key + 1 for live blocks, 0 for dead ones: the searches below find key + 1 and
+  // exclude dead blocks by the comparison alone (adding 0.f leaves every sum unchanged)
+  // (kept in registers up to 32 per lane, recomputed from q beyond that)
+  constexpr bool kStore = VPT <= 32;
+  uint32_t kks[kStore ? VPT : 1];
+  if (kStore) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) kks[kStore ? i : 0] = q[i] >= 0.f ? key_of(q[i]) + 1u : 0u;
+  }
+  auto kk_at = [&](int i) -> uint32_t {
+    if (kStore) return kks[kStore ? i : 0];
+    const uint32_t u = key_of(q[i]);
+    return (u + 1u) & ~uint32_t(int32_t(u) >> 31);  // negative (dead) -> 0
+  };
 
   // ---- Top-p: largest key v with sum(P >= v) > p
   int n_p = nlive, need_p = 0;
@@ -215,28 +264,25 @@ __global__ __launch_bounds__(NT) void k_select(const float* __restrict__ scores,
     uint32_t Tk = 0;
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = Tk | (1u << bit);
-      float s = 0.f;
-      for (int J = tid; J < nb; J += NT) {
-        const float q = sP[J];
-        if (q >= 0.f && key_of(q) >= cand) s += q;
-      }
-      s = block_sum<NT>(s, redf);
-      if (s > p) Tk = cand;
+      float sm = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) sm += kk_at(i) >= cand ? q[i] : 0.f;
+      sm = pass_sum(sm);
+      if (sm > p) Tk = cand;
     }
-    vstar = Tk;
+    vstar = Tk - 1u;  // Tk >= 1: all live blocks have kk >= 1 and sum to tot > p
     float sg = 0.f;
     int cg = 0, ce = 0;
-    for (int J = tid; J < nb; J += NT) {
-      const float q = sP[J];
-      if (q < 0.f) continue;
-      const uint32_t kq = key_of(q);
-      if (kq > Tk) { sg += q; ++cg; }
-      else if (kq == Tk) ++ce;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      sg += kk_at(i) > Tk ? q[i] : 0.f;
+      cg += kk_at(i) > Tk;
+      ce += kk_at(i) == Tk;
     }
-    sg = block_sum<NT>(sg, redf);
-    cg = block_sum_i<NT>(cg, redi);
-    ce = block_sum_i<NT>(ce, redi);
-    const float v = __uint_as_float(Tk);
+    sg = block_sum<TPB>(sg, redf);
+    cg = block_sum_i<TPB>(cg, redi);
+    ce = block_sum_i<TPB>(ce, redi);
+    const float v = __uint_as_float(vstar);
     int m = 1;
     while (m < ce && !(sg + float(m) * v > p)) ++m;
     n_p = cg + m;
@@ -245,74 +291,98 @@ __global__ __launch_bounds__(NT) void k_select(const float* __restrict__ scores,
   }
   const int n = min(min(max(n_p, prm.k_min), prm.k_max), nlive);
 
-  // ---- cut threshold for exactly n kept blocks
+  // ---- cut threshold (as kk) for exactly n kept blocks
   uint32_t Tcut;
   int need_eq;
   if (n == n_p && tot > p) {
-    Tcut = vstar;
+    Tcut = vstar + 1u;
     need_eq = need_p;
   } else {
     uint32_t Tk = 0;
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = Tk | (1u << bit);
       int c = 0;
-      for (int J = tid; J < nb; J += NT) {
-        const float q = sP[J];
-        c += (q >= 0.f && key_of(q) >= cand);
-      }
-      c = block_sum_i<NT>(c, redi);
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) c += kk_at(i) >= cand;
+      c = pass_sum_i(c);
       if (c >= n) Tk = cand;
     }
     Tcut = Tk;
     int cg = 0;
-    for (int J = tid; J < nb; J += NT) {
-      const float q = sP[J];
-      cg += (q >= 0.f && key_of(q) > Tk);
-    }
-    cg = block_sum_i<NT>(cg, redi);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) cg += kk_at(i) > Tk;
+    cg = block_sum_i<TPB>(cg, redi);
     need_eq = n - cg;
   }
 
-  // ---- emit ascending: each thread owns a contiguous range of key blocks
-  const int R = (nb + NT - 1) / NT;
-  const int J0 = min(nb, tid * R), J1 = min(nb, J0 + R);
-  int my_eq = 0;
-  for (int J = J0; J < J1; ++J) {
-    const float q = sP[J];
-    my_eq += (q >= 0.f && key_of(q) == Tcut);
+  // ---- emit ascending.  Block order is (round i, wave, lane).  Each wave counts its
+  // equal-key blocks per round (ballots); lane i of every wave then holds the number of
+  // such blocks that precede round i of this wave (a scan over rounds plus the earlier
+  // waves of round i), which the lanes of round i read back with readlane.  The same is
+  // done for the taken blocks.
+  auto offsets = [&](int k2) {  // lane i < VPT: blocks of kind k2 before (round i, this wave)
+    int tot_i = 0, before_i = 0;
+    if (lane < VPT) {
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) {
+        const int c = wcnt[k2][w2][lane];
+        tot_i += c;
+        before_i += w2 < wv ? c : 0;
+      }
+    }
+    int incl = tot_i;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int nn = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += nn;
+    }
+    return incl - tot_i + before_i;
+  };
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const uint64_t eq = __builtin_amdgcn_ballot_w64(kk_at(i) == Tcut);
+    if (lane == 0) wcnt[0][wv][i] = __builtin_popcountll(eq);
   }
-  int tot_eq;
-  int eq_rank = block_excl_scan<NT>(my_eq, redi, &tot_eq);
-  int my_sel = 0;
-  for (int J = J0, r = eq_rank; J < J1; ++J) {
-    const float q = sP[J];
-    if (q < 0.f) continue;
-    const uint32_t kq = key_of(q);
-    if (kq > Tcut) ++my_sel;
-    else if (kq == Tcut) { my_sel += (r < need_eq); ++r; }
+  __syncthreads();
+  const int eqo = offsets(0);
+  // taken: above the cut, or at it and among the first need_eq such blocks in block order
+  auto take_at = [&](int i) {
+    const bool isq = kk_at(i) == Tcut;
+    const int rank = __builtin_amdgcn_readlane(eqo, i) + below(__builtin_amdgcn_ballot_w64(isq));
+    return kk_at(i) > Tcut || (isq && rank < need_eq);
+  };
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const uint64_t tk = __builtin_amdgcn_ballot_w64(take_at(i));
+    if (lane == 0) wcnt[1][wv][i] = __builtin_popcountll(tk);
   }
-  int tot_sel;
-  int pos = block_excl_scan<NT>(my_sel, redi, &tot_sel);
+  __syncthreads();
+  const int tko = offsets(1);
+  int tot_sel = 0;
+  if (lane < VPT) {
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) tot_sel += wcnt[1][w2][lane];
+  }
+  tot_sel = wave_sum_i(tot_sel);
   float pmin_sel = INFINITY, pmax_uns = -INFINITY;
   uint32_t* bm = bitmap + size_t(bh) * nb * words32(nb);
-  for (int J = J0, r = eq_rank; J < J1; ++J) {
-    const float q = sP[J];
-    if (q < 0.f) continue;
-    const uint32_t kq = key_of(q);
-    bool take = kq > Tcut;
-    if (kq == Tcut) { take = r < need_eq; ++r; }
-    if (take) {
-      out[pos++] = J;
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const bool tk = take_at(i);
+    const int pos = __builtin_amdgcn_readlane(tko, i) + below(__builtin_amdgcn_ballot_w64(tk));
+    const int J = tid + TPB * i;
+    if (tk) {
+      out[pos] = J;
       atomicOr(bm + size_t(J) * words32(nb) + (I >> 5), 1u << (I & 31));
-      pmin_sel = fminf(pmin_sel, q);
-    } else {
-      pmax_uns = fmaxf(pmax_uns, q);
+      pmin_sel = fminf(pmin_sel, q[i]);
+    } else if (kk_at(i) > 0u) {
+      pmax_uns = fmaxf(pmax_uns, q[i]);
     }
   }
-  for (int s = tot_sel + tid; s < k_max; s += NT) out[s] = -1;
+  for (int s = tot_sel + tid; s < k_max; s += TPB) out[s] = -1;
   if (sel_margin) {
-    pmin_sel = -block_max<NT>(-pmin_sel, redf);
-    pmax_uns = block_max<NT>(pmax_uns, redf);
+    pmin_sel = -block_max<TPB>(-pmin_sel, redf);
+    pmax_uns = block_max<TPB>(pmax_uns, redf);
   }
   if (tid == 0) {
     sel_cnt[size_t(bh) * nb + I] = tot_sel;
@@ -410,9 +480,24 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
   else
     launch_pool<float>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
   const int tiles = (nb + 63) / 64;
-  hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, w.qbar, w.kbar, nb, d, scale, w.scores);
-  hipLaunchKernelGGL(k_select, dim3(nb, BH), dim3(NT), size_t(nb) * 4, s, w.scores, bvalid, nb, p, p.k_max,
-                     sel_idx, sel_cnt, sel_margin, w.bitmap);
+  hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, w.qbar, w.kbar, bvalid, nb, d, scale,
+                     w.scores);
+  // Workgroup shapes as measured fastest: 256 lanes up to 32 blocks each, then 512 lanes of
+  // 32 (at 64 per lane the register file allows one wave per SIMD).  nb <= 512 * 32 is
+  // checked by the caller.
+  const dim3 sg(nb, BH);
+  if (nb <= 256 * 8)
+    hipLaunchKernelGGL((k_select_reg<256, 8>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
+                       sel_cnt, sel_margin, w.bitmap);
+  else if (nb <= 256 * 16)
+    hipLaunchKernelGGL((k_select_reg<256, 16>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
+                       sel_cnt, sel_margin, w.bitmap);
+  else if (nb <= 256 * 32)
+    hipLaunchKernelGGL((k_select_reg<256, 32>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
+                       sel_cnt, sel_margin, w.bitmap);
+  else
+    hipLaunchKernelGGL((k_select_reg<512, 32>), sg, dim3(512), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
+                       sel_cnt, sel_margin, w.bitmap);
   const int rows = BH * nb;
   hipLaunchKernelGGL(k_rev_count, dim3((rows + 255) / 256), dim3(256), 0, s, w.bitmap, nb, rows, w.rcnt);
   hipLaunchKernelGGL(k_rev_scan, dim3(BH), dim3(1024), 0, s, w.rcnt, nb, rev_ptr);

@@ -113,6 +113,8 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_ARG),                                                             # workspace too small
         ("prism_select_blocks", (P, P, F32, P, 1, 2, 20000, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 40,
                                  None), E.PRISM_ERR_SHAPE),
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 16385, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 40,
+                                 None), E.PRISM_ERR_SHAPE),                            # one past the limit
         ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 8, 1, 2, 16, 16, 96, 0.125, P, P, None, 0, None),
          E.PRISM_ERR_DTYPE),
         ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 8, 1, 2, 16, 128, 64, 0.125, P, P, None, 0, None),
