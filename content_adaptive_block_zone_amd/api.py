@@ -295,6 +295,9 @@ def prism_sparse_attn_fwd(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, s
     nb = npad // vol
     km = sel_idx.shape[-1]
     dt = _same_dtype(qp, kp, vp, op)
+    if workspace is None:
+        need = prism_fwd_workspace_size(B, Hh, nb, vol, d, qp.dtype)
+        workspace = torch.empty(need, dtype=torch.uint8, device=qp.device) if need else None
     check(load().prism_sparse_attn_fwd(
         _ptr(qp, name="qp"), _ptr(kp, shape=qp.shape, name="kp"), _ptr(vp, shape=qp.shape, name="vp"), dt,
         _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"),

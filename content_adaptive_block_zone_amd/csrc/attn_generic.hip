@@ -77,10 +77,11 @@ __global__ __launch_bounds__(NT) void k_fwd_generic(AttnArgs a) {
   }
   const int tr = tile_rows(a);
   if (r < nI) {
-    const float inv = 1.f / l;
+    // nothing to attend (l = 0): O = 0 and LSE = 0, as at padding rows
+    const float inv = l > 0.f ? 1.f / l : 0.f;
 #pragma unroll
     for (int c = 0; c < CP; ++c) O[(r0 + r) * D + part * CP + c] = from_f32<T>(acc[c] * inv);
-    if (part == 0) a.lse_out[r0 + r] = m + logf(l);
+    if (part == 0) a.lse_out[r0 + r] = l > 0.f ? m + logf(l) : 0.f;
   } else if (!a.dense && r < tr) {
 #pragma unroll
     for (int c = 0; c < CP; ++c) O[(r0 + r) * D + part * CP + c] = from_f32<T>(0.f);
@@ -281,22 +282,34 @@ hipError_t launch_attn_bwd_generic(const AttnArgs& a, prism_dtype dt, hipEvent_t
 }
 
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_bwd_mfma(const AttnArgs& a, hipEvent_t* marks, hipStream_t s);
+size_t attn_mfma_sched_bytes(const AttnArgs& a);
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
+hipError_t launch_attn_bwd_mfma(const AttnArgs& a, int32_t* sched, hipEvent_t* marks, hipStream_t s);
 
-size_t attn_fwd_ws_bytes(const AttnArgs&, prism_dtype) { return 0; }
+// Forward workspace: the matrix-core path's workgroup schedule (sparse mode), else none.
+size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt) {
+  return attn_mfma_supported(a, dt) ? attn_mfma_sched_bytes(a) : 0;
+}
 
-size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype) { return align256(size_t(a.BH) * a.nrows * 4); }
+// Backward workspace: D = rowsum(dO * O) per row, then (matrix-core path, sparse mode)
+// the query-major and key-major workgroup schedules.
+size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt) {
+  const size_t dbuf = align256(size_t(a.BH) * a.nrows * 4);
+  return dbuf + (attn_mfma_supported(a, dt) ? 2 * attn_mfma_sched_bytes(a) : 0);
+}
 
-hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void*, hipStream_t s) {
-  if (attn_mfma_supported(a, dt)) return launch_attn_fwd_mfma(a, s);
+hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s) {
+  if (attn_mfma_supported(a, dt)) return launch_attn_fwd_mfma(a, static_cast<int32_t*>(ws), s);
   return launch_attn_fwd_generic(a, dt, s);
 }
 
 hipError_t launch_attn_bwd(const AttnArgs& a_in, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s) {
   AttnArgs a = a_in;
   a.Dbuf = static_cast<float*>(ws);
-  if (attn_mfma_supported(a, dt)) return launch_attn_bwd_mfma(a, marks, s);
+  if (attn_mfma_supported(a, dt)) {
+    int32_t* sched = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + align256(size_t(a.BH) * a.nrows * 4));
+    return launch_attn_bwd_mfma(a, sched, marks, s);
+  }
   return launch_attn_bwd_generic(a, dt, marks, s);
 }
 

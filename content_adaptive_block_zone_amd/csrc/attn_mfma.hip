@@ -30,8 +30,9 @@
 namespace prism {
 
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_bwd_mfma(const AttnArgs& a, hipEvent_t* marks, hipStream_t s);
+size_t attn_mfma_sched_bytes(const AttnArgs& a);
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
+hipError_t launch_attn_bwd_mfma(const AttnArgs& a, int32_t* sched, hipEvent_t* marks, hipStream_t s);
 
 namespace {
 
@@ -73,23 +74,84 @@ __device__ __forceinline__ size_t krow0_of(const AttnArgs& a, int bh, int J) {
 }
 
 // Owner block of a workgroup.  Heads are taken in order, so that a head's K/V (or Q/dO)
-// pass through the 256 MB last-level cache one at a time.  Workgroups are dealt to the
-// eight XCDs round-robin by id; the ids are remapped so that each XCD receives runs of G
-// consecutive blocks (runs dealt round-robin, so the work stays balanced), which puts
-// blocks of the same zone, whose key lists overlap a little more than chance, behind the
-// same L2.  G = 16 (one zone of 64-token blocks) for the query-major kernels and 64 for
-// the key-major one measured 1-2 % faster than no remap; one contiguous run per XCD
-// measured slower.  Ids past the last whole group of 8G keep their place.
+// pass through the 256 MB last-level cache one at a time.
+// Sparse mode: the launcher's schedule (k_schedule: longest list first within each head).
+// Dense mode (every list the same length): workgroups are dealt to the eight XCDs
+// round-robin by id, and the ids are remapped so that each XCD receives runs of G
+// consecutive blocks (runs dealt round-robin, so the work stays balanced); G = 16 for the
+// query-major kernels and 64 for the key-major one.  Ids past the last whole group of 8G
+// keep their place.
 template <int G>
-__device__ __forceinline__ void owner_of(const AttnArgs& a, int& I, int& bh) {
+__device__ __forceinline__ void owner_of(const AttnArgs& a, const int32_t* order, int& I, int& bh) {
   int id = blockIdx.x;
-  const int full = (a.nb * a.BH / (8 * G)) * (8 * G);
-  if (id < full) {
-    const int x = id % 8, l = id / 8;
-    id = (l / G) * (8 * G) + x * G + (l % G);
+  if (order) {
+    id = __builtin_amdgcn_readfirstlane(order[id]);
+  } else {
+    const int full = (a.nb * a.BH / (8 * G)) * (8 * G);
+    if (id < full) {
+      const int x = id % 8, l = id / 8;
+      id = (l / G) * (8 * G) + x * G + (l % G);
+    }
   }
   I = id % a.nb;
   bh = id / a.nb;
+}
+
+// ------------------------------------------------------------------ workgroup schedule
+// The order in which the workgroups of one sparse launch take their owner blocks: within
+// each head (heads stay in order), longest list first, in bins of `width` lengths.  Two
+// effects, both measured on the 2K-like workload (about 7 % over the three kernels):
+//   * the longest lists start first, so a launch does not end on a few long workgroups;
+//   * workgroups resident together have lists of about the same length, so, walking their
+//     ascending lists, they move through the streamed blocks at about the same pace and
+//     ask for the same tiles close together in time, which then hit in L2.
+// The order changes only which workgroup runs when: every block's result is computed by
+// one workgroup alone, so the outputs do not depend on it.  Within a bin the order is
+// that of LDS atomics and may differ from call to call.
+// Grid: BH workgroups for the query-major order (from the list counts), then, when
+// order_k is given, BH more for the key-major order (from the reverse-list lengths).
+constexpr int kSchedBins = 2048;
+constexpr int kSchedThreads = 1024;
+__global__ __launch_bounds__(kSchedThreads) void k_schedule(AttnArgs a, int32_t* order_q, int32_t* order_k) {
+  __shared__ int bins[kSchedBins];
+  __shared__ int wsum[kSchedThreads / 64];
+  const int key_major = blockIdx.x >= a.BH;
+  const int bh = blockIdx.x - (key_major ? a.BH : 0);
+  int32_t* out = (key_major ? order_k : order_q) + size_t(bh) * a.nb;
+  const int bound = key_major ? a.nb : a.k_max;  // longest possible list
+  const int width = bound / kSchedBins + 1;
+  auto bin_of = [&](int I) {
+    int len;
+    if (key_major) {
+      const int32_t* rp = a.rev_ptr + size_t(bh) * (a.nb + 1) + I;
+      len = rp[1] - rp[0];
+    } else {
+      len = a.bvalid[size_t(bh) * a.nb + I] > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0;
+    }
+    return kSchedBins - 1 - min(max(len, 0), bound) / width;  // longest first
+  };
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  for (int i = t; i < kSchedBins; i += kSchedThreads) bins[i] = 0;
+  __syncthreads();
+  for (int I = t; I < a.nb; I += kSchedThreads) atomicAdd(&bins[bin_of(I)], 1);
+  __syncthreads();
+  // exclusive prefix sum of the bins, two per thread
+  static_assert(kSchedBins == 2 * kSchedThreads, "two bins per thread");
+  const int h0 = bins[2 * t], h1 = bins[2 * t + 1];
+  int x = h0 + h1;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  int start = x - h0 - h1;
+  for (int i = 0; i < w; ++i) start += wsum[i];
+  bins[2 * t] = start;  // each thread rewrites only the two bins it read
+  bins[2 * t + 1] = start + h0;
+  __syncthreads();
+  for (int I = t; I < a.nb; I += kSchedThreads) out[atomicAdd(&bins[bin_of(I)], 1)] = bh * a.nb + I;
 }
 
 // The streamed block list of a workgroup, with each block's valid-row count, is copied to
@@ -251,7 +313,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
   __shared__ int sMeta[kMetaCap];
   int I, bh;
-  owner_of<16>(a, I, bh);
+  owner_of<16>(a, a.order_q, I, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int qh = w & 1, kh = w >> 1;
   const int nI = nrows_of(a, bh, I);
@@ -369,16 +431,17 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
       for (int e = 0; e < 16; ++e) o[t][e] = o[t][e] * a0 + red[(t * 16 + e) * 64 + lane] * a1;
   }
   // O, LSE and the row norm are each optional (the norm serves the audio-to-video
-  // cross-attention's per-token norm)
+  // cross-attention's per-token norm).  A row with nothing to attend (an empty list, or
+  // lists of blocks without valid rows: l = 0) gets O = 0 and LSE = 0, as padding rows do.
   if (qok) {
-    const float inv = 1.f / l;
+    const float inv = l > 0.f ? 1.f / l : 0.f;
     if (O) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int j = 0; j < 4; ++j) store4_32(O + (q0 + qrow) * D + 32 * t + 8 * j + 4 * g, o[t], j, inv);
     }
-    if (a.lse_out && g == 0) a.lse_out[q0 + qrow] = (m + log2f(l)) * 0.6931471805599453f;
+    if (a.lse_out && g == 0) a.lse_out[q0 + qrow] = l > 0.f ? (m + log2f(l)) * 0.6931471805599453f : 0.f;
     if (a.norm_out) {
       float ss = 0.f;
 #pragma unroll
@@ -407,7 +470,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
   __shared__ int sMeta[kMetaCap];
   int I, bh;
-  owner_of<16>(a, I, bh);
+  owner_of<16>(a, a.order_q, I, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int qh = w & 1, kh = w >> 1;
   const int nI = nrows_of(a, bh, I);
@@ -508,7 +571,7 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   __shared__ int sMeta[kMetaCapKV];
   bf16x8* xbuf = reinterpret_cast<bf16x8*>(smem + 4 * TB);  // 2 KB per wave
   int J, bh;
-  owner_of<64>(a, J, bh);
+  owner_of<64>(a, a.order_k, J, bh);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
   const int kh = w & 1, x = w >> 1;
   const int nJ = nrows_of(a, bh, J);
@@ -638,13 +701,30 @@ int attn_mfma_supported(const AttnArgs& a, prism_dtype dt) {
   return dt == PRISM_BF16 && a.d == D && (a.dense || a.vol == TR);
 }
 
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s) {
+// Bytes of one workgroup schedule (sparse mode; dense mode needs none).
+size_t attn_mfma_sched_bytes(const AttnArgs& a) { return a.dense ? 0 : align256(size_t(a.BH) * a.nb * 4); }
+
+// sched: attn_mfma_sched_bytes() bytes of device scratch (sparse mode)
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a_in, int32_t* sched, hipStream_t s) {
+  AttnArgs a = a_in;
+  if (!a.dense) {
+    a.order_q = sched;
+    hipLaunchKernelGGL(k_schedule, dim3(a.BH), dim3(kSchedThreads), 0, s, a, sched, nullptr);
+  }
   hipLaunchKernelGGL(k_fwd, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_mfma(const AttnArgs& a, hipEvent_t* marks, hipStream_t s) {
+// sched: 2 * attn_mfma_sched_bytes() bytes of device scratch (sparse mode)
+hipError_t launch_attn_bwd_mfma(const AttnArgs& a_in, int32_t* sched, hipEvent_t* marks, hipStream_t s) {
+  AttnArgs a = a_in;
   if (marks) (void)hipEventRecord(marks[0], s);
+  if (!a.dense) {
+    a.order_q = sched;
+    a.order_k = sched + attn_mfma_sched_bytes(a) / 4;
+    hipLaunchKernelGGL(k_schedule, dim3(2 * a.BH), dim3(kSchedThreads), 0, s, a, const_cast<int32_t*>(a.order_q),
+                       const_cast<int32_t*>(a.order_k));
+  }
   const size_t rows = size_t(a.BH) * a.nrows;
   hipLaunchKernelGGL(k_bwd_pre_bf16, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, s, a, rows);
   if (marks) (void)hipEventRecord(marks[1], s);

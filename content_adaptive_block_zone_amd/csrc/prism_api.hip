@@ -403,7 +403,7 @@ prism_status prism_a2v_attn_norm(const void* q, const void* ka, const void* va, 
   a.out = o;
   a.lse_out = nullptr;
   a.norm_out = a2v_norm;
-  return launched(launch_attn_fwd_mfma(a, stream), who);
+  return launched(launch_attn_fwd_mfma(a, nullptr, stream), who);  // dense: no schedule
 }
 
 size_t prism_tiles_workspace_size(int B, int Hh, int nb, int vol) {

@@ -188,6 +188,11 @@ struct AttnArgs {
   // and nb except for a cross-attention, whose keys are a different sequence).
   int nkrows, nkb;
   float* norm_out;  // forward only, nullable: L2 norm of each output row, float [BH][nrows]
+  // Matrix-core kernels, sparse mode: the order in which workgroups take their owner
+  // blocks, int32 [BH * nb] of bh * nb + block (query-major kernels: order_q, key-major:
+  // order_k); null = the kernels' own fixed order.  Set by the launchers.
+  const int32_t* order_q;
+  const int32_t* order_k;
 };
 
 // Launchers (each returns the first HIP error of its launches).
@@ -226,7 +231,8 @@ hipError_t launch_blocks_to_tiles(const int32_t* bvalid, const int32_t* sel_idx,
                                   const int32_t* rev_ptr, const int32_t* rev_idx, int BH, int nb, int vol, int k_max,
                                   int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt, int32_t* tile_rev_ptr,
                                   int32_t* tile_rev_idx, void* ws, hipStream_t s);
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, hipStream_t s);
+// sched: device scratch for the workgroup schedule of a sparse launch (null in dense mode)
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s);

@@ -256,7 +256,9 @@ prism_status prism_blocks_to_tiles_mixed(const int32_t* block_valid, const int32
  * op   out [B][Hh][nb*vol][d] (zeros at padding rows);  lse out float [B][Hh][nb*vol]
  * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}; bf16 with vol = 64 and
  * d = 128 runs on the matrix cores.  workspace: prism_fwd_workspace_size() bytes of device
- * scratch (currently 0 for every case; workspace may then be NULL). */
+ * scratch: on the matrix-core path B*Hh*nb int32 (rounded up to 256 bytes), the order in
+ * which workgroups take their query blocks (longest list first), which changes no output;
+ * 0 bytes otherwise, and workspace may then be NULL.  Too small: PRISM_ERR_ARG. */
 size_t prism_fwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
                                    const int32_t* block_valid, const int32_t* sel_idx,
@@ -270,8 +272,11 @@ prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* v
  * dqp, dkp, dvp out [B][Hh][nb*vol][d] (zeros at padding rows).  dK/dV walk the reverse
  * index; no atomics, results are deterministic.
  * marks    optional array of 4 caller-created hipEvents recorded on `stream` before the
- *          D kernel, after it, after the dK/dV kernel and after the dQ kernel.
- * workspace    device scratch of prism_bwd_workspace_size() bytes (D = rowsum(dO*O) per row). */
+ *          D kernel (and the schedule kernel), after it, after the dK/dV kernel and after
+ *          the dQ kernel.
+ * workspace    device scratch of prism_bwd_workspace_size() bytes: D = rowsum(dO*O) per row,
+ *          and on the matrix-core path the orders in which the dQ and dK/dV workgroups take
+ *          their blocks (longest list first; they change no output). */
 size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* vp, const void* op,
                                    const void* dop, const float* lse, prism_dtype dtype,

@@ -675,7 +675,9 @@ def _rows(x, b, h, B_, vol, n):
 
 def sparse_attn_fwd(qp, kp, vp, bvalid, sel: Dict, scale: float, vol: int,
                     blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
-    """O' [B,Hh,Npad,C] and LSE [B,Hh,Npad] in float64 (rows of unlisted blocks stay 0)."""
+    """O' [B,Hh,Npad,C] and LSE [B,Hh,Npad] in float64 (rows of unlisted blocks stay 0).
+    Reading: a valid query row with nothing to attend (an empty list, or listed blocks
+    without valid rows) has no softmax; it outputs 0 with LSE 0, as padding rows do."""
     qp, kp, vp = (np.asarray(a, dtype=np.float64) for a in (qp, kp, vp))
     B, Hh, Np, C = qp.shape
     O = np.zeros((B, Hh, Np, vp.shape[-1]))
@@ -683,8 +685,8 @@ def sparse_attn_fwd(qp, kp, vp, bvalid, sel: Dict, scale: float, vol: int,
     it = blocks if blocks is not None else [(b, h, I) for b in range(B) for h in range(Hh) for I in range(Np // vol)]
     for (b, h, I) in it:
         n = int(bvalid[b, h, I])
-        js = sel[(b, h, I)]
-        if n == 0 or js.size == 0:
+        js = [J for J in sel[(b, h, I)] if bvalid[b, h, J] > 0]
+        if n == 0 or not js:
             continue
         q = _rows(qp, b, h, I, vol, n)
         K = np.concatenate([_rows(kp, b, h, J, vol, int(bvalid[b, h, J])) for J in js])

@@ -576,6 +576,31 @@ def test_single_selected_block_is_attention_inside_that_block():
     assert (op[0, 0, 48 + n:64] == 0).all()
 
 
+def test_rows_with_nothing_to_attend_are_zero():
+    """Reading of the attention over an empty key set: a block whose list is empty, or holds
+    only blocks without valid rows, outputs 0 with LSE 0 and gets no gradient; the other
+    blocks are unaffected (each equals softmax attention over its own keys)."""
+    rng = np.random.default_rng(3)
+    vol, C = 8, 4
+    bv = np.array([[[8, 5, 0, 8]]], dtype=np.int32)
+    qp, kp, vp, dop = (rng.standard_normal((1, 1, 4 * vol, C)) for _ in range(4))
+    for x in (qp, kp, vp, dop):
+        for I in range(4):
+            x[0, 0, I * vol + bv[0, 0, I]:(I + 1) * vol] = 0.0
+    sel = {(0, 0, 0): np.array([], np.int32), (0, 0, 1): np.array([2], np.int32),
+           (0, 0, 2): np.array([], np.int32), (0, 0, 3): np.array([0, 2, 3], np.int32)}
+    op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, 0.5, vol)
+    assert (op[0, 0, :2 * vol] == 0).all() and (lse[0, 0, :2 * vol] == 0).all()
+    Q = torch.from_numpy(qp[0, 0, 24:32])
+    K = torch.from_numpy(np.concatenate([kp[0, 0, 0:8], kp[0, 0, 24:32]]))
+    V = torch.from_numpy(np.concatenate([vp[0, 0, 0:8], vp[0, 0, 24:32]]))
+    assert np.allclose(op[0, 0, 24:32], (torch.softmax(0.5 * Q @ K.T, dim=1) @ V).numpy(), atol=1e-12)
+    assert np.allclose(lse[0, 0, 24:32], torch.logsumexp(0.5 * Q @ K.T, dim=1).numpy(), atol=1e-12)
+    dq, dk, dv = O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, 0.5, vol)
+    assert (dq[0, 0, :2 * vol] == 0).all()
+    assert (dk[0, 0, 8:24] == 0).all() and (dv[0, 0, 8:24] == 0).all()
+
+
 def test_backward_matches_central_finite_differences():
     q, k, v, tok, N = _tiny_problem(2, C=4)
     bv = O.block_valid(tok, 16)
