@@ -64,20 +64,44 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
 // ----------------------------------------------------------------------------------
 // Reductions (64-lane wavefronts).
 // ----------------------------------------------------------------------------------
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+// Reductions over the 64 lanes of a wavefront, every lane receiving the result, without
+// the LDS crossbar: DPP moves within 16-lane rows (swap neighbours, swap pairs, mirror
+// within 8 lanes, mirror within 16 lanes: each step pairs lanes that hold the partial
+// results of disjoint groups), then v_permlane16_swap and v_permlane32_swap exchange
+// rows and halves.  Every lane combines the same operands (a + b and b + a are equal),
+// so all lanes get bitwise equal results.  All 64 lanes must be active.
+template <int CTRL>
+__device__ __forceinline__ int dpp_move(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t lane_xor16(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (threadIdx.x & 16) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor32(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (threadIdx.x & 32) ? r[0] : r[1];
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce(T v, Op op) {
+  auto bits = [](T x) { return __builtin_bit_cast(int, x); };
+  auto from = [](int x) { return __builtin_bit_cast(T, x); };
+  v = op(v, from(dpp_move<0xB1>(bits(v))));   // quad_perm [1,0,3,2]
+  v = op(v, from(dpp_move<0x4E>(bits(v))));   // quad_perm [2,3,0,1]
+  v = op(v, from(dpp_move<0x141>(bits(v))));  // row_half_mirror
+  v = op(v, from(dpp_move<0x140>(bits(v))));  // row_mirror
+  v = op(v, from(int(lane_xor16(uint32_t(bits(v))))));
+  v = op(v, from(int(lane_xor32(uint32_t(bits(v))))));
   return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](int x, int y) { return x + y; });
 }
 
 // Sum over a workgroup of NT threads; `red` holds at least NT/64 floats.  Every thread
