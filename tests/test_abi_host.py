@@ -73,6 +73,23 @@ def test_host_helpers_reject_bad_geometry(lib):
     assert api.prism_bwd_workspace_size(1, 4, 5760, 64, 128, torch.bfloat16) >= 4 * 5760 * 64 * 4
 
 
+def test_attention_workspace_holds_the_schedules(lib):
+    """The matrix-core path (bf16, 64-row blocks, d = 128) keeps its workgroup schedules in
+    the workspace: one int32 per (head, block) for the forward; D (one float per row) and
+    two schedules for the backward, each rounded up to 256 bytes.  Other paths need none."""
+    import torch
+    from content_adaptive_block_zone_amd import api
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    for B, Hh, nb in ((1, 4, 5760), (2, 3, 77)):
+        sched = a256(B * Hh * nb * 4)
+        assert api.prism_fwd_workspace_size(B, Hh, nb, 64, 128, torch.bfloat16) == sched
+        assert api.prism_bwd_workspace_size(B, Hh, nb, 64, 128, torch.bfloat16) == a256(B * Hh * nb * 64 * 4) + 2 * sched
+        assert api.prism_fwd_workspace_size(B, Hh, nb, 64, 64, torch.bfloat16) == 0           # generic path
+        assert api.prism_fwd_workspace_size(B, Hh, nb, 16, 128, torch.bfloat16) == 0
+        assert api.prism_bwd_workspace_size(B, Hh, nb, 64, 128, torch.float32) == a256(B * Hh * nb * 64 * 4)
+    assert api.prism_dense_fwd_workspace_size(1, 4, 1000, 128, torch.bfloat16) == 0         # dense: no schedule
+
+
 def _status(fn, *args):
     return fn(*args)
 
@@ -121,6 +138,12 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_SHAPE),
         ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 0, 1, 2, 16, 16, 64, 0.125, P, P, None, 0, None),
          E.PRISM_ERR_ARG),
+        ("prism_sparse_attn_fwd", (P, P, P, BF16, P, P, P, 8, 1, 2, 16, 64, 128, 0.125, P, P, None, 0, None),
+         E.PRISM_ERR_ARG),                                                             # schedule needs a workspace
+        ("prism_sparse_attn_fwd", (P, P, P, BF16, P, P, P, 8, 1, 2, 16, 64, 128, 0.125, P, P, P, 127, None),
+         E.PRISM_ERR_ARG),                                                             # workspace too small
+        ("prism_sparse_attn_bwd", (P, P, P, P, P, P, BF16, P, P, P, 8, P, P, 1, 2, 16, 64, 128, 0.125, P, P, P,
+                                   P, 2 * 16 * 64 * 4, None, None), E.PRISM_ERR_ARG),  # D only, no room for schedules
         ("prism_sparse_attn_bwd", (P, P, P, P, P, P, F32, P, P, P, 8, P, P, 1, 2, 16, 16, 64, 0.125, P, P, P,
                                    P, 8, None, None), E.PRISM_ERR_ARG),
         ("prism_dense_attn_fwd", (P, P, P, F32, 1, 2, 0, 64, 0.125, P, P, None, 0, None), E.PRISM_ERR_ARG),
