@@ -24,6 +24,9 @@
 // transposing LDS read (ds_read_b64_tr_b16), two 8-byte reads per operand.
 // All accumulation is fp32; the forward's P V product takes P as a bf16 head plus a bf16
 // remainder.
+// In sparse mode the workgroups take their owner blocks longest list first within each
+// head (k_schedule), which balances the launch and lets workgroups resident together
+// share tiles in L2.
 
 #include "prism_internal.h"
 
@@ -720,10 +723,11 @@ hipError_t launch_attn_bwd_mfma(const AttnArgs& a_in, int32_t* sched, hipEvent_t
   AttnArgs a = a_in;
   if (marks) (void)hipEventRecord(marks[0], s);
   if (!a.dense) {
-    a.order_q = sched;
-    a.order_k = sched + attn_mfma_sched_bytes(a) / 4;
-    hipLaunchKernelGGL(k_schedule, dim3(2 * a.BH), dim3(kSchedThreads), 0, s, a, const_cast<int32_t*>(a.order_q),
-                       const_cast<int32_t*>(a.order_k));
+    int32_t* order_q = sched;
+    int32_t* order_k = sched + attn_mfma_sched_bytes(a) / 4;
+    a.order_q = order_q;
+    a.order_k = order_k;
+    hipLaunchKernelGGL(k_schedule, dim3(2 * a.BH), dim3(kSchedThreads), 0, s, a, order_q, order_k);
   }
   const size_t rows = size_t(a.BH) * a.nrows;
   hipLaunchKernelGGL(k_bwd_pre_bf16, dim3(unsigned((rows + 15) / 16)), dim3(256), 0, s, a, rows);
