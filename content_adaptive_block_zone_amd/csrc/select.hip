@@ -4,7 +4,7 @@
 // attention weight exceeds the threshold).
 //
 //   k_pool    mean of each block's valid rows (float32)           HBM-bound
-//   k_scores  scale * Qbar Kbar^T per head, 64x64 register tiles  fp32 ALU
+//   k_scores  scale * Qbar Kbar^T per head, 128x128 tiles, 8x8 per thread   fp32 ALU
 //   k_select_reg  per query block, the row of scores in registers: softmax over live
 //             key blocks, then the hybrid count found by bitwise search on the float bits
 //             of the probabilities (no sort): the Top-p threshold is the largest
@@ -114,45 +114,71 @@ void launch_pool(const void* qp, const void* kp, const int32_t* bvalid, int BH, 
 
 // scores[bh][I][J] = scale * sum_c qbar[bh][I][c] kbar[bh][J][c]
 // Dead key blocks (no valid token) get the score -inf.
+// 128x128 tile per workgroup, 8x8 per thread (rows ty + 16i, columns tx + 16j), c in
+// chunks of 16 staged in LDS: four FMAs per LDS value read.  Each score sums its d
+// products in order of c, one fused multiply-add at a time.
+constexpr int kScT = 128;
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                 const int32_t* __restrict__ bvalid, int nb, int d, float scale,
                                                 float* __restrict__ scores) {
-  __shared__ float As[16][64];
-  __shared__ float Bs[16][64];
+  __shared__ float As[16][kScT];
+  __shared__ float Bs[16][kScT];
   const int bh = blockIdx.z;
-  const int I0 = blockIdx.y * 64, J0 = blockIdx.x * 64;
+  const int I0 = blockIdx.y * kScT, J0 = blockIdx.x * kScT;
   const float* Q = qbar + size_t(bh) * nb * d;
   const float* K = kbar + size_t(bh) * nb * d;
   const int t = threadIdx.x, ty = t / 16, tx = t % 16;
-  const int lr = t / 4, lc = (t % 4) * 4;
-  float acc[4][4] = {};
+  const int lr = t / 4, lc = (t % 4) * 4;  // staging: rows lr and lr + 64, columns lc..lc+3
+  float acc[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
   for (int k0 = 0; k0 < d; k0 += 16) {
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-    if (I0 + lr < nb) a = *reinterpret_cast<const float4*>(Q + size_t(I0 + lr) * d + k0 + lc);
-    if (J0 + lr < nb) b = *reinterpret_cast<const float4*>(K + size_t(J0 + lr) * d + k0 + lc);
+    float4 a[2], b[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 64 * h;
+      a[h] = I0 + r < nb ? *reinterpret_cast<const float4*>(Q + size_t(I0 + r) * d + k0 + lc) : make_float4(0.f, 0.f, 0.f, 0.f);
+      b[h] = J0 + r < nb ? *reinterpret_cast<const float4*>(K + size_t(J0 + r) * d + k0 + lc) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     __syncthreads();
-    As[lc + 0][lr] = a.x; As[lc + 1][lr] = a.y; As[lc + 2][lr] = a.z; As[lc + 3][lr] = a.w;
-    Bs[lc + 0][lr] = b.x; Bs[lc + 1][lr] = b.y; Bs[lc + 2][lr] = b.z; Bs[lc + 3][lr] = b.w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = lr + 64 * h;
+      As[lc + 0][r] = a[h].x; As[lc + 1][r] = a[h].y; As[lc + 2][r] = a[h].z; As[lc + 3][r] = a[h].w;
+      Bs[lc + 0][r] = b[h].x; Bs[lc + 1][r] = b[h].y; Bs[lc + 2][r] = b[h].z; Bs[lc + 3][r] = b[h].w;
+    }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < 16; ++kk) {
-      const float4 av = *reinterpret_cast<const float4*>(&As[kk][ty * 4]);
-      const float4 bv = *reinterpret_cast<const float4*>(&Bs[kk][tx * 4]);
-      const float ar[4] = {av.x, av.y, av.z, av.w}, br[4] = {bv.x, bv.y, bv.z, bv.w};
+      float ar[8], br[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 8; ++i) ar[i] = As[kk][ty + 16 * i];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+      for (int j = 0; j < 8; ++j) br[j] = Bs[kk][tx + 16 * j];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
     }
   }
+  const int32_t* bv = bvalid + size_t(bh) * nb;
+  bool live[8];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int I = I0 + ty * 4 + i;
+  for (int j = 0; j < 8; ++j) {
+    const int J = J0 + tx + 16 * j;
+    live[j] = J < nb && bv[J] > 0;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int I = I0 + ty + 16 * i;
     if (I >= nb) continue;
+    float* row = scores + (size_t(bh) * nb + I) * nb;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int J = J0 + tx * 4 + j;
-      if (J < nb) scores[(size_t(bh) * nb + I) * nb + J] = bvalid[size_t(bh) * nb + J] > 0 ? acc[i][j] * scale : -INFINITY;
+    for (int j = 0; j < 8; ++j) {
+      const int J = J0 + tx + 16 * j;
+      if (J < nb) row[J] = live[j] ? acc[i][j] * scale : -INFINITY;
     }
   }
 }
@@ -479,7 +505,7 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
     launch_pool<bf16_t>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
   else
     launch_pool<float>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
-  const int tiles = (nb + 63) / 64;
+  const int tiles = (nb + kScT - 1) / kScT;
   hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, w.qbar, w.kbar, bvalid, nb, d, scale,
                      w.scores);
   // Workgroup shapes as measured fastest: 256 lanes up to 32 blocks each, then 512 lanes of
