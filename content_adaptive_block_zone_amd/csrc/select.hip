@@ -183,7 +183,6 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
   }
 }
 
-__device__ __forceinline__ uint32_t key_of(float p) { return __float_as_uint(p); }
 
 // One workgroup per query block, the row held in registers: thread t of a TPB-thread
 // workgroup keeps key blocks t, t + TPB, t + 2 TPB, ... (VPT of them), so that the 31-step
@@ -267,20 +266,14 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     }
   const float p = prm.top_p;
   tot = block_sum<TPB>(tot, redf);
-  // kk = key + 1 for live blocks, 0 for dead ones: the searches below find key + 1 and
-  // exclude dead blocks by the comparison alone (adding 0.f leaves every sum unchanged)
-  // (kept in registers up to 32 per lane, recomputed from q beyond that)
-  constexpr bool kStore = VPT <= 32;
-  uint32_t kks[kStore ? VPT : 1];
-  if (kStore) {
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) kks[kStore ? i : 0] = q[i] >= 0.f ? key_of(q[i]) + 1u : 0u;
-  }
-  auto kk_at = [&](int i) -> uint32_t {
-    if (kStore) return kks[kStore ? i : 0];
-    const uint32_t u = key_of(q[i]);
-    return (u + 1u) & ~uint32_t(int32_t(u) >> 31);  // negative (dead) -> 0
-  };
+  // The searches run over keys kk = bits(P) + 1 for live blocks and 0 for dead ones, so
+  // they find key + 1.  Probabilities are never -0 and the bit patterns of non-negative
+  // floats are ordered like their values, so for a live block kk >= c is P >= at(c - 1)
+  // and kk == c is P == at(c - 1) (at(u): the float with bits u); a dead block's -1 fails
+  // every such comparison, as its kk = 0 does (c >= 1 throughout).  The searches never
+  // accept a key above that of 1.0, so every threshold compared is finite.  The
+  // comparisons therefore run on q itself and no keys are kept.
+  auto at = [](uint32_t u) { return __uint_as_float(u); };
 
   // ---- Top-p: largest key v with sum(P >= v) > p
   int n_p = nlive, need_p = 0;
@@ -290,20 +283,22 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     uint32_t Tk = 0;
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = Tk | (1u << bit);
+      const float c = at(cand - 1u);
       float sm = 0.f;
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) sm += kk_at(i) >= cand ? q[i] : 0.f;
+      for (int i = 0; i < VPT; ++i) sm += q[i] >= c ? q[i] : 0.f;
       sm = pass_sum(sm);
       if (sm > p) Tk = cand;
     }
     vstar = Tk - 1u;  // Tk >= 1: all live blocks have kk >= 1 and sum to tot > p
     float sg = 0.f;
     int cg = 0, ce = 0;
+    const float above = at(Tk), equal = at(Tk - 1u);  // kk > Tk, kk == Tk
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      sg += kk_at(i) > Tk ? q[i] : 0.f;
-      cg += kk_at(i) > Tk;
-      ce += kk_at(i) == Tk;
+      sg += q[i] >= above ? q[i] : 0.f;
+      cg += q[i] >= above;
+      ce += q[i] == equal;
     }
     sg = block_sum<TPB>(sg, redf);
     cg = block_sum_i<TPB>(cg, redi);
@@ -327,16 +322,17 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     uint32_t Tk = 0;
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = Tk | (1u << bit);
+      const float cf = at(cand - 1u);
       int c = 0;
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) c += kk_at(i) >= cand;
+      for (int i = 0; i < VPT; ++i) c += q[i] >= cf;
       c = pass_sum_i(c);
       if (c >= n) Tk = cand;
     }
     Tcut = Tk;
     int cg = 0;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) cg += kk_at(i) > Tk;
+    for (int i = 0; i < VPT; ++i) cg += q[i] >= at(Tk);
     cg = block_sum_i<TPB>(cg, redi);
     need_eq = n - cg;
   }
@@ -364,18 +360,19 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     }
     return incl - tot_i + before_i;
   };
+  const float cut_eq = at(Tcut - 1u), cut_above = at(Tcut);  // kk == Tcut, kk > Tcut
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const uint64_t eq = __builtin_amdgcn_ballot_w64(kk_at(i) == Tcut);
+    const uint64_t eq = __builtin_amdgcn_ballot_w64(q[i] == cut_eq);
     if (lane == 0) wcnt[0][wv][i] = __builtin_popcountll(eq);
   }
   __syncthreads();
   const int eqo = offsets(0);
   // taken: above the cut, or at it and among the first need_eq such blocks in block order
   auto take_at = [&](int i) {
-    const bool isq = kk_at(i) == Tcut;
+    const bool isq = q[i] == cut_eq;
     const int rank = __builtin_amdgcn_readlane(eqo, i) + below(__builtin_amdgcn_ballot_w64(isq));
-    return kk_at(i) > Tcut || (isq && rank < need_eq);
+    return q[i] >= cut_above || (isq && rank < need_eq);
   };
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
@@ -401,7 +398,7 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
       out[pos] = J;
       atomicOr(bm + size_t(J) * words32(nb) + (I >> 5), 1u << (I & 31));
       pmin_sel = fminf(pmin_sel, q[i]);
-    } else if (kk_at(i) > 0u) {
+    } else if (q[i] >= 0.f) {  // live
       pmax_uns = fmaxf(pmax_uns, q[i]);
     }
   }
