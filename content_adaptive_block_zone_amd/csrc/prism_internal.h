@@ -11,7 +11,7 @@
 namespace prism {
 
 constexpr int kMaxZoneVol = 4096;   // zone-local LDS map of the A2V norm
-constexpr int kMaxSelectNb = 16384; // one score row of the selection kernel lives in registers (512 x 32)
+constexpr int kMaxSelectNb = 32768; // one score row of the selection kernel lives in registers (1024 x 32)
 constexpr int kTileRows = 64;       // query/key rows per attention tile
 
 // ----------------------------------------------------------------------------------

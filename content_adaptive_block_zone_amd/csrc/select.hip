@@ -188,7 +188,7 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
 // workgroup keeps key blocks t, t + TPB, t + 2 TPB, ... (VPT of them), so that the 31-step
 // searches are register passes.  Sums run over each thread's blocks in that order, then
 // across the workgroup, so results are deterministic.  Ascending emission uses wave
-// ballots per round of TPB blocks.  Used for nb <= TPB * VPT (at most 512 * 32).
+// ballots per round of TPB blocks.  Used for nb <= TPB * VPT (at most 1024 * 32).
 __device__ __forceinline__ int below(uint64_t mask) {  // set bits of mask below this lane
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
@@ -506,8 +506,9 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
   hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, w.qbar, w.kbar, bvalid, nb, d, scale,
                      w.scores);
   // Workgroup shapes as measured fastest: 256 lanes up to 32 blocks each, then 512 lanes of
-  // 32 (at 64 per lane the register file allows one wave per SIMD).  nb <= 512 * 32 is
-  // checked by the caller.
+  // 32 (at 64 per lane the register file allows one wave per SIMD), then 1024 lanes of 32
+  // (at most 128 registers per lane, which the kernel fits).  nb <= 1024 * 32 is checked
+  // by the caller.
   const dim3 sg(nb, BH);
   if (nb <= 256 * 8)
     hipLaunchKernelGGL((k_select_reg<256, 8>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
@@ -518,8 +519,11 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
   else if (nb <= 256 * 32)
     hipLaunchKernelGGL((k_select_reg<256, 32>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
                        sel_cnt, sel_margin, w.bitmap);
-  else
+  else if (nb <= 512 * 32)
     hipLaunchKernelGGL((k_select_reg<512, 32>), sg, dim3(512), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
+                       sel_cnt, sel_margin, w.bitmap);
+  else
+    hipLaunchKernelGGL((k_select_reg<1024, 32>), sg, dim3(1024), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
                        sel_cnt, sel_margin, w.bitmap);
   const int rows = BH * nb;
   hipLaunchKernelGGL(k_rev_count, dim3((rows + 255) / 256), dim3(256), 0, s, w.bitmap, nb, rows, w.rcnt);

@@ -197,7 +197,7 @@ prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int
 /* (a4, a5) Block pooling and hybrid Top-k/Top-p selection (abstract; Figure 2 caption;
  * Table 7 caption).
  * qp, kp       [B][Hh][nb*vol][d] permuted Q and K.
- * block_valid  int32 [B][Hh][nb].  nb <= 16384 (a row of block scores is held in the
+ * block_valid  int32 [B][Hh][nb].  nb <= 32768 (a row of block scores is held in the
  *              registers of one workgroup), else PRISM_ERR_SHAPE.
  * Pooled means (float32) of each block's valid rows give scores scale * <Qbar_I, Kbar_J>
  * over live key blocks; softmax, then the hybrid count on the descending order (ties to

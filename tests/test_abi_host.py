@@ -128,9 +128,9 @@ def test_calls_validate_before_launch(lib):
                                  P, P, P, P, None, P, 1 << 30, None), E.PRISM_ERR_ARG),
         ("prism_select_blocks", (P, P, F32, P, 1, 2, 16, 16, 64, 0.125, sel, P, P, P, P, None, P, 16, None),
          E.PRISM_ERR_ARG),                                                             # workspace too small
-        ("prism_select_blocks", (P, P, F32, P, 1, 2, 20000, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 40,
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 40000, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 44,
                                  None), E.PRISM_ERR_SHAPE),
-        ("prism_select_blocks", (P, P, F32, P, 1, 2, 16385, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 40,
+        ("prism_select_blocks", (P, P, F32, P, 1, 2, 32769, 16, 64, 0.125, sel, P, P, P, P, None, P, 1 << 44,
                                  None), E.PRISM_ERR_SHAPE),                            # one past the limit
         ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 8, 1, 2, 16, 16, 96, 0.125, P, P, None, 0, None),
          E.PRISM_ERR_DTYPE),

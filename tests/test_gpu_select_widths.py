@@ -1,6 +1,6 @@
 """GPU parity of the block selection at every row width the library dispatches on: its
-four workgroup shapes (up to 2,048 / 4,096 / 8,192 / 16,384 key blocks, the largest width
-accepted).  Synthetic rows: each query
+five workgroup shapes (up to 2,048 / 4,096 / 8,192 / 16,384 / 32,768 key blocks, the
+largest width accepted).  Synthetic rows: each query
 block's pooled feature has its own magnitude, so that some rows are flat (the Top-k clamp
 decides) and some are peaked (Top-p decides); about 5 % of the blocks are dead and the
 valid counts are ragged.  Sampled rows are compared with the oracle's selection (exact,
@@ -60,7 +60,7 @@ def reverse_is_transpose(idx, cnt, rp, ri):
     assert (ri[:rp[-1]] == I[o]).all()
 
 
-@pytest.mark.parametrize("nb", [1500, 3000, 6000, 9000, 16384])
+@pytest.mark.parametrize("nb", [1500, 3000, 6000, 9000, 16384, 20000, 32768])
 def test_select_width(nb):
     from content_adaptive_block_zone_amd import api
     q, k, bv = make_case(nb, seed=nb)
