@@ -525,6 +525,8 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
       st_ = mma32(lds8<bf16x8>(sK + tofs(32 * kh + l32, 16 * s + 8 * g)), qf[s], st_);
       dp = mma32(lds8<bf16x8>(sV + tofs(32 * kh + l32, 16 * s + 8 * g)), gf[s], dp);
     }
+    // the first K^T operands of the dQ product, read before the softmax step
+    const auto preK0 = ldtr(sK, 0, 2 * kh), preK1 = ldtr(sK, 0, 2 * kh + 1);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const bool ok = 32 * kh + acc_row32(e, g) < nJ;
@@ -534,8 +536,8 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
     const bf16x8 s0 = pack8(dp, 0), s1 = pack8(dp, 1);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      dq[t] = mma32(ldtr(sK, t, 2 * kh), s0, dq[t]);
-      dq[t] = mma32(ldtr(sK, t, 2 * kh + 1), s1, dq[t]);
+      dq[t] = mma32(t == 0 ? preK0 : ldtr(sK, t, 2 * kh), s0, dq[t]);
+      dq[t] = mma32(t == 0 ? preK1 : ldtr(sK, t, 2 * kh + 1), s1, dq[t]);
     }
   }
   // sum the two key halves: waves with kh = 1 hand their partials to kh = 0 through LDS
@@ -656,6 +658,10 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
     const bf16x8 P0 = pack8(s_, 0), P1 = pack8(s_, 1), S0 = pack8(dp, 0), S1 = pack8(dp, 1);
     const bf16x8 own0 = x == 0 ? P0 : S0, own1 = x == 0 ? P1 : S1;
     const bf16x8 give0 = x == 0 ? S0 : P0, give1 = x == 0 ? S1 : P1;
+    // the first transposed operands of the dV/dK products do not depend on the swap: read
+    // them before its barrier, so their LDS latency overlaps the wait
+    const uint16_t* At = x == 0 ? sG : sQ;  // dO^T for dV, Q^T for dK
+    const auto pre0 = ldtr(At, 0, 0), pre1 = ldtr(At, 0, 1), pre2 = ldtr(At, 0, 2), pre3 = ldtr(At, 0, 3);
     xbuf[w * 128 + lane] = give0;
     xbuf[w * 128 + 64 + lane] = give1;
     __syncthreads();
@@ -663,13 +669,12 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
     // query half 0 comes from wave x = 0, half 1 from x = 1
     const bf16x8 lo0 = x == 0 ? own0 : got0, lo1 = x == 0 ? own1 : got1;
     const bf16x8 hi0 = x == 0 ? got0 : own0, hi1 = x == 0 ? got1 : own1;
-    const uint16_t* At = x == 0 ? sG : sQ;  // dO^T for dV, Q^T for dK
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      acc[t] = mma32(ldtr(At, t, 0), lo0, acc[t]);
-      acc[t] = mma32(ldtr(At, t, 1), lo1, acc[t]);
-      acc[t] = mma32(ldtr(At, t, 2), hi0, acc[t]);
-      acc[t] = mma32(ldtr(At, t, 3), hi1, acc[t]);
+      acc[t] = mma32(t == 0 ? pre0 : ldtr(At, t, 0), lo0, acc[t]);
+      acc[t] = mma32(t == 0 ? pre1 : ldtr(At, t, 1), lo1, acc[t]);
+      acc[t] = mma32(t == 0 ? pre2 : ldtr(At, t, 2), hi0, acc[t]);
+      acc[t] = mma32(t == 0 ? pre3 : ldtr(At, t, 3), hi1, acc[t]);
     }
   }
   if (kok || (!a.dense && key < TR)) {
