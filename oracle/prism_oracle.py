@@ -505,11 +505,13 @@ def hybrid_count(P_sorted: np.ndarray, top_p: float, k_min: int, k_max: int, dty
 
     Top-p: n_p = the smallest n whose cumulative sum C_n exceeds top_p (strictly),
     or every live block if no prefix does.  Hybrid: n = min(max(n_p, k_min), k_max, n_live).
+    Reading for top_p >= 1: the weights of a row sum to exactly 1, so no prefix exceeds
+    top_p and every live block is kept, however the float rounding of C_n comes out.
     Returns (n, n_p)."""
     P_sorted = np.asarray(P_sorted).astype(dtype)
     n_live = P_sorted.size
     C = np.cumsum(P_sorted, dtype=dtype)
-    over = np.nonzero(C > dtype(top_p))[0]
+    over = np.nonzero(C > dtype(top_p))[0] if top_p < 1 else np.zeros(0, dtype=np.int64)
     n_p = int(over[0]) + 1 if over.size else n_live
     n = min(max(n_p, k_min), k_max, n_live)
     return n, n_p
@@ -542,9 +544,10 @@ def select_row(qbar_row: np.ndarray, kbar: np.ndarray, live: np.ndarray, scale: 
     near = False
     if n < Ps.size and (float(Ps[n - 1]) - float(Ps[n])) <= NEAR_TIE * float(Ps[n - 1]):
         near = True
-    if abs(Cs[n_p - 1] - top_p) < NEAR_TIE and _clamp(n_p + 1, k_min, k_max, Ps.size) != n:
+    if top_p < 1 and abs(Cs[n_p - 1] - top_p) < NEAR_TIE and _clamp(n_p + 1, k_min, k_max, Ps.size) != n:
         near = True
-    if n_p >= 2 and abs(Cs[n_p - 2] - top_p) < NEAR_TIE and _clamp(n_p - 1, k_min, k_max, Ps.size) != n:
+    if top_p < 1 and n_p >= 2 and abs(Cs[n_p - 2] - top_p) < NEAR_TIE and \
+            _clamp(n_p - 1, k_min, k_max, Ps.size) != n:
         near = True
     return sel.astype(np.int32), near
 
@@ -595,16 +598,17 @@ def select_blocks_all(qbar: np.ndarray, kbar: np.ndarray, bvalid: np.ndarray, sc
             Cd = np.cumsum(Ps.astype(np.float64), axis=1)
             nl = J.size
             for r, I in enumerate(Ilive):
-                over = np.nonzero(Cs[r] > dtype(top_p))[0]
+                over = np.nonzero(Cs[r] > dtype(top_p))[0] if top_p < 1 else np.zeros(0, dtype=np.int64)
                 n_p = int(over[0]) + 1 if over.size else nl
                 n = _clamp(n_p, k_min, k_max, nl)
                 sel[(b, h, int(I))] = np.sort(J[order[r, :n]]).astype(np.int32)
                 nr = False
                 if n < nl and (float(Ps[r, n - 1]) - float(Ps[r, n])) <= NEAR_TIE * float(Ps[r, n - 1]):
                     nr = True
-                if abs(Cd[r, n_p - 1] - top_p) < NEAR_TIE and _clamp(n_p + 1, k_min, k_max, nl) != n:
+                if top_p < 1 and abs(Cd[r, n_p - 1] - top_p) < NEAR_TIE and _clamp(n_p + 1, k_min, k_max, nl) != n:
                     nr = True
-                if n_p >= 2 and abs(Cd[r, n_p - 2] - top_p) < NEAR_TIE and _clamp(n_p - 1, k_min, k_max, nl) != n:
+                if top_p < 1 and n_p >= 2 and abs(Cd[r, n_p - 2] - top_p) < NEAR_TIE and \
+                        _clamp(n_p - 1, k_min, k_max, nl) != n:
                     nr = True
                 near[(b, h, int(I))] = nr
             for I in np.nonzero(~live)[0]:

@@ -441,6 +441,30 @@ def test_hybrid_count_hand_rows(dtype):
     assert O.hybrid_count(P, 0.9, 1, 8, dtype)[0] == 3
 
 
+def test_top_p_one_keeps_every_live_block():
+    """Top-p at p = 1 (Table 7 caption: the smallest set whose cumulative weight exceeds
+    the threshold): weights that sum to 1 have no prefix exceeding 1, so every live block
+    stays, also when the float32 running sum rounds above 1 before the last block, and the
+    Top-k floor alone does not cut the row."""
+    P = np.array([0.6, 0.4000001, 1e-9, 1e-9], dtype=np.float32)
+    assert np.cumsum(P, dtype=np.float32)[1] > np.float32(1.0)      # the float32 sum overshoots at n = 2
+    assert O.hybrid_count(P, 1.0, 1, 8, np.float32) == (4, 4)
+    # a whole selection row: softmax of many logits, Top-p 1 with k_min 1 keeps all live blocks
+    rng = np.random.default_rng(3)
+    nb, d = 600, 16
+    qb = rng.standard_normal((1, 1, nb, d)).astype(np.float32)
+    kb = rng.standard_normal((1, 1, nb, d)).astype(np.float32)
+    bv = np.full((1, 1, nb), 4, dtype=np.int32)
+    bv[0, 0, ::7] = 0
+    live = np.nonzero(bv[0, 0] > 0)[0]
+    sel, near = O.select_blocks_all(qb, kb, bv, 0.25, 1.0, 1, nb)
+    for I in live:
+        assert sel[(0, 0, int(I))].tolist() == live.tolist()
+        assert not near[(0, 0, int(I))]
+    sel_r, _ = O.select_blocks(qb, kb, bv, 0.25, 1.0, 1, nb, rows=[int(live[0])])
+    assert sel_r[(0, 0, int(live[0]))].tolist() == live.tolist()
+
+
 def test_top_p_is_smallest_subset_by_bruteforce():
     rng = np.random.default_rng(5)
     for _ in range(200):
