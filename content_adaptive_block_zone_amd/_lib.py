@@ -54,7 +54,11 @@ PROTOTYPES = {
                                             _P, c_size_t, _P]),
     "prism_assign_shapes": (c_int, [_P, c_int, c_int, _GP, _SP, _SHP, _P, _P, _P]),
     "prism_permute": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _SP, _P, c_int, _P, _P]),
+    "prism_permute_pool": (c_int, [_P, _P, c_int, c_int, c_int, c_int, _GP, _SP, _P, _P, _P, _P]),
     "prism_select_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "prism_select_pooled_workspace_size": (c_size_t, [c_int, c_int, c_int]),
+    "prism_select_blocks_pooled": (c_int, [_P, _P, _P, c_int, c_int, c_int, c_int, c_float, _SLP, _P, _P, _P, _P, _P,
+                                           _P, c_size_t, _P]),
     "prism_tiles_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int]),
     "prism_blocks_to_tiles": (c_int, [_P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, _P, _P, _P, _P, _P,
                                       _P, c_size_t, _P]),

@@ -233,6 +233,40 @@ def prism_permute(x: torch.Tensor, y: torch.Tensor, grid: PrismGrid, shapes: Pri
           "prism_permute")
 
 
+def prism_permute_pool(x: torch.Tensor, y: torch.Tensor, grid: PrismGrid, shapes: PrismShapes,
+                       shape_id: torch.Tensor, pooled: torch.Tensor, block_valid: Optional[torch.Tensor] = None,
+                       stream=None) -> None:
+    """Forward permutation that also writes each block's mean valid row (float32 [B, Hh, nb, d])."""
+    B, Hh, n, d = x.shape
+    dt = _same_dtype(x, y)
+    nb = prism_num_blocks(grid, shapes)
+    check(load().prism_permute_pool(_ptr(x, shape=(B, Hh, grid.T * grid.H * grid.W, d), name="x"),
+                                    _ptr(y, shape=(B, Hh, nb * shapes.vol, d), name="y"), dt, B, Hh, d, grid, shapes,
+                                    _ptr(shape_id, torch.int32, (B, Hh, prism_num_zones(grid)), "shape_id"),
+                                    _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"),
+                                    _ptr(pooled, torch.float32, (B, Hh, nb, d), "pooled"), _stream(stream)),
+          "prism_permute_pool")
+
+
+def prism_select_pooled_workspace_size(B: int, Hh: int, nb: int) -> int:
+    return int(load().prism_select_pooled_workspace_size(B, Hh, nb))
+
+
+def prism_select_blocks_pooled(qbar: torch.Tensor, kbar: torch.Tensor, block_valid: torch.Tensor, scale: float,
+                               params: PrismSelectParams, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                               rev_ptr: torch.Tensor, rev_idx: torch.Tensor, workspace: torch.Tensor,
+                               sel_margin: Optional[torch.Tensor] = None, stream=None) -> None:
+    B, Hh, nb, d = qbar.shape
+    km = params.k_max
+    check(load().prism_select_blocks_pooled(
+        _ptr(qbar, torch.float32, name="qbar"), _ptr(kbar, torch.float32, qbar.shape, "kbar"),
+        _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"), B, Hh, nb, d, float(scale), params,
+        _ptr(sel_idx, torch.int32, (B, Hh, nb, km), "sel_idx"), _ptr(sel_cnt, torch.int32, (B, Hh, nb), "sel_cnt"),
+        _ptr(rev_ptr, torch.int32, (B, Hh, nb + 1), "rev_ptr"), _ptr(rev_idx, torch.int32, (B, Hh, nb * km), "rev_idx"),
+        _ptr(sel_margin, torch.float32, (B, Hh, nb), "sel_margin"), _ptr(workspace, torch.uint8, name="workspace"),
+        workspace.numel(), _stream(stream)), "prism_select_blocks_pooled")
+
+
 def prism_select_blocks(qp: torch.Tensor, kp: torch.Tensor, block_valid: torch.Tensor, vol: int, scale: float,
                         params: PrismSelectParams, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
                         rev_ptr: torch.Tensor, rev_idx: torch.Tensor, workspace: torch.Tensor,

@@ -12,7 +12,7 @@ namespace prism {
 
 __device__ __forceinline__ int tile_rows(const AttnArgs& a) { return a.dense ? kTileRows : a.vol; }
 __device__ __forceinline__ int block_rows(const AttnArgs& a, int bh, int I) {
-  return a.dense ? min(kTileRows, a.nrows - I * kTileRows) : a.bvalid[size_t(bh) * a.nb + I];
+  return a.dense ? min(kTileRows, a.nrows - I * kTileRows) : clampi(a.bvalid[size_t(bh) * a.nb + I], 0, a.vol);
 }
 __device__ __forceinline__ size_t block_row0(const AttnArgs& a, int bh, int I) {
   return size_t(bh) * a.nrows + size_t(I) * tile_rows(a);
@@ -50,10 +50,10 @@ __global__ __launch_bounds__(NT) void k_fwd_generic(AttnArgs a) {
     acc[c] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
+  const int cnt = a.dense ? a.nb : (nI > 0 ? clampi(a.sel_cnt[size_t(bh) * a.nb + I], 0, a.k_max) : 0);
   const int32_t* lst = a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max;
   for (int s = 0; s < cnt; ++s) {
-    const int J = a.dense ? s : lst[s];
+    const int J = a.dense ? s : clampi(lst[s], 0, a.nb - 1);
     const int nJ = block_rows(a, bh, J);
     const size_t k0 = block_row0(a, bh, J);
     __syncthreads();
@@ -135,12 +135,12 @@ __global__ __launch_bounds__(NT) void k_dkdv_generic(AttnArgs a) {
   if (a.dense) {
     cnt = a.nb;
   } else if (nJ > 0) {
-    const int32_t* rp = a.rev_ptr + size_t(bh) * (a.nb + 1);
-    cnt = rp[J + 1] - rp[J];
-    lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rp[J];
+    const RevRange rr = rev_range(a.rev_ptr + size_t(bh) * (a.nb + 1), J, a.nb, a.k_max);
+    cnt = rr.cnt;
+    lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rr.start;
   }
   for (int s = 0; s < cnt; ++s) {
-    const int I = a.dense ? s : lst[s];
+    const int I = a.dense ? s : clampi(lst[s], 0, a.nb - 1);
     const int nI = block_rows(a, bh, I);
     const size_t q0 = block_row0(a, bh, I);
     __syncthreads();
@@ -211,10 +211,10 @@ __global__ __launch_bounds__(NT) void k_dq_generic(AttnArgs a) {
   }
   const float li = r < nI ? a.lse_in[r0 + r] : 0.f;
   const float Di = r < nI ? a.Dbuf[r0 + r] : 0.f;
-  const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
+  const int cnt = a.dense ? a.nb : (nI > 0 ? clampi(a.sel_cnt[size_t(bh) * a.nb + I], 0, a.k_max) : 0);
   const int32_t* lst = a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max;
   for (int s = 0; s < cnt; ++s) {
-    const int J = a.dense ? s : lst[s];
+    const int J = a.dense ? s : clampi(lst[s], 0, a.nb - 1);
     const int nJ = block_rows(a, bh, J);
     const size_t k0 = block_row0(a, bh, J);
     __syncthreads();

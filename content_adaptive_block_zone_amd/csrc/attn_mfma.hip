@@ -66,7 +66,7 @@ __device__ __forceinline__ uint32_t pk2(float a, float b) {
   return uint32_t(__builtin_bit_cast(uint16_t, (__bf16)a)) | (uint32_t(__builtin_bit_cast(uint16_t, (__bf16)b)) << 16);
 }
 __device__ __forceinline__ int nrows_of(const AttnArgs& a, int bh, int I) {
-  return a.dense ? min(TR, a.nrows - I * TR) : a.bvalid[size_t(bh) * a.nb + I];
+  return a.dense ? min(TR, a.nrows - I * TR) : clampi(a.bvalid[size_t(bh) * a.nb + I], 0, TR);
 }
 __device__ __forceinline__ size_t row0_of(const AttnArgs& a, int bh, int I) {
   return size_t(bh) * a.nrows + size_t(I) * TR;
@@ -172,7 +172,7 @@ __device__ __forceinline__ BlockList load_list(const AttnArgs& a, int bh, const 
   BlockList L{lst, cnt, !a.dense && cnt <= CAP && a.nb < 65536};
   if (L.in_lds)
     for (int k = threadIdx.x; k < cnt; k += NT) {
-      const int J = lst[k];
+      const int J = clampi(lst[k], 0, a.nb - 1);
       meta[k] = J | (nrows_of(a, bh, J) << 16);
     }
   __syncthreads();
@@ -189,7 +189,7 @@ __device__ __forceinline__ void list_at(const AttnArgs& a, int bh, const BlockLi
     J = m & 0xffff;
     n = m >> 16;
   } else {
-    J = __builtin_amdgcn_readfirstlane(L.lst[k]);
+    J = __builtin_amdgcn_readfirstlane(clampi(L.lst[k], 0, a.nb - 1));
     n = __builtin_amdgcn_readfirstlane(nrows_of(a, bh, J));
   }
 }
@@ -325,7 +325,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   const bf16_t* K = static_cast<const bf16_t*>(a.k);
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   bf16_t* O = static_cast<bf16_t*>(a.out);
-  const int cnt = a.dense ? a.nkb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
+  const int cnt = a.dense ? a.nkb : (nI > 0 ? clampi(a.sel_cnt[size_t(bh) * a.nb + I], 0, a.k_max) : 0);
   const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
   const int qrow = 32 * qh + l32;
   const bool qok = qrow < nI;
@@ -483,7 +483,7 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
   const bf16_t* V = static_cast<const bf16_t*>(a.v);
   const bf16_t* Gd = static_cast<const bf16_t*>(a.dout);
   bf16_t* dQ = static_cast<bf16_t*>(a.dq);
-  const int cnt = a.dense ? a.nb : (nI > 0 ? a.sel_cnt[size_t(bh) * a.nb + I] : 0);
+  const int cnt = a.dense ? a.nb : (nI > 0 ? clampi(a.sel_cnt[size_t(bh) * a.nb + I], 0, a.k_max) : 0);
   const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
   const int qrow = 32 * qh + l32;
   const bool qok = qrow < nI;
@@ -590,9 +590,9 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   if (a.dense) {
     cnt = a.nb;
   } else if (nJ > 0) {
-    const int32_t* rp = a.rev_ptr + size_t(bh) * (a.nb + 1);
-    cnt = rp[J + 1] - rp[J];
-    lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rp[J];
+    const RevRange rr = rev_range(a.rev_ptr + size_t(bh) * (a.nb + 1), J, a.nb, a.k_max);
+    cnt = rr.cnt;
+    lst = a.rev_idx + size_t(bh) * a.nb * a.k_max + rr.start;
   }
   const BlockList bl = load_list<kMetaCapKV>(a, bh, lst, cnt, sMeta);
   const int key = 32 * kh + l32;

@@ -233,12 +233,40 @@ prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int
   ShapeTab t;
   st = check_shapes(shapes, g, &t);
   if (st != PRISM_OK) return st;
-  return launched(launch_permute(x, y, dtype, B * Hh, d, g, t, shape_id, inverse, block_valid, stream), "prism_permute");
+  return launched(launch_permute(x, y, dtype, B * Hh, d, g, t, shape_id, inverse, block_valid, nullptr, stream),
+                  "prism_permute");
+}
+
+prism_status prism_permute_pool(const void* x, void* y, prism_dtype dtype, int B, int Hh, int d,
+                                const prism_grid* grid, const prism_shapes* shapes, const int32_t* shape_id,
+                                int32_t* block_valid, float* pooled, hipStream_t stream) {
+  const char* who = "prism_permute_pool";
+  if (!x || !y || !shape_id || !pooled) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1 || d < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, d must be >= 1", who);
+  if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "%s: unknown dtype %d", who, int(dtype));
+  const size_t row_bytes = size_t(d) * esize(dtype);
+  const size_t chunks = row_bytes / 16;
+  if (row_bytes % 16 != 0 || chunks > 256 || (chunks & (chunks - 1)) != 0)
+    return fail(PRISM_ERR_DTYPE, "%s: d*sizeof(dtype) must be 16 bytes times a power of two, at most 4096 bytes", who);
+  if (x == y) return fail(PRISM_ERR_ARG, "%s: x and y must not alias", who);
+  Geo g;
+  prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  ShapeTab t;
+  st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  if (!t.uniform) return fail(PRISM_ERR_SHAPE, "%s: candidates of several volumes (blocks span several units)", who);
+  return launched(launch_permute(x, y, dtype, B * Hh, d, g, t, shape_id, 0, block_valid, pooled, stream), who);
 }
 
 size_t prism_select_workspace_size(int B, int Hh, int nb, int d) {
   if (B < 1 || Hh < 1 || nb < 1 || d < 1) return 0;
-  return select_ws_bytes(B * Hh, nb, d);
+  return select_ws_bytes(B * Hh, nb, d, true);
+}
+
+size_t prism_select_pooled_workspace_size(int B, int Hh, int nb) {
+  if (B < 1 || Hh < 1 || nb < 1) return 0;
+  return select_ws_bytes(B * Hh, nb, 1, false);
 }
 
 prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dtype, const int32_t* block_valid,
@@ -256,12 +284,33 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
   if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(PRISM_ERR_ARG, "prism_select_blocks: top_p must be in (0, 1]");
   if (p.k_min < 1 || p.k_max < p.k_min) return fail(PRISM_ERR_ARG, "prism_select_blocks: need 1 <= k_min <= k_max");
   if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "prism_select_blocks: scale must be finite");
-  if (ws_bytes < select_ws_bytes(B * Hh, nb, d))
+  if (ws_bytes < select_ws_bytes(B * Hh, nb, d, true))
     return fail(PRISM_ERR_ARG, "prism_select_blocks: workspace of %zu bytes < required %zu", ws_bytes,
-                select_ws_bytes(B * Hh, nb, d));
+                select_ws_bytes(B * Hh, nb, d, true));
   return launched(launch_select(qp, kp, dtype, block_valid, B * Hh, nb, vol, d, scale, p, sel_idx, sel_cnt,
                                 rev_ptr, rev_idx, sel_margin, workspace, stream),
                   "prism_select_blocks");
+}
+
+prism_status prism_select_blocks_pooled(const float* qbar, const float* kbar, const int32_t* block_valid, int B,
+                                        int Hh, int nb, int d, float scale, const prism_select_params* params,
+                                        int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
+                                        float* sel_margin, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  const char* who = "prism_select_blocks_pooled";
+  if (!qbar || !kbar || !block_valid || !params || !sel_idx || !sel_cnt || !rev_ptr || !rev_idx || !workspace)
+    return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (B < 1 || Hh < 1 || nb < 1) return fail(PRISM_ERR_ARG, "%s: sizes must be >= 1", who);
+  if (nb > kMaxSelectNb) return fail(PRISM_ERR_SHAPE, "%s: nb=%d exceeds %d", who, nb, kMaxSelectNb);
+  if (d < 1 || d % 16 != 0 || d > 4096) return fail(PRISM_ERR_DTYPE, "%s: d=%d must be a multiple of 16 up to 4096", who, d);
+  const prism_select_params p = *params;
+  if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(PRISM_ERR_ARG, "%s: top_p must be in (0, 1]", who);
+  if (p.k_min < 1 || p.k_max < p.k_min) return fail(PRISM_ERR_ARG, "%s: need 1 <= k_min <= k_max", who);
+  if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "%s: scale must be finite", who);
+  const size_t need = select_ws_bytes(B * Hh, nb, d, false);
+  if (ws_bytes < need) return fail(PRISM_ERR_ARG, "%s: workspace of %zu bytes < required %zu", who, ws_bytes, need);
+  return launched(launch_select_pooled(qbar, kbar, block_valid, B * Hh, nb, d, scale, p, sel_idx, sel_cnt, rev_ptr,
+                                       rev_idx, sel_margin, workspace, stream),
+                  who);
 }
 
 static prism_status check_attn_common(const char* who, prism_dtype dtype, int B, int Hh, int nb, int vol, int d,

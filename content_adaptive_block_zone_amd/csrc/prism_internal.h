@@ -62,6 +62,24 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
 }
 
 // ----------------------------------------------------------------------------------
+// Caller-provided device lists (valid counts, selection lists, reverse index) are
+// clamped into range before they address memory: a malformed list gives unspecified
+// results but no access outside the caller's buffers.
+// ----------------------------------------------------------------------------------
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return min(max(x, lo), hi); }
+// Entries [start, start + cnt) of key block J's reverse list, inside [0, nb * k_max) and at
+// most nb long.
+struct RevRange {
+  int start, cnt;
+};
+__device__ __forceinline__ RevRange rev_range(const int32_t* rp, int J, int nb, int k_max) {
+  const long long cap = (long long)nb * k_max;
+  const long long s = min(max((long long)rp[J], 0LL), cap);
+  const long long e = min(max((long long)rp[J + 1], s), cap);
+  return RevRange{int(s), int(min(e - s, (long long)nb))};
+}
+
+// ----------------------------------------------------------------------------------
 // Reductions (64-lane wavefronts).
 // ----------------------------------------------------------------------------------
 // Reductions over the 64 lanes of a wavefront, every lane receiving the result, without
@@ -233,14 +251,19 @@ hipError_t launch_assign_shapes_multi(const float* stats, const float* vact, int
                                       float tau_256, int32_t* shape_id, float* margin, hipStream_t s);
 hipError_t launch_block_heads(const int32_t* unit_valid, const int32_t* shape_id, int BH, const Geo& g,
                               const ShapeTab& tab, int32_t* block_valid, hipStream_t s);
+// pooled: optional out float [BH][nb][d], the mean of each unit's valid rows (forward only)
 hipError_t launch_permute(const void* x, void* y, prism_dtype dt, int BH, int d, const Geo& g,
                           const ShapeTab& tab, const int32_t* shape_id, int inverse,
-                          int32_t* block_valid, hipStream_t s);
+                          int32_t* block_valid, float* pooled, hipStream_t s);
 hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const int32_t* bvalid,
                          int BH, int nb, int vol, int d, float scale, const prism_select_params& p,
                          int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
                          float* sel_margin, void* ws, hipStream_t s);
-size_t select_ws_bytes(int BH, int nb, int d);
+// with pooled means given by the caller (qbar, kbar float [BH][nb][d])
+hipError_t launch_select_pooled(const float* qbar, const float* kbar, const int32_t* bvalid, int BH, int nb, int d,
+                                float scale, const prism_select_params& p, int32_t* sel_idx, int32_t* sel_cnt,
+                                int32_t* rev_ptr, int32_t* rev_idx, float* sel_margin, void* ws, hipStream_t s);
+size_t select_ws_bytes(int BH, int nb, int d, bool with_pooled);
 // Attention: the bf16 / d=128 / 64-token path runs on MFMA kernels, everything else on the
 // scalar kernels.  The forward needs no scratch; the backward's holds D (one float per row).
 size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt);

@@ -29,13 +29,17 @@ struct SelWs {
 
 __host__ __device__ inline int words32(int nb) { return (nb + 31) / 32; }
 
-SelWs carve(void* ws, int BH, int nb, int d) {
+// Workspace layout: [pooled Q, pooled K,] scores, bitmap, reverse counts.  The pooled
+// means are absent when the caller passes them in (prism_select_blocks_pooled).
+SelWs carve(void* ws, int BH, int nb, int d, bool with_pooled) {
   char* p = static_cast<char*>(ws);
-  SelWs w;
-  w.qbar = reinterpret_cast<float*>(p);
-  p += align256(size_t(BH) * nb * d * 4);
-  w.kbar = reinterpret_cast<float*>(p);
-  p += align256(size_t(BH) * nb * d * 4);
+  SelWs w{};
+  if (with_pooled) {
+    w.qbar = reinterpret_cast<float*>(p);
+    p += align256(size_t(BH) * nb * d * 4);
+    w.kbar = reinterpret_cast<float*>(p);
+    p += align256(size_t(BH) * nb * d * 4);
+  }
   w.scores = reinterpret_cast<float*>(p);
   p += align256(size_t(BH) * nb * nb * 4);
   w.bitmap = reinterpret_cast<uint32_t*>(p);
@@ -266,6 +270,9 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     }
   const float p = prm.top_p;
   tot = block_sum<TPB>(tot, redf);
+  // Top-p at p >= 1 keeps every live block: no proper prefix of weights summing to 1
+  // exceeds 1, and a float32 total that rounds above 1 must not cut the tail.
+  const bool cut_p = p < 1.f && tot > p;
   // The searches run over keys kk = bits(P) + 1 for live blocks and 0 for dead ones, so
   // they find key + 1.  Probabilities are never -0 and the bit patterns of non-negative
   // floats are ordered like their values, so for a live block kk >= c is P >= at(c - 1)
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
   int n_p = nlive, need_p = 0;
   uint32_t vstar = 0;
   float sum_gt_p = 0.f;
-  if (tot > p) {
+  if (cut_p) {
     uint32_t Tk = 0;
     for (int bit = 30; bit >= 0; --bit) {
       const uint32_t cand = Tk | (1u << bit);
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
   // ---- cut threshold (as kk) for exactly n kept blocks
   uint32_t Tcut;
   int need_eq;
-  if (n == n_p && tot > p) {
+  if (n == n_p && cut_p) {
     Tcut = vstar + 1u;
     need_eq = need_p;
   } else {
@@ -411,7 +418,7 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     sel_cnt[size_t(bh) * nb + I] = tot_sel;
     if (sel_margin) {
       float mg = n < nlive ? (pmin_sel - pmax_uns) / pmin_sel : 1.f;
-      if (tot > p && n == n_p) {
+      if (cut_p && n == n_p) {
         const float v = __uint_as_float(vstar);
         const float c_np = sum_gt_p + float(need_p) * v, c_prev = c_np - v;
         mg = fminf(mg, fabsf(c_np - p));
@@ -483,28 +490,21 @@ __global__ __launch_bounds__(64) void k_rev_fill(const uint32_t* __restrict__ bi
 
 }  // namespace
 
-size_t select_ws_bytes(int BH, int nb, int d) {
-  return 2 * align256(size_t(BH) * nb * d * 4) + align256(size_t(BH) * nb * nb * 4) +
+size_t select_ws_bytes(int BH, int nb, int d, bool with_pooled) {
+  return (with_pooled ? 2 * align256(size_t(BH) * nb * d * 4) : 0) + align256(size_t(BH) * nb * nb * 4) +
          align256(size_t(BH) * nb * words32(nb) * 4) + align256(size_t(BH) * nb * 4);
 }
 
-hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const int32_t* bvalid,
-                         int BH, int nb, int vol, int d, float scale, const prism_select_params& p,
-                         int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
-                         float* sel_margin, void* ws, hipStream_t s) {
-  SelWs w = carve(ws, BH, nb, d);
+// Scores, hybrid cut and reverse index from pooled means qbar, kbar [BH][nb][d] float32.
+static void launch_select_core(const float* qbar, const float* kbar, const int32_t* bvalid, int BH, int nb, int d,
+                               float scale, const prism_select_params& p, int32_t* sel_idx, int32_t* sel_cnt,
+                               int32_t* rev_ptr, int32_t* rev_idx, float* sel_margin, const SelWs& w, hipStream_t s) {
   const size_t nbits = size_t(BH) * nb * words32(nb);
   hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, w.bitmap, nbits, 0u);
   hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(rev_idx),
                      size_t(BH) * nb * p.k_max, 0xffffffffu);
-  // d is one of 32, 64, 128, 256 (checked by the caller)
-  if (dt == PRISM_BF16)
-    launch_pool<bf16_t>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
-  else
-    launch_pool<float>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
   const int tiles = (nb + kScT - 1) / kScT;
-  hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, w.qbar, w.kbar, bvalid, nb, d, scale,
-                     w.scores);
+  hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, qbar, kbar, bvalid, nb, d, scale, w.scores);
   // Workgroup shapes as measured fastest: 256 lanes up to 32 blocks each, then 512 lanes of
   // 32 (at 64 per lane the register file allows one wave per SIMD), then 1024 lanes of 32
   // (at most 128 registers per lane, which the kernel fits).  nb <= 1024 * 32 is checked
@@ -529,6 +529,28 @@ hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const i
   hipLaunchKernelGGL(k_rev_count, dim3((rows + 255) / 256), dim3(256), 0, s, w.bitmap, nb, rows, w.rcnt);
   hipLaunchKernelGGL(k_rev_scan, dim3(BH), dim3(1024), 0, s, w.rcnt, nb, rev_ptr);
   hipLaunchKernelGGL(k_rev_fill, dim3(nb, BH), dim3(64), 0, s, w.bitmap, rev_ptr, nb, p.k_max, rev_idx);
+}
+
+hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const int32_t* bvalid,
+                         int BH, int nb, int vol, int d, float scale, const prism_select_params& p,
+                         int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
+                         float* sel_margin, void* ws, hipStream_t s) {
+  const SelWs w = carve(ws, BH, nb, d, true);
+  // d is one of 32, 64, 128, 256 (checked by the caller)
+  if (dt == PRISM_BF16)
+    launch_pool<bf16_t>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
+  else
+    launch_pool<float>(qp, kp, bvalid, BH, nb, vol, d, w.qbar, w.kbar, s);
+  launch_select_core(w.qbar, w.kbar, bvalid, BH, nb, d, scale, p, sel_idx, sel_cnt, rev_ptr, rev_idx, sel_margin, w,
+                     s);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_pooled(const float* qbar, const float* kbar, const int32_t* bvalid, int BH, int nb, int d,
+                                float scale, const prism_select_params& p, int32_t* sel_idx, int32_t* sel_cnt,
+                                int32_t* rev_ptr, int32_t* rev_idx, float* sel_margin, void* ws, hipStream_t s) {
+  const SelWs w = carve(ws, BH, nb, d, false);
+  launch_select_core(qbar, kbar, bvalid, BH, nb, d, scale, p, sel_idx, sel_cnt, rev_ptr, rev_idx, sel_margin, w, s);
   return hipGetLastError();
 }
 

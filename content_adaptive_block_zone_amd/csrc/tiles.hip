@@ -15,7 +15,9 @@ namespace {
 constexpr int NT = 256;
 constexpr int TT = 64;  // rows per tile
 
-__device__ __forceinline__ int live_tiles(int n) { return (n + TT - 1) / TT; }
+// live tiles of a block with n valid rows, at most maxu (the most tiles a block owns;
+// counts out of range are clamped, see prism_internal.h)
+__device__ __forceinline__ int live_tiles(int n, int maxu) { return clampi((max(n, 0) + TT - 1) / TT, 0, maxu); }
 
 __global__ void k_tile_valid(const int32_t* __restrict__ bvalid, size_t total_tiles, int g,
                              int32_t* __restrict__ tvalid) {
@@ -34,14 +36,14 @@ __global__ void k_tile_valid(const int32_t* __restrict__ bvalid, size_t total_ti
 // written to every live tile of the block; with `rows_owned` > own_live also the empty
 // lists of the block's dead tiles.  Offsets come from an exclusive scan of the listed
 // blocks' live-tile counts, taken in chunks of NT with a running carry.
-__device__ void expand_rows(const int32_t* __restrict__ lst, int cnt, const int32_t* __restrict__ bv_head,
-                            int own_live, int rows_owned, int stride, int cap, int32_t* __restrict__ out_rows,
+__device__ void expand_rows(const int32_t* __restrict__ lst, int cnt, const int32_t* __restrict__ bv_head, int nb,
+                            int maxu, int own_live, int rows_owned, int stride, int cap, int32_t* __restrict__ out_rows,
                             int32_t* __restrict__ out_cnt, int* red) {
   int carry = 0;
   for (int k0 = 0; k0 < cnt; k0 += NT) {
     const int k = k0 + int(threadIdx.x);
-    const int J = k < cnt ? lst[k] : 0;
-    const int c = k < cnt ? live_tiles(bv_head[J]) : 0;
+    const int J = k < cnt ? clampi(lst[k], 0, nb - 1) : 0;
+    const int c = k < cnt ? live_tiles(bv_head[J], maxu) : 0;
     int tot;
     const int off = carry + block_excl_scan<NT>(c, red, &tot);
     for (int u = 0; u < own_live; ++u)
@@ -64,27 +66,29 @@ __global__ __launch_bounds__(NT) void k_tile_lists(const int32_t* __restrict__ b
   __shared__ int red[8];
   const int I = blockIdx.x, bh = blockIdx.y;
   const int32_t* bv = bvalid + size_t(bh) * nb;
-  const int own_live = live_tiles(bv[I]);
+  const int maxu = cap / k_max;  // tiles per block: g (fixed volume) or the largest block's units (mixed)
+  // a mixed block's tiles are the units from its first one on, inside the head
+  const int own_live = min(live_tiles(bv[I], maxu), mixed ? nb - I : stride);
   if (mixed && own_live == 0) return;  // no block starts here (or a dead one): pre-filled
-  const int cnt = own_live > 0 ? sel_cnt[size_t(bh) * nb + I] : 0;
+  const int cnt = own_live > 0 ? clampi(sel_cnt[size_t(bh) * nb + I], 0, k_max) : 0;
   const size_t t0 = size_t(bh) * nb * stride + size_t(I) * stride;
-  expand_rows(sel_idx + (size_t(bh) * nb + I) * k_max, cnt, bv, own_live, mixed ? own_live : stride, stride, cap,
-              tile_idx + t0 * cap, tile_cnt + t0, red);
+  expand_rows(sel_idx + (size_t(bh) * nb + I) * k_max, cnt, bv, nb, maxu, own_live, mixed ? own_live : stride,
+              stride, cap, tile_idx + t0 * cap, tile_cnt + t0, red);
 }
 
 // Reverse counts: key tile (J, v) is listed by every live tile of every block that selected J.
 __global__ __launch_bounds__(64) void k_tile_rev_count(const int32_t* __restrict__ bvalid,
                                                        const int32_t* __restrict__ rev_ptr,
                                                        const int32_t* __restrict__ rev_idx, int nb, int stride,
-                                                       int k_max, int mixed, int32_t* __restrict__ rcnt) {
+                                                       int k_max, int maxu, int mixed, int32_t* __restrict__ rcnt) {
   const int J = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
   const int32_t* bv = bvalid + size_t(bh) * nb;
-  const int32_t* rp = rev_ptr + size_t(bh) * (nb + 1);
-  const int32_t* ri = rev_idx + size_t(bh) * nb * k_max;
+  const RevRange rr = rev_range(rev_ptr + size_t(bh) * (nb + 1), J, nb, k_max);
+  const int32_t* ri = rev_idx + size_t(bh) * nb * k_max + rr.start;
   int c = 0;
-  for (int k = rp[J] + lane; k < rp[J + 1]; k += 64) c += live_tiles(bv[ri[k]]);
+  for (int k = lane; k < rr.cnt; k += 64) c += live_tiles(bv[clampi(ri[k], 0, nb - 1)], maxu);
   c = wave_sum_i(c);
-  const int live = live_tiles(bv[J]);
+  const int live = min(live_tiles(bv[J], maxu), mixed ? nb - J : stride);
   if (lane < (mixed ? live : stride)) rcnt[(size_t(bh) * nb + J) * stride + lane] = lane < live ? c : 0;
 }
 
@@ -114,23 +118,25 @@ __global__ __launch_bounds__(1024) void k_tile_rev_scan(const int32_t* __restric
 __global__ __launch_bounds__(NT) void k_tile_rev_fill(const int32_t* __restrict__ bvalid,
                                                       const int32_t* __restrict__ rev_ptr,
                                                       const int32_t* __restrict__ rev_idx, int nb, int stride,
-                                                      int k_max, int cap, const int32_t* __restrict__ tile_rev_ptr,
+                                                      int k_max, int maxu, int mixed, int cap,
+                                                      const int32_t* __restrict__ tile_rev_ptr,
                                                       int32_t* __restrict__ tile_rev_idx) {
   __shared__ int red[8];
   const int J = blockIdx.x, bh = blockIdx.y;
   const int32_t* bv = bvalid + size_t(bh) * nb;
-  const int32_t* rp = rev_ptr + size_t(bh) * (nb + 1);
-  const int32_t* ri = rev_idx + size_t(bh) * nb * k_max;
+  const RevRange rr = rev_range(rev_ptr + size_t(bh) * (nb + 1), J, nb, k_max);
+  const int32_t* ri = rev_idx + size_t(bh) * nb * k_max + rr.start;
   const int nt = nb * stride;
   const int32_t* trp = tile_rev_ptr + size_t(bh) * (nt + 1);
   int32_t* out = tile_rev_idx + size_t(bh) * nt * size_t(cap);
-  const int live = live_tiles(bv[J]);
-  const int k_beg = rp[J], cnt = rp[J + 1] - rp[J];
+  // the same clamps as k_tile_rev_count, so that the fill stays inside the counted ranges
+  const int live = min(live_tiles(bv[J], maxu), mixed ? nb - J : stride);
+  const int cnt = rr.cnt;
   int carry = 0;
   for (int k0 = 0; k0 < cnt; k0 += NT) {
     const int k = k0 + int(threadIdx.x);
-    const int I = k < cnt ? ri[k_beg + k] : 0;
-    const int c = k < cnt ? live_tiles(bv[I]) : 0;
+    const int I = k < cnt ? clampi(ri[k], 0, nb - 1) : 0;
+    const int c = k < cnt ? live_tiles(bv[I], maxu) : 0;
     int tot;
     const int off = carry + block_excl_scan<NT>(c, red, &tot);
     for (int v = 0; v < live; ++v) {
@@ -157,9 +163,10 @@ hipError_t launch_blocks_to_tiles(const int32_t* bvalid, const int32_t* sel_idx,
   hipLaunchKernelGGL(k_tile_valid, dim3(unsigned((total + 255) / 256)), dim3(256), 0, s, bvalid, total, g, tile_valid);
   hipLaunchKernelGGL(k_tile_lists, dim3(nb, BH), dim3(NT), 0, s, bvalid, sel_idx, sel_cnt, nb, g, k_max, cap, 0,
                      tile_idx, tile_cnt);
-  hipLaunchKernelGGL(k_tile_rev_count, dim3(nb, BH), dim3(64), 0, s, bvalid, rev_ptr, rev_idx, nb, g, k_max, 0, rcnt);
+  hipLaunchKernelGGL(k_tile_rev_count, dim3(nb, BH), dim3(64), 0, s, bvalid, rev_ptr, rev_idx, nb, g, k_max, g, 0,
+                     rcnt);
   hipLaunchKernelGGL(k_tile_rev_scan, dim3(BH), dim3(1024), 0, s, rcnt, nt, tile_rev_ptr);
-  hipLaunchKernelGGL(k_tile_rev_fill, dim3(nb, BH), dim3(NT), 0, s, bvalid, rev_ptr, rev_idx, nb, g, k_max, cap,
+  hipLaunchKernelGGL(k_tile_rev_fill, dim3(nb, BH), dim3(NT), 0, s, bvalid, rev_ptr, rev_idx, nb, g, k_max, g, 0, cap,
                      tile_rev_ptr, tile_rev_idx);
   return hipGetLastError();
 }
@@ -178,11 +185,11 @@ hipError_t launch_blocks_to_tiles_mixed(const int32_t* block_valid, const int32_
   hipLaunchKernelGGL(k_fill_i32, dim3(256), dim3(256), 0, s, rcnt, total, 0);
   hipLaunchKernelGGL(k_tile_lists, dim3(nb, BH), dim3(NT), 0, s, block_valid, sel_idx, sel_cnt, nb, 1, k_max, cap, 1,
                      tile_idx, tile_cnt);
-  hipLaunchKernelGGL(k_tile_rev_count, dim3(nb, BH), dim3(64), 0, s, block_valid, rev_ptr, rev_idx, nb, 1, k_max, 1,
-                     rcnt);
+  hipLaunchKernelGGL(k_tile_rev_count, dim3(nb, BH), dim3(64), 0, s, block_valid, rev_ptr, rev_idx, nb, 1, k_max,
+                     max_units, 1, rcnt);
   hipLaunchKernelGGL(k_tile_rev_scan, dim3(BH), dim3(1024), 0, s, rcnt, nb, tile_rev_ptr);
-  hipLaunchKernelGGL(k_tile_rev_fill, dim3(nb, BH), dim3(NT), 0, s, block_valid, rev_ptr, rev_idx, nb, 1, k_max, cap,
-                     tile_rev_ptr, tile_rev_idx);
+  hipLaunchKernelGGL(k_tile_rev_fill, dim3(nb, BH), dim3(NT), 0, s, block_valid, rev_ptr, rev_idx, nb, 1, k_max,
+                     max_units, 1, cap, tile_rev_ptr, tile_rev_idx);
   return hipGetLastError();
 }
 

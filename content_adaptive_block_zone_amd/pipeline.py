@@ -88,11 +88,21 @@ class PrismLayer:
         self.sel_margin = e(B_, H_, self.nb, dt=f32)
         self.rev_ptr = e(B_, H_, self.nb + 1, dt=i32)
         self.rev_idx = e(B_, H_, self.nb * self.k_max, dt=i32)
-        self.ws_sel = e(api.prism_select_workspace_size(B, Hh, self.nb, d), dt=torch.uint8)
+        # Uniform block volume: pooling is fused into the permutation of Q and K
+        # (prism_permute_pool) and the selection starts from the pooled means.  Mixed volumes
+        # pool whole blocks that span several units, inside prism_select_blocks.
+        self.fused_pool = mixed is None
+        if self.fused_pool:
+            self.qbar = e(B_, H_, self.nb, d, dt=f32)
+            self.kbar = e(B_, H_, self.nb, d, dt=f32)
+            self.ws_sel = e(api.prism_select_pooled_workspace_size(B, Hh, self.nb), dt=torch.uint8)
+        else:
+            self.ws_sel = e(api.prism_select_workspace_size(B, Hh, self.nb, d), dt=torch.uint8)
         self.ws_fwd = e(max(1, api.prism_fwd_workspace_size(B, Hh, self.nb, self.vol, d, dtype)), dt=torch.uint8)
         self.ws_bwd = e(api.prism_bwd_workspace_size(B, Hh, self.nb, self.vol, d, dtype), dt=torch.uint8)
         self.o = e(B_, H_, self.N, d)
         self._grad_bufs = None
+        self._ws_sel_slots = None
         # Blocks of more than 64 tokens run the attention on 64-row tiles (vol/64 per block).
         self.g = self.vol // 64 if self.vol > 64 else 1
         if self.mixed is not None:
@@ -162,22 +172,40 @@ class PrismLayer:
                                 self.shape_margin)
 
     def permute_qkv(self, q, k, v):
-        """Q, K, V into slot order; block_valid (block heads, when volumes are mixed) from Q's pass."""
+        """Q, K, V into slot order; block_valid (block heads, when volumes are mixed) from Q's
+        pass; with a uniform volume also the pooled means of Q and K."""
         if self.mixed is not None:
             self.permute(q, self.qp, block_valid=self.unit_valid)
             api.prism_block_heads(self.unit_valid, self.shape_id, self.grid, self.shapes, self.bvalid)
+            self.permute(k, self.kp)
         else:
-            self.permute(q, self.qp, block_valid=self.bvalid)
-        self.permute(k, self.kp)
+            api.prism_permute_pool(q, self.qp, self.grid, self.shapes, self.shape_id, self.qbar, self.bvalid)
+            api.prism_permute_pool(k, self.kp, self.grid, self.shapes, self.shape_id, self.kbar)
         self.permute(v, self.vp)
 
     def permute(self, x, y, inverse=False, block_valid=None):
         api.prism_permute(x, y, self.grid, self.shapes, self.shape_id, inverse, block_valid)
 
-    def select(self):
-        api.prism_select_blocks(self.qp, self.kp, self.bvalid, self.vol, self.scale, self.sel_params,
-                                self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.ws_sel,
-                                self.sel_margin)
+    def select(self, from_slots: bool = False):
+        """Scores, hybrid cut and reverse index.  With a uniform volume this starts from the
+        pooled means that permute_qkv wrote (qbar, kbar); from_slots=True pools Q' and K'
+        inside the selection instead (prism_select_blocks), for Q' and K' filled by other
+        means."""
+        if from_slots and self.fused_pool:
+            if getattr(self, "_ws_sel_slots", None) is None:
+                self._ws_sel_slots = torch.empty(api.prism_select_workspace_size(self.B, self.Hh, self.nb, self.d),
+                                                 dtype=torch.uint8, device=self.device)
+            api.prism_select_blocks(self.qp, self.kp, self.bvalid, self.vol, self.scale, self.sel_params,
+                                    self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self._ws_sel_slots,
+                                    self.sel_margin)
+        elif self.fused_pool:
+            api.prism_select_blocks_pooled(self.qbar, self.kbar, self.bvalid, self.scale, self.sel_params,
+                                           self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.ws_sel,
+                                           self.sel_margin)
+        else:
+            api.prism_select_blocks(self.qp, self.kp, self.bvalid, self.vol, self.scale, self.sel_params,
+                                    self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx, self.ws_sel,
+                                    self.sel_margin)
         if self.mixed is not None:
             api.prism_blocks_to_tiles_mixed(self.bvalid, self.sel_idx, self.sel_cnt, self.rev_ptr, self.rev_idx,
                                             self.max_units, self.tile_idx, self.tile_cnt, self.tile_rev_ptr,

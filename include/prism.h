@@ -84,7 +84,8 @@ typedef struct {
 /* Hybrid selection (Table 7 caption): the Top-p count is the smallest number of key
  * blocks whose cumulative pooled attention weight strictly exceeds top_p, then clamped
  * to [k_min, k_max] and to the number of live key blocks.  0 < top_p <= 1,
- * 1 <= k_min <= k_max. */
+ * 1 <= k_min <= k_max.  top_p = 1 keeps every live block before the clamp (the weights
+ * sum to 1, so no proper prefix exceeds it, whatever the float32 rounding of the sum). */
 typedef struct {
   float top_p;
   int32_t k_min, k_max;
@@ -188,11 +189,27 @@ prism_status prism_block_heads(const int32_t* unit_valid, const int32_t* shape_i
  * inverse == 0: x [B][Hh][N][d] -> y [B][Hh][Npad][d], zeros at padding slots.
  * inverse == 1: x [B][Hh][Npad][d] -> y [B][Hh][N][d], padding slots dropped.
  * block_valid optional out int32 [B][Hh][nb]: valid slots per block (0 = dead block).
+ * shape_id  int32 [B][Hh][nZ] device array, each entry the index of a candidate that tiles
+ *           the zone (as prism_assign_shapes writes).  This is not checked on the host; a
+ *           zone whose id is out of range or names a candidate that does not tile it maps no
+ *           token: its slots are written as padding (forward), its tokens are left as they
+ *           were (inverse), and its blocks get block_valid 0.
  * Requires d * sizeof(dtype) % 16 == 0. */
 prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int Hh, int d,
                            const prism_grid* grid, const prism_shapes* shapes,
                            const int32_t* shape_id, int inverse, int32_t* block_valid,
                            hipStream_t stream);
+
+/* Forward permutation fused with the block pooling of the selection (abstract:
+ * block-level features): prism_permute(..., inverse = 0, block_valid) that also writes
+ * pooled  out float [B][Hh][nb][d]: the mean of each block's valid rows, summed in float32
+ *         (0 for a dead block),
+ * the input of prism_select_blocks_pooled.  Every candidate must hold shapes->vol tokens
+ * (PRISM_ERR_SHAPE otherwise) and d * sizeof(dtype) must be 16 bytes times a power of two
+ * up to 4096 bytes (PRISM_ERR_DTYPE).  block_valid may be NULL. */
+prism_status prism_permute_pool(const void* x, void* y, prism_dtype dtype, int B, int Hh, int d,
+                                const prism_grid* grid, const prism_shapes* shapes, const int32_t* shape_id,
+                                int32_t* block_valid, float* pooled, hipStream_t stream);
 
 /* (a4, a5) Block pooling and hybrid Top-k/Top-p selection (abstract; Figure 2 caption;
  * Table 7 caption).
@@ -215,6 +232,16 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
                                  int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
                                  float* sel_margin, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* prism_select_blocks from pooled means given by the caller (prism_permute_pool of Q and
+ * K): qbar, kbar float [B][Hh][nb][d], d a multiple of 16 up to 4096.  Outputs, parameters
+ * and errors as prism_select_blocks; workspace: prism_select_pooled_workspace_size() bytes
+ * (the pooled means are not part of it). */
+size_t prism_select_pooled_workspace_size(int B, int Hh, int nb);
+prism_status prism_select_blocks_pooled(const float* qbar, const float* kbar, const int32_t* block_valid, int B,
+                                        int Hh, int nb, int d, float scale, const prism_select_params* params,
+                                        int32_t* sel_idx, int32_t* sel_cnt, int32_t* rev_ptr, int32_t* rev_idx,
+                                        float* sel_margin, void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* Blocks of 128 or 256 tokens (the C_128 / C_256 candidate sets, Tables 9 and 11) run
  * through the attention as runs of vol/64 consecutive 64-row tiles.  This call expands a
@@ -249,6 +276,19 @@ prism_status prism_blocks_to_tiles_mixed(const int32_t* block_valid, const int32
                                          int k_max, int max_units, int32_t* tile_idx, int32_t* tile_cnt,
                                          int32_t* tile_rev_ptr, int32_t* tile_rev_idx, void* workspace,
                                          size_t ws_bytes, hipStream_t stream);
+
+/* Preconditions on the device lists of the attention calls (as prism_select_blocks and
+ * prism_blocks_to_tiles write them; they are device data and are not read on the host):
+ *   block_valid[I] in [0, vol];
+ *   sel_cnt[I] in [0, k_max]; sel_idx[I][0:sel_cnt[I]] distinct block indices in [0, nb),
+ *     ascending;
+ *   rev_ptr[0] = 0, rev_ptr non-decreasing, rev_ptr[nb] <= nb * k_max; rev_idx[rev_ptr[J] :
+ *     rev_ptr[J+1]] distinct query blocks in [0, nb), ascending, and exactly the query
+ *     blocks whose sel_idx row holds J.
+ * The kernels clamp every count, pointer and index into its range before using it, so a
+ * malformed list cannot make them read or write outside the caller's buffers; the results
+ * are then unspecified.  Ascending order is what the kernels' workgroup schedule and cache
+ * reuse assume; any order gives the same results up to float32 summation order. */
 
 /* Block-sparse attention forward (Figure 2 caption).  Query row i of block I attends
  * to every valid row of every block in sel_idx[I][0:sel_cnt[I]]:

@@ -97,3 +97,35 @@ def check_reverse_is_transpose(idx, cnt, rev_ptr, rev_idx):
             assert [I for (_, I) in pairs] == lst.tolist()
             counts = np.bincount(np.array([J for (J, _) in pairs], dtype=np.int64), minlength=nb)
             assert (np.diff(rp) == counts).all()
+
+
+def oracle_fwd_blocks(qp, kp, vp, bv, sel, scale, vol, blocks, threads=None):
+    """The oracle's sparse forward on the listed query blocks, the blocks split over a
+    thread pool (one BLAS thread per call; the oracle's arithmetic is unchanged, each block
+    is computed by one O.sparse_attn_fwd call exactly as in a serial run).  Returns O' and
+    LSE of full shape with the listed blocks' rows filled, zeros elsewhere."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import threadpoolctl
+    blocks = sorted(blocks)
+    # widen once here (bf16 and float32 values are exact in float64), so that the calls
+    # below do not each convert the whole tensors
+    qp, kp, vp = (np.asarray(a, dtype=np.float64) for a in (qp, kp, vp))
+    nt = max(1, min(threads or os.cpu_count() or 1, 16, len(blocks) or 1))
+    chunks = [blocks[i::nt] for i in range(nt)]
+    B, Hh, Np, _ = qp.shape
+    O_ = np.zeros((B, Hh, Np, vp.shape[-1]))
+    L_ = np.zeros((B, Hh, Np))
+
+    def run(chunk):
+        o, l = O.sparse_attn_fwd(qp, kp, vp, bv, sel, scale, vol, blocks=chunk)
+        return chunk, o, l
+
+    with threadpoolctl.threadpool_limits(1):
+        with ThreadPoolExecutor(nt) as ex:
+            for chunk, o, l in ex.map(run, chunks):
+                for (b, h, I) in chunk:
+                    rs = slice(I * vol, (I + 1) * vol)
+                    O_[b, h, rs] = o[b, h, rs]
+                    L_[b, h, rs] = l[b, h, rs]
+    return O_, L_

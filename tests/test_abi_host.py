@@ -161,6 +161,20 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_ARG),
         ("prism_dense_attn_bwd", (P, P, P, P, P, P, F32, 1, 2, 256, 64, float("nan"), P, P, P, P, 1 << 30,
                                   None, None), E.PRISM_ERR_ARG),
+        ("prism_permute_pool", (P, P, F32, 1, 2, 64, g, s, P, None, None, None), E.PRISM_ERR_ARG),   # no pooled
+        ("prism_permute_pool", (P, P, BF16, 1, 2, 24, g, s, P, None, P, None), E.PRISM_ERR_DTYPE),  # 48-byte rows
+        ("prism_permute_pool", (P, P, F32, 1, 2, 64, g, s, P, None, P, None), E.PRISM_ERR_ARG),     # x aliases y
+        ("prism_permute_pool", (P, ctypes.c_void_p(128), F32, 1, 2, 64, g,
+                                api.make_shapes([(1, 4, 4), (2, 4, 4)], unit=16), P, None, P, None),
+         E.PRISM_ERR_SHAPE),                                                           # mixed volumes
+        ("prism_select_blocks_pooled", (P, P, P, 1, 2, 16, 64, 0.125, api.make_select_params(1.5, 2, 8), P, P, P,
+                                        P, None, P, 1 << 30, None), E.PRISM_ERR_ARG),
+        ("prism_select_blocks_pooled", (P, P, P, 1, 2, 16, 60, 0.125, sel, P, P, P, P, None, P, 1 << 30, None),
+         E.PRISM_ERR_DTYPE),                                                           # d not a multiple of 16
+        ("prism_select_blocks_pooled", (P, P, P, 1, 2, 16, 64, 0.125, sel, P, P, P, P, None, P, 8, None),
+         E.PRISM_ERR_ARG),                                                             # workspace too small
+        ("prism_select_blocks_pooled", (P, P, P, 1, 2, 32769, 64, 0.125, sel, P, P, P, P, None, P, 1 << 44, None),
+         E.PRISM_ERR_SHAPE),
     ]
     for name, args, want in cases:
         st = getattr(lib, name)(*args)

@@ -141,7 +141,7 @@ def test_single_criterion_selection(mode):
     L.qp.copy_(dev(f["qp"], torch.bfloat16))
     L.kp.copy_(dev(f["kp"], torch.bfloat16))
     L.bvalid.copy_(torch.from_numpy(f["bvalid"]))
-    L.select()
+    L.select(from_slots=True)
     sel, near = O.select_blocks(f["qbar"].astype(np.float32), f["kbar"].astype(np.float32), f["bvalid"],
                                 1.0 / math.sqrt(w.d), kw["top_p"], kw["k_min"], kw["k_max"])
     idx, cnt = i32(L.sel_idx), i32(L.sel_cnt)

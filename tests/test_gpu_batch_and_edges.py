@@ -99,3 +99,21 @@ def test_tiny_top_p_falls_back_to_k_min():
     bad = [k for k in sel if got[k].tolist() != sel[k].tolist() and not near[k]]
     log(f"[edges] tiny p: {len(bad)} hard mismatches of {len(sel)} rows")
     assert not bad
+
+
+def test_top_p_one_keeps_every_live_block():
+    """Top-p = 1 with a small Top-k floor keeps every live key block of every live row
+    (reading of the Table 7 rule at p = 1), whatever the float32 total of the row."""
+    w, x, n = batch_case()
+    from content_adaptive_block_zone_amd.pipeline import PrismLayer
+    L = PrismLayer.for_workload(w, top_p=1.0, k_min=1, k_max=256)
+    L.forward(x["q"].cuda(), x["k"].cuda(), x["v"].cuda(), x["a2v"].cuda())
+    torch.cuda.synchronize()
+    bv = i32(L.bvalid)
+    idx, cnt = i32(L.sel_idx), i32(L.sel_cnt)
+    for b in range(w.B):
+        for h in range(w.heads):
+            live = np.nonzero(bv[b, h] > 0)[0]
+            for I in range(bv.shape[-1]):
+                want = live.tolist() if bv[b, h, I] > 0 else []
+                assert idx[b, h, I, :cnt[b, h, I]].tolist() == want

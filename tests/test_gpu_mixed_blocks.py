@@ -94,7 +94,7 @@ def test_mixed_tile_lists():
     L.kp.copy_(dev(f["kp"], torch.bfloat16))
     L.bvalid.copy_(torch.from_numpy(f["bvalid"]))
     L.unit_valid.copy_(torch.from_numpy(O.block_valid(f["tok"], 64)))
-    L.select()
+    L.select(from_slots=True)
     bv, idx, cnt = i32(L.bvalid), i32(L.sel_idx), i32(L.sel_cnt)
     live = lambda nn: (int(nn) + 63) // 64  # noqa: E731
     tidx, tcnt = i32(L.tile_idx), i32(L.tile_cnt)

@@ -100,6 +100,34 @@ def test_permute_roundtrip(i):
 
 
 @pytest.mark.parametrize("i", CASES)
+def test_permute_pool(i):
+    """The permutation fused with pooling: the same slot-order tensors as prism_permute, and
+    block means equal to the oracle's element by element (float32 sums of at most 64
+    rows); then the selection from those means against the oracle's."""
+    w, x = inputs(i)
+    f = oracle_chain(i)
+    L = layer(i)
+    L.shape_id.copy_(torch.from_numpy(f["shape_id"]))
+    L.permute_qkv(x["q"].cuda(), x["k"].cuda(), x["v"].cuda())
+    assert (i32(L.bvalid) == f["bvalid"]).all()
+    for key, buf in (("qp", L.qp), ("kp", L.kp), ("vp", L.vp)):
+        assert (f64(buf) == f[key]).all(), key
+    for name, got, want in (("Qbar", L.qbar, f["qbar"]), ("Kbar", L.kbar, f["kbar"])):
+        err = float(np.abs(f64(got) - want).max())
+        log(f"[pool] workload {i} {name}: max-abs {err:.3e}")
+        assert err <= 1e-5
+    # the selection from the oracle's pooled means (the precision its cut uses)
+    L.qbar.copy_(torch.from_numpy(f["qbar"].astype(np.float32)))
+    L.kbar.copy_(torch.from_numpy(f["kbar"].astype(np.float32)))
+    L.select()
+    idx, cnt = i32(L.sel_idx), i32(L.sel_cnt)
+    bad = sum(1 for (b, h, I), want in f["sel"].items()
+              if idx[b, h, I, :cnt[b, h, I]].tolist() != want.tolist() and not f["sel_near"][(b, h, I)])
+    assert bad == 0
+    check_reverse_is_transpose(idx, cnt, i32(L.rev_ptr), i32(L.rev_idx))
+
+
+@pytest.mark.parametrize("i", CASES)
 def test_select_blocks(i):
     w, _ = inputs(i)
     f = oracle_chain(i)
@@ -108,7 +136,7 @@ def test_select_blocks(i):
     L.qp.copy_(dev(f["qp"], dt))
     L.kp.copy_(dev(f["kp"], dt))
     L.bvalid.copy_(torch.from_numpy(f["bvalid"]))
-    L.select()
+    L.select(from_slots=True)
     idx, cnt = i32(L.sel_idx), i32(L.sel_cnt)
     rp, ri = i32(L.rev_ptr), i32(L.rev_idx)
     B, Hh, nb = cnt.shape

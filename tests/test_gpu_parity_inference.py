@@ -98,7 +98,7 @@ def test_inference_select_sampled_rows():
     L.qp.copy_(dev(c["qp"], torch.bfloat16))
     L.kp.copy_(dev(c["kp"], torch.bfloat16))
     L.bvalid.copy_(torch.from_numpy(c["bv"]))
-    L.select()
+    L.select(from_slots=True)
     idx, cnt = i32(L.sel_idx), i32(L.sel_cnt)
     bad = near_bad = 0
     for (b, h, I), want in c["sel"].items():
