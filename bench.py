@@ -205,6 +205,70 @@ def density(L):
     return float(per_head.mean().item())
 
 
+MFMA_PER_PAIR = {"sparse_attn_fwd": 96, "sparse_attn_bwd_dkdv": 128, "sparse_attn_bwd_dq": 96}
+"""v_mfma_f32_32x32x16_bf16 products (32768 flops each) issued per selected 64x64 block pair:
+forward 2 x 32 (S, then P V with P as a bf16 head and remainder: 64), dK/dV 128 (S, dP,
+dV, dK), dQ 96 (S and dP recomputed, then dQ)."""
+
+
+def flush_cache(buf):
+    """Overwrite a buffer twice the size of the 256 MB last-level cache, so that the next
+    kernel reads its inputs from HBM as it does inside the layer."""
+    buf.zero_()
+
+
+def time_stages(L, calls, reps, flush_buf):
+    """Per-stage GPU time: each stage enqueued `reps` times, each run preceded by a cache
+    flush and bracketed by its own pair of events on the launch stream; the median over
+    runs.  The host enqueues everything before synchronising once, so the GPU runs the
+    work back to back and the events see kernel time, not host launch latency."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = {}
+    for name, fn in calls:
+        evs = []
+        for _ in range(reps):
+            flush_cache(flush_buf)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        out[name] = round(t[len(t) // 2], 4)
+    return out
+
+
+def mfma_peak(dev, reps=3):
+    """The project's own matrix-core loop (prism_bench_mfma_peak): 512 workgroups of 4
+    waves (2 per SIMD), four independent 32x32x16 bf16 products per wave and step.
+    Returns (best TFLOP/s, mean shader clock in MHz over that run)."""
+    import torch
+
+    from content_adaptive_block_zone_amd import api
+    wgs, iters = 512, 4096
+    clocks = torch.zeros(wgs, 2, dtype=torch.int64, device=dev)
+    sink = torch.zeros(wgs, dtype=torch.float32, device=dev)
+    api.prism_bench_mfma_peak(wgs, 64, clocks, sink)       # warm-up
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        api.prism_bench_mfma_peak(wgs, iters, clocks, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        tf = wgs * 4 * iters * 4 * 32768 / (ms * 1e-3) / 1e12
+        c = clocks.double().cpu()
+        mhz = float((c[:, 0] / c[:, 1].clamp(min=1)).mean()) * 100.0
+        if best is None or tf > best[0]:
+            best = (tf, mhz)
+    return round(best[0], 1), round(best[1], 1)
+
+
 def run_gpu(args):
     import torch
 
@@ -310,45 +374,66 @@ def run_gpu(args):
     value = f_sel / (ms_step * 1e-3) / 1e12
     t_attn = t_fwd + t_pre + t_dkdv + t_dq
     attn_tflops = f_sel / (t_attn * 1e-3) / 1e12
+    # tile flops: every selected pair counted as a whole 64 x 64 tile pair, padding included
+    f_tile = (4.0 if fwd_only else 14.0) * d * 64 * 64 * sums["block_pairs"]
+    f_dense_eq = (4.0 if fwd_only else 14.0) * d * w.N * w.N * w.B * w.heads
 
-    # dominant kernel: the one with the largest share of the step.  At about 64 flop per
-    # streamed byte these kernels sit far below MI355X's ridge point (2.5 PFLOP/s / 8 TB/s
-    # = 312 flop/B), so their roofline is HBM bandwidth on algorithmic bytes.
+    # Roofline: the attention kernels are priced on the bf16 matrix-core peak, each on its
+    # own algorithmic flops (forward 4d, dK/dV 8d, dQ 2d per valid token pair); the
+    # dominant kernel is the one that takes longest.
     kb = kernel_bytes(sums, d)
     kern = {"sparse_attn_fwd": t_fwd, "sparse_attn_bwd_dkdv": t_dkdv, "sparse_attn_bwd_dq": t_dq}
     if fwd_only:
         kern = {"sparse_attn_fwd": t_fwd}
-    dom = max(kern, key=lambda n: kern[n])
-    t_dom = kern[dom]
-    achieved = kb[dom] / (t_dom * 1e-3) / 1e9
     kflops = {"sparse_attn_fwd": 4.0 * d * pairs, "sparse_attn_bwd_dkdv": 8.0 * d * pairs,
               "sparse_attn_bwd_dq": 2.0 * d * pairs}
+    dom = max(kern, key=lambda n: kern[n])
+    t_dom = kern[dom]
+    achieved = kflops[dom] / (t_dom * 1e-3) / 1e12
 
-    # per-stage breakdown from one extra instrumented pass (outside the timed region)
-    stage = {}
-    names = ["zone_stats", "assign_shapes", "permute_qkv", "select", "attn_fwd", "unpermute_o", "permute_do",
-             "attn_bwd", "unpermute_grads"]
-    calls = [lambda: L.zone_stats(feat, a2v) if shape_ids is None else L.shape_id.copy_(shape_ids),
-             lambda: L.assign_shapes() if shape_ids is None else None,
-             lambda: L.permute_qkv(q, k, v),
-             L.select, L.attn_fwd, lambda: L.permute(L.op, L.o, inverse=True)]
-    if fwd_only:
-        names = names[:len(calls)]
-    else:
+    # per-stage kernel time, cold cache, queued back to back (outside the timed region)
+    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    calls = [("zone_stats", lambda: L.zone_stats(feat, a2v) if shape_ids is None else L.shape_id.copy_(shape_ids)),
+             ("assign_shapes", lambda: L.assign_shapes() if shape_ids is None else None),
+             ("permute_pool_qkv", lambda: L.permute_qkv(q, k, v)),
+             ("select", L.select), ("attn_fwd", L.attn_fwd),
+             ("unpermute_o", lambda: L.permute(L.op, L.o, inverse=True))]
+    if not fwd_only:
         g = L._grads()
-        calls += [lambda: L.permute(do, g["dop"]), L.attn_bwd,
-                  lambda: (L.permute(g["dqp"], g["dq"], inverse=True), L.permute(g["dkp"], g["dk"], inverse=True),
-                           L.permute(g["dvp"], g["dv"], inverse=True))]
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
-    ev[0].record(stream)
-    for i, c in enumerate(calls):
-        c()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    for i, n in enumerate(names):
-        stage[n] = round(ev[i].elapsed_time(ev[i + 1]), 4)
+        calls += [("permute_do", lambda: L.permute(do, g["dop"])), ("attn_bwd", L.attn_bwd),
+                  ("unpermute_grads", lambda: (L.permute(g["dqp"], g["dq"], inverse=True),
+                                               L.permute(g["dkp"], g["dk"], inverse=True),
+                                               L.permute(g["dvp"], g["dv"], inverse=True)))]
+    stage = time_stages(L, calls, args.stage_reps, flush_buf)
+    log(f"[bench] stages (ms, cold cache): {stage}")
+    del flush_buf
 
-    # dense comparator on the same (unpermuted) inputs
+    # measured ceilings: the matrix-core peak and clock, and the forward's tile traffic alone
+    ceil = None
+    if not args.no_microbench:
+        pk, mhz = mfma_peak(dev)
+        gop = torch.empty_like(L.op)
+        bv_t, idx_t, cnt_t, _, _, vol_t = L._attn_lists()
+        api.prism_bench_tile_gather(L.qp, L.kp, L.vp, bv_t, idx_t, cnt_t, vol_t, gop, L.ws_fwd)
+        torch.cuda.synchronize()
+        gt = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            api.prism_bench_tile_gather(L.qp, L.kp, L.vp, bv_t, idx_t, cnt_t, vol_t, gop, L.ws_fwd)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gt.append(e0.elapsed_time(e1))
+        del gop
+        g_ms = sorted(gt)[1]
+        ceil = dict(mfma_peak_tflops=pk, mfma_peak_frac_of_spec=round(pk / MI355X_BF16_DENSE_TFLOPS, 4),
+                    shader_clock_mhz=mhz,
+                    fwd_tile_gather_ms=round(g_ms, 4),
+                    fwd_tile_gather_gbps=round(kb["sparse_attn_fwd"] / (g_ms * 1e-3) / 1e9, 1),
+                    fwd_over_gather=round(t_fwd / g_ms, 3))
+        log(f"[bench] ceilings: {ceil}")
+
+    # dense comparator on the same (unpermuted) inputs, per kernel
     dense = None
     if not args.no_dense:
         o_d = torch.empty_like(q)
@@ -359,24 +444,45 @@ def run_gpu(args):
             dq_d, dk_d, dv_d = (torch.empty_like(q) for _ in range(3))
             ws = torch.empty(api.prism_dense_bwd_workspace_size(w.B, w.heads, w.N, w.d), dtype=torch.uint8,
                              device=dev)
+        mk = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        for m in mk:
+            m.record(stream)
 
-        def dense_step():
+        def dense_step(marks=None):
             api.prism_dense_attn_fwd(q, k, v, L.scale, o_d, lse_d, wsf)
             if not fwd_only:
-                api.prism_dense_attn_bwd(q, k, v, o_d, do, lse_d, L.scale, dq_d, dk_d, dv_d, ws)
+                api.prism_dense_attn_bwd(q, k, v, o_d, do, lse_d, L.scale, dq_d, dk_d, dv_d, ws, marks)
 
         dense_step()
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        for _ in range(args.dense_steps):
-            dense_step()
-        e1.record(stream)
+        dense_step(mk)
         torch.cuda.synchronize()
-        dense_ms = e0.elapsed_time(e1) / args.dense_steps
-        dflops = (4.0 if fwd_only else 14.0) * d * w.N * w.N * w.B * w.heads
-        dense = dict(ms=round(dense_ms, 3), tflops=round(dflops / (dense_ms * 1e-3) / 1e12, 2),
-                     speedup=round(dense_ms / ms_step, 3))
+        dense_ms = e0.elapsed_time(mk[3]) if not fwd_only else None
+        dfl = d * w.N * w.N * w.B * w.heads
+        if fwd_only:
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            dense_step()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            dense_ms = e0.elapsed_time(e1)
+            dk_ms = {"fwd": dense_ms}
+        else:
+            dk_ms = {"fwd": e0.elapsed_time(mk[0]), "bwd_pre": mk[0].elapsed_time(mk[1]),
+                     "bwd_dkdv": mk[1].elapsed_time(mk[2]), "bwd_dq": mk[2].elapsed_time(mk[3])}
+        dflops = {"fwd": 4.0 * dfl, "bwd_dkdv": 8.0 * dfl, "bwd_dq": 2.0 * dfl}
+        tot_fl = (4.0 if fwd_only else 14.0) * dfl
+        dense = dict(ms=round(dense_ms, 3), tflops=round(tot_fl / (dense_ms * 1e-3) / 1e12, 2),
+                     mfma_frac=round(tot_fl / (dense_ms * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4),
+                     speedup=round(dense_ms / ms_step, 3),
+                     kernels={n: dict(ms=round(t, 3),
+                                      **({} if n not in dflops else dict(
+                                          tflops=round(dflops[n] / (t * 1e-3) / 1e12, 1),
+                                          mfma_frac=round(dflops[n] / (t * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS,
+                                                          4))))
+                              for n, t in dk_ms.items()})
         log(f"[bench] dense comparator: {dense}")
 
     res = dict(
@@ -393,61 +499,108 @@ def run_gpu(args):
                     **({"ablation": args.ablation} if args.ablation else {})),
         ms_per_layer=round(ms_step, 3),
         attn_tflops=round(attn_tflops, 3),
+        tile_tflops=round(f_tile / (ms_step * 1e-3) / 1e12, 3),
+        dense_equivalent_tflops=round(f_dense_eq / (ms_step * 1e-3) / 1e12, 3),
         attn_ms=dict(fwd=round(t_fwd, 4), bwd_pre=round(t_pre, 4), bwd_dkdv=round(t_dkdv, 4), bwd_dq=round(t_dq, 4)),
         select_ms=round(t_select, 4),
         stage_ms=stage,
         dense=dense,
         speedup_vs_dense=None if dense is None else dense["speedup"],
-        roofline=dict(bound="hbm", kernel=dom, achieved=round(achieved, 1), peak=MI355X_HBM_GBPS, unit="GB/s",
-                      frac=round(achieved / MI355X_HBM_GBPS, 4), traffic=recorded_traffic(dom), avg_ms=round(t_dom, 4),
-                      bytes_per_launch=kb[dom],
-                      mfma_tflops=round(kflops[dom] / (t_dom * 1e-3) / 1e12, 2),
-                      mfma_frac=round(kflops[dom] / (t_dom * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4)),
-        kernels={n: dict(ms=round(kern[n], 4), gbps=round(kb[n] / (kern[n] * 1e-3) / 1e9, 1),
-                         frac_hbm=round(kb[n] / (kern[n] * 1e-3) / 1e9 / MI355X_HBM_GBPS, 4)) for n in kern},
+        roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=MI355X_BF16_DENSE_TFLOPS,
+                      unit="TFLOP/s", frac=round(achieved / MI355X_BF16_DENSE_TFLOPS, 4),
+                      traffic=recorded_traffic(dom), avg_ms=round(t_dom, 4), flops_per_launch=kflops[dom],
+                      attn_achieved=round(attn_tflops, 2),
+                      attn_frac=round(attn_tflops / MI355X_BF16_DENSE_TFLOPS, 4),
+                      traffic_model_gbps=round(kb[dom] / (t_dom * 1e-3) / 1e9, 1)),
+        ceilings=ceil,
+        kernels={n: dict(ms=round(kern[n], 4), tflops=round(kflops[n] / (kern[n] * 1e-3) / 1e12, 2),
+                         mfma_frac=round(kflops[n] / (kern[n] * 1e-3) / 1e12 / MI355X_BF16_DENSE_TFLOPS, 4),
+                         mfma_issued_tflops=round(MFMA_PER_PAIR[n] * 32768.0 * sums["block_pairs"] /
+                                                  (kern[n] * 1e-3) / 1e12, 2),
+                         traffic_model_gbps=round(kb[n] / (kern[n] * 1e-3) / 1e9, 1)) for n in kern},
     )
     return res, (w, x)
 
 
-def cpu_baseline(w, x, budget_blocks: int, fwd_only: bool = False):
-    """The oracle as it stands, on one head of the same inputs: the whole chain for that
-    head with the attention restricted to `budget_blocks` query blocks (forward, and
-    unless fwd_only the full backward of exactly those blocks' selected pairs)."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x, n_blocks: int, fwd_only: bool = False):
+    """The oracle in float32 (its timing precision) on the host cores, every BLAS thread
+    in use, over a bounded sample of the same workload, extrapolated to the whole layer.
+
+    Sample: head 0 (the heads are alike in size and density) -- zone statistics, shapes,
+    permutation of Q, K, V, pooling and the whole head's selection in full; the forward
+    and dQ of n_blocks sampled query blocks; dK/dV of n_blocks sampled key blocks (their
+    O' and LSE inputs are placeholders for the rows outside the sample: the oracle's work
+    does not depend on their values).  Extrapolation: each attention part scales by the
+    head's selected token pairs over the sample's, and everything by the number of
+    heads."""
     import numpy as np
     import threadpoolctl
 
     from oracle import prism_oracle as O
 
-    info = threadpoolctl.threadpool_info()
-    threads = max([i.get("num_threads", 1) for i in info] or [1])
-    h = 0
-    n = {k: t[:, h:h + 1].float().numpy().astype(np.float64) for k, t in x.items()}
-    t0 = time.perf_counter()
-    scale = 1.0 / math.sqrt(w.d)
-    stats = O.zone_stats(n["v"], n["a2v"], w.grid, w.zone)
-    sid, _ = O.assign_shapes(stats.astype(np.float32), list(w.cands), w.zone)
-    tok = O.slot_map(w.grid, w.zone, list(w.cands), sid)
-    bv = O.block_valid(tok, w.vol)
-    qp, kp, vp = O.permute(n["q"], tok), O.permute(n["k"], tok), O.permute(n["v"], tok)
-    qb, kb = O.pool_blocks(qp, bv, w.vol), O.pool_blocks(kp, bv, w.vol)
-    live = np.nonzero(bv[0, 0] > 0)[0]
-    rows = live[np.linspace(0, live.size - 1, budget_blocks).astype(int)]
-    sel, _ = O.select_blocks(qb.astype(np.float32), kb.astype(np.float32), bv, scale, w.top_p, w.k_min,
-                             w.k_max, rows=rows)
-    blocks = [(0, 0, int(I)) for I in rows]
-    op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, scale, w.vol, blocks=blocks)
-    if not fwd_only:
-        dop = O.permute(n["do"], tok)
-        touched = sorted({(0, 0, int(J)) for s in sel.values() for J in s})
-        O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, scale, w.vol, q_blocks=blocks, k_blocks=touched)
-    dt = time.perf_counter() - t0
-    pairs = sum(int(bv[0, 0, I]) * int(bv[0, 0, s].sum()) for (_, _, I), s in sel.items())
-    flops = (4.0 if fwd_only else 14.0) * w.d * pairs
-    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
-                seconds=round(dt, 2),
-                sample=(f"head 0 of {w.name}: zone stats, shapes, permutation and pooling of the whole head, "
-                        f"selection, forward{'' if fwd_only else ' and backward'} of {budget_blocks} query blocks "
-                        f"({pairs} valid token pairs, {4 if fwd_only else 14}*d flops each), float64 numpy"))
+    nproc = len(os.sched_getaffinity(0))
+    f32 = np.float32
+    with threadpoolctl.threadpool_limits(nproc):
+        h = 0
+        n = {k: t[:, h:h + 1].float().numpy() for k, t in x.items()}
+        scale = 1.0 / math.sqrt(w.d)
+        t0 = time.perf_counter()
+        stats = O.zone_stats(n["v"], n["a2v"], w.grid, w.zone)
+        sid, _ = O.assign_shapes(stats.astype(f32), list(w.cands), w.zone)
+        tok = O.slot_map(w.grid, w.zone, list(w.cands), sid)
+        bv = O.block_valid(tok, w.vol)
+        qp, kp, vp = O.permute(n["q"], tok), O.permute(n["k"], tok), O.permute(n["v"], tok)
+        qb, kb = O.pool_blocks(qp, bv, w.vol), O.pool_blocks(kp, bv, w.vol)
+        sel, _ = O.select_blocks_all(qb.astype(f32), kb.astype(f32), bv, scale, w.top_p, w.k_min, w.k_max)
+        t_pre = time.perf_counter() - t0
+        live = np.nonzero(bv[0, 0] > 0)[0]
+        rows = live[np.linspace(0, live.size - 1, n_blocks).astype(int)]
+        qblk = [(0, 0, int(I)) for I in rows]
+
+        def pairs_of(blocks):
+            return sum(int(bv[0, 0, I]) * int(bv[0, 0, sel[(0, 0, I)]].sum()) for (_, _, I) in blocks)
+
+        head_pairs = O.selected_pair_flops(bv, sel, 1) / 14.0
+        t0 = time.perf_counter()
+        op, lse = O.sparse_attn_fwd(qp, kp, vp, bv, sel, scale, w.vol, blocks=qblk, dtype=f32)
+        t_fwd = time.perf_counter() - t0
+        parts = dict(fwd=(t_fwd, pairs_of(qblk)))
+        if not fwd_only:
+            dop = O.permute(n["do"], tok)
+            t0 = time.perf_counter()
+            O.sparse_attn_bwd(qp, kp, vp, op, dop, lse, bv, sel, scale, w.vol, q_blocks=qblk, k_blocks=[], dtype=f32)
+            parts["dq"] = (time.perf_counter() - t0, pairs_of(qblk))
+            rev = O._transpose_selection(sel)
+            kblk = [(0, 0, int(J)) for J in rows if (0, 0, int(J)) in rev]
+            lse_ph = np.where(lse == 0, 30.0, lse)            # placeholder rows: P = exp(s - 30) stays finite
+            t0 = time.perf_counter()
+            O.sparse_attn_bwd(qp, kp, vp, op, dop, lse_ph, bv, sel, scale, w.vol, q_blocks=[], k_blocks=kblk,
+                              dtype=f32)
+            kpairs = sum(int(bv[0, 0, J]) * int(bv[0, 0, rev[(0, 0, J)]].sum()) for (_, _, J) in kblk)
+            parts["dkdv"] = (time.perf_counter() - t0, kpairs)
+    n_k = 0 if fwd_only else len(kblk)
+    sample_s = t_pre + sum(t for t, _ in parts.values())
+    head_s = t_pre + sum(t * head_pairs / max(p, 1) for t, p in parts.values())
+    layer_s = head_s * w.heads * w.B
+    f_layer = (4.0 if fwd_only else 14.0) * w.d * head_pairs * w.heads * w.B
+    return dict(value=round(f_layer / layer_s / 1e12, 6), unit="TFLOP/s", cores=nproc, kind="oracle",
+                cpu=cpu_model(), dtype="f32", extrapolated=True,
+                layer_seconds_extrapolated=round(layer_s, 1), sample_seconds=round(sample_s, 2),
+                sample=(f"oracle in float32 on {nproc} host threads: head 0 of {w.name} -- zone statistics, shapes, "
+                        f"permutation, pooling and selection of the whole head ({t_pre:.1f} s); attention forward"
+                        f"{'' if fwd_only else ', dQ'} of {n_blocks} query blocks"
+                        f"{'' if fwd_only else f' and dK/dV of {n_k} key blocks'}"
+                        f"; extrapolated to the layer by selected token pairs and heads ({w.heads} heads)"))
 
 
 def main():
@@ -462,9 +615,11 @@ def main():
                          "variance=global (comma-separated)")
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward chain only (inference; e.g. --workload 5)")
-    ap.add_argument("--dense-steps", type=int, default=1)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-blocks", type=int, default=200)
+    ap.add_argument("--no-microbench", action="store_true",
+                    help="skip the measured ceilings (matrix-core peak and clock, forward tile gather)")
+    ap.add_argument("--stage-reps", type=int, default=3, help="cold-cache runs per stage for stage_ms")
+    ap.add_argument("--cpu-blocks", type=int, default=16)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one elementwise pass y = -x over this many MiB after warm-up (counter calibration)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),

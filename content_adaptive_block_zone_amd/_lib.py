@@ -76,6 +76,9 @@ PROTOTYPES = {
     "prism_dense_bwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "prism_dense_attn_bwd": (c_int, [_P, _P, _P, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_float,
                                      _P, _P, _P, _P, c_size_t, _P, _P]),
+    "prism_bench_mfma_peak": (c_int, [c_int, c_int, _P, _P, _P]),
+    "prism_bench_tile_gather": (c_int, [_P, _P, _P, c_int, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, _P,
+                                        _P, c_size_t, _P]),
     "prism_last_error": (c_char_p, []),
 }
 

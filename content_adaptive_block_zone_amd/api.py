@@ -401,3 +401,25 @@ def _event_array(marks):
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
+
+
+# ------------------------------------------------------------------ measurement kernels
+def prism_bench_mfma_peak(workgroups: int, iters: int, clocks: torch.Tensor, sink: torch.Tensor,
+                          stream=None) -> None:
+    """clocks int64 [workgroups, 2] (shader cycles, 100 MHz ticks), sink float32 [workgroups]."""
+    check(load().prism_bench_mfma_peak(int(workgroups), int(iters),
+                                       _ptr(clocks, torch.int64, (workgroups, 2), "clocks"),
+                                       _ptr(sink, torch.float32, (workgroups,), "sink"), _stream(stream)),
+          "prism_bench_mfma_peak")
+
+
+def prism_bench_tile_gather(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, op, workspace, stream=None) -> None:
+    B, Hh, npad, d = qp.shape
+    nb = npad // vol
+    km = sel_idx.shape[-1]
+    dt = _same_dtype(qp, kp, vp, op)
+    check(load().prism_bench_tile_gather(
+        _ptr(qp, name="qp"), _ptr(kp, shape=qp.shape, name="kp"), _ptr(vp, shape=qp.shape, name="vp"), dt,
+        _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"), _ptr(sel_idx, torch.int32, (B, Hh, nb, km), "sel_idx"),
+        _ptr(sel_cnt, torch.int32, (B, Hh, nb), "sel_cnt"), km, B, Hh, nb, vol, d, _ptr(op, shape=qp.shape, name="op"),
+        _ptr(workspace, torch.uint8, name="workspace"), workspace.numel(), _stream(stream)), "prism_bench_tile_gather")

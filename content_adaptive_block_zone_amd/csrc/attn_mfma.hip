@@ -36,6 +36,7 @@ int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 size_t attn_mfma_sched_bytes(const AttnArgs& a);
 hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
 hipError_t launch_attn_bwd_mfma(const AttnArgs& a, int32_t* sched, hipEvent_t* marks, hipStream_t s);
+hipError_t launch_gather_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
 
 namespace {
 
@@ -687,6 +688,45 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ tile-gather ceiling
+// A measurement kernel, not part of the path: the forward's launch (its schedule, grid,
+// workgroup size, LDS footprint and two LDS stages) moving the same bytes with no
+// arithmetic.  Every listed K and V tile is copied into LDS by the forward's own copy
+// routine, and each owner block's valid Q rows are copied to O, so the kernel reads and
+// writes the forward's algorithmic bytes; its time is what the forward's memory traffic
+// alone costs with this launch.
+__global__ __launch_bounds__(NT, 2) void k_gather_fwd(AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
+  __shared__ int sMeta[kMetaCap];
+  int I, bh;
+  owner_of<16>(a, a.order_q, I, bh);
+  const int nI = nrows_of(a, bh, I);
+  const size_t q0 = row0_of(a, bh, I);
+  const bf16_t* K = static_cast<const bf16_t*>(a.k);
+  const bf16_t* V = static_cast<const bf16_t*>(a.v);
+  const int cnt = nI > 0 ? clampi(a.sel_cnt[size_t(bh) * a.nb + I], 0, a.k_max) : 0;
+  const BlockList bl = load_list(a, bh, a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
+  // the owner block: Q rows in, O rows out (16 bytes per lane, 4 rows per wave step)
+  const u32x4* Q = reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(a.q) + q0 * D);
+  u32x4* O = reinterpret_cast<u32x4*>(static_cast<bf16_t*>(a.out) + q0 * D);
+  for (int e = threadIdx.x; e < nI * (D / 8); e += NT) O[e] = Q[e];
+  int pre = list_first(bl, sMeta);
+  auto issue = [&](int k, int st) {
+    int J, n;
+    list_next(a, bh, bl, sMeta, k, pre, J, n, a.nkrows);
+    const size_t r0 = krow0_of(a, bh, J);
+    load_tile(K + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
+    load_tile(V + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
+  };
+  if (cnt > 0) issue(0, 0);
+  for (int it = 0; it < cnt; ++it) {
+    wait_loads();
+    __syncthreads();
+    if (it + 1 < cnt) issue(it + 1, (it & 1) ^ 1);
+  }
+  wait_loads();
+}
+
 __global__ __launch_bounds__(256) void k_bwd_pre_bf16(AttnArgs a, size_t total_rows) {
   const size_t row = size_t(blockIdx.x) * 16 + threadIdx.x / 16;
   const int cg = threadIdx.x % 16;
@@ -720,6 +760,15 @@ hipError_t launch_attn_fwd_mfma(const AttnArgs& a_in, int32_t* sched, hipStream_
     hipLaunchKernelGGL(k_schedule, dim3(a.BH), dim3(kSchedThreads), 0, s, a, sched, nullptr);
   }
   hipLaunchKernelGGL(k_fwd, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+// The forward's tile traffic without its arithmetic (measurement only; sparse mode).
+hipError_t launch_gather_fwd_mfma(const AttnArgs& a_in, int32_t* sched, hipStream_t s) {
+  AttnArgs a = a_in;
+  a.order_q = sched;
+  hipLaunchKernelGGL(k_schedule, dim3(a.BH), dim3(kSchedThreads), 0, s, a, sched, nullptr);
+  hipLaunchKernelGGL(k_gather_fwd, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

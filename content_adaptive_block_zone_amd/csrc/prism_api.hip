@@ -455,6 +455,31 @@ prism_status prism_a2v_attn_norm(const void* q, const void* ka, const void* va, 
   return launched(launch_attn_fwd_mfma(a, nullptr, stream), who);  // dense: no schedule
 }
 
+prism_status prism_bench_mfma_peak(int workgroups, int iters, uint64_t* clocks, float* sink, hipStream_t stream) {
+  const char* who = "prism_bench_mfma_peak";
+  if (!clocks || !sink) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1) return fail(PRISM_ERR_ARG, "%s: need 1 <= workgroups <= 2^20, iters >= 1", who);
+  return launched(launch_mfma_peak(workgroups, iters, reinterpret_cast<unsigned long long*>(clocks), sink, stream), who);
+}
+
+prism_status prism_bench_tile_gather(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
+                                     const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     int k_max, int B, int Hh, int nb, int vol, int d, void* op, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream) {
+  const char* who = "prism_bench_tile_gather";
+  if (!qp || !kp || !vp || !block_valid || !sel_idx || !sel_cnt || !op || !workspace)
+    return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  prism_status st = check_attn_common(who, dtype, B, Hh, nb, vol, d, k_max, 1.f);
+  if (st != PRISM_OK) return st;
+  AttnArgs a = sparse_args(B, Hh, nb, vol, d, k_max, 1.f);
+  if (!attn_mfma_supported(a, dtype)) return fail(PRISM_ERR_DTYPE, "%s: needs bf16, d = 128 and vol = 64", who);
+  const size_t need = attn_mfma_sched_bytes(a);
+  if (ws_bytes < need) return fail(PRISM_ERR_ARG, "%s: workspace of %zu bytes < required %zu", who, ws_bytes, need);
+  a.q = qp; a.k = kp; a.v = vp; a.out = op;
+  a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt;
+  return launched(launch_gather_fwd_mfma(a, static_cast<int32_t*>(workspace), stream), who);
+}
+
 size_t prism_tiles_workspace_size(int B, int Hh, int nb, int vol) {
   if (B < 1 || Hh < 1 || nb < 1 || vol < kTileRows || vol % kTileRows != 0) return 0;
   return tiles_ws_bytes(B * Hh, nb, vol);

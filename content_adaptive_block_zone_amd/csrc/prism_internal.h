@@ -284,6 +284,12 @@ int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s);
 
+// Measurement kernels (not part of the path): the matrix-core peak and clock, and the
+// forward's tile traffic without arithmetic.
+hipError_t launch_mfma_peak(int workgroups, int iters, unsigned long long* clocks, float* sink, hipStream_t s);
+hipError_t launch_gather_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
+size_t attn_mfma_sched_bytes(const AttnArgs& a);
+
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace prism

@@ -340,6 +340,29 @@ prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, c
                                   void* workspace, size_t ws_bytes, hipEvent_t* marks,
                                   hipStream_t stream);
 
+/* Measurement kernels.  They are not steps of the method: they measure the ceilings the
+ * attention kernels are judged against on the GPU at hand.
+ *
+ * prism_bench_mfma_peak: `workgroups` workgroups of 4 wavefronts, each wave issuing
+ * `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 products (32768 flops
+ * each), so the run does workgroups * 4 * iters * 4 * 32768 flops.  clocks (device,
+ * uint64 [workgroups][2]) receives per workgroup the shader-clock cycles and the 100 MHz
+ * reference ticks over its loop; sink (device, float [workgroups]) is never written in
+ * practice and keeps the products from being removed.  Errors: null pointers,
+ * workgroups outside [1, 2^20] or iters < 1 -> PRISM_ERR_ARG. */
+prism_status prism_bench_mfma_peak(int workgroups, int iters, uint64_t* clocks, float* sink, hipStream_t stream);
+
+/* prism_bench_tile_gather: the launch of prism_sparse_attn_fwd (workgroup schedule, grid,
+ * LDS stages, the same copies of every listed K and V tile into LDS) with no arithmetic;
+ * each query block's valid Q rows are copied to op.  Arguments as prism_sparse_attn_fwd
+ * (no scale, no lse); bf16, d = 128 and vol = 64 only (PRISM_ERR_DTYPE otherwise);
+ * workspace: prism_fwd_workspace_size() bytes.  Its time is the forward's memory traffic
+ * alone with this launch. */
+prism_status prism_bench_tile_gather(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
+                                     const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
+                                     int k_max, int B, int Hh, int nb, int vol, int d, void* op, void* workspace,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* prism_last_error(void);
 

@@ -678,14 +678,15 @@ def _rows(x, b, h, B_, vol, n):
 
 
 def sparse_attn_fwd(qp, kp, vp, bvalid, sel: Dict, scale: float, vol: int,
-                    blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
+                    blocks: Optional[Sequence[Tuple[int, int, int]]] = None, dtype=np.float64):
     """O' [B,Hh,Npad,C] and LSE [B,Hh,Npad] in float64 (rows of unlisted blocks stay 0).
     Reading: a valid query row with nothing to attend (an empty list, or listed blocks
-    without valid rows) has no softmax; it outputs 0 with LSE 0, as padding rows do."""
-    qp, kp, vp = (np.asarray(a, dtype=np.float64) for a in (qp, kp, vp))
+    without valid rows) has no softmax; it outputs 0 with LSE 0, as padding rows do.
+    dtype: the precision of the arithmetic (float64 for parity; float32 only for timing)."""
+    qp, kp, vp = (np.asarray(a, dtype=dtype) for a in (qp, kp, vp))
     B, Hh, Np, C = qp.shape
-    O = np.zeros((B, Hh, Np, vp.shape[-1]))
-    L = np.zeros((B, Hh, Np))
+    O = np.zeros((B, Hh, Np, vp.shape[-1]), dtype=dtype)
+    L = np.zeros((B, Hh, Np), dtype=dtype)
     it = blocks if blocks is not None else [(b, h, I) for b in range(B) for h in range(Hh) for I in range(Np // vol)]
     for (b, h, I) in it:
         n = int(bvalid[b, h, I])
@@ -715,7 +716,7 @@ def _transpose_selection(sel: Dict) -> Dict:
 
 def sparse_attn_bwd(qp, kp, vp, op, dop, lse, bvalid, sel: Dict, scale: float, vol: int,
                     q_blocks: Optional[Sequence[Tuple[int, int, int]]] = None,
-                    k_blocks: Optional[Sequence[Tuple[int, int, int]]] = None):
+                    k_blocks: Optional[Sequence[Tuple[int, int, int]]] = None, dtype=np.float64):
     """Gradients of sum(O' * dO') w.r.t. Q', K', V' with the selection held fixed
     (reading: the statistics, shapes and selection are piecewise constant, so no
     gradient flows through them).
@@ -724,12 +725,13 @@ def sparse_attn_bwd(qp, kp, vp, op, dop, lse, bvalid, sel: Dict, scale: float, v
         dQ_i = scale sum_j dS_ij k_j,  dK_j = scale sum_i dS_ij q_i.
     dQ is accumulated per query block over its selected key blocks, dK/dV per key block
     over the query blocks that selected it.  q_blocks / k_blocks limit the work to the
-    listed blocks (all by default); other rows stay 0.  Returns float64 dQ', dK', dV'."""
-    qp, kp, vp, op, dop = (np.asarray(a, dtype=np.float64) for a in (qp, kp, vp, op, dop))
+    listed blocks (all by default); other rows stay 0.  Returns float64 dQ', dK', dV'
+    (dtype: the precision of the arithmetic, float64 for parity; float32 only for timing)."""
+    qp, kp, vp, op, dop = (np.asarray(a, dtype=dtype) for a in (qp, kp, vp, op, dop))
     B, Hh, Np, C = qp.shape
     nb = Np // vol
     dQ, dK, dV = np.zeros_like(qp), np.zeros_like(kp), np.zeros_like(vp)
-    lse = np.asarray(lse, dtype=np.float64)
+    lse = np.asarray(lse, dtype=dtype)
 
     def rows(x, b, h, I):
         return x[b, h, I * vol: I * vol + int(bvalid[b, h, I])]

@@ -713,3 +713,21 @@ def test_vectorised_selection_and_reverse_match_row_forms():
     idx, cnt = O.selection_arrays(s1, 1, 2, nb, 9)
     a, b = O.reverse_index(idx, cnt), O.reverse_index_sorted(idx, cnt)
     assert (a[0] == b[0]).all() and (a[1] == b[1]).all()
+
+
+def test_selected_pair_flops_closed_forms():
+    """14 d flops per valid (query, key) token pair: with every live block selected the
+    pair count is (valid tokens)^2 per head; a hand case with partial blocks."""
+    rng = np.random.default_rng(9)
+    B, Hh, nb, d = 1, 2, 9, 32
+    bv = rng.integers(0, 5, size=(B, Hh, nb)).astype(np.int32)
+    sel = {}
+    for h in range(Hh):
+        live = np.nonzero(bv[0, h] > 0)[0].astype(np.int32)
+        for I in range(nb):
+            sel[(0, h, I)] = live if bv[0, h, I] > 0 else np.zeros(0, np.int32)
+    want = 14.0 * d * sum(int(bv[0, h].sum()) ** 2 for h in range(Hh))
+    assert O.selected_pair_flops(bv, sel, d) == want
+    bv2 = np.array([[[3, 0, 5]]], dtype=np.int32)
+    sel2 = {(0, 0, 0): np.array([0, 2], np.int32), (0, 0, 1): np.zeros(0, np.int32), (0, 0, 2): np.array([2], np.int32)}
+    assert O.selected_pair_flops(bv2, sel2, 8) == 14.0 * 8 * (3 * (3 + 5) + 5 * 5)
