@@ -96,62 +96,73 @@ def recorded_traffic(kernel):
     return traffic.get(kernel)
 
 
-def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
-    """Text summary of a `rocprofv3 --kernel-trace --stats` run of the benchmark and of its
-    FETCH_SIZE / WRITE_SIZE counter runs, with the traffic per launch of each attention
-    kernel scaled by what the counters read for the plain copy (written to stdout)."""
-    import csv
+def _rocpd(path):
+    """The rocprofv3 database (rocpd SQLite) under a result directory."""
     import glob
-    lines = ["# Commands (one MI355X, repository at /root/repo; rocprofv3 runs from /tmp)"]
+    import sqlite3
+    dbs = sorted(glob.glob(os.path.join(path, "**", "*results.db"), recursive=True))
+    if not dbs:
+        raise SystemExit(f"no rocprofv3 database under {path}")
+    return sqlite3.connect(dbs[0])
+
+
+def _short(name):
+    import re
+    m = re.search(r"::(k_\w+)", name)
+    if m:
+        t = re.search(r"k_\w+(<[^>(]*>)?", name[m.start(1):])
+        return t.group(0) if t else m.group(1)
+    return "neg_kernel (calibration)" if "neg_kernel" in name else name[:44]
+
+
+def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
+    """Text summary of a `rocprofv3 --kernel-trace --stats` run of the benchmark and, when
+    given, of its FETCH_SIZE / WRITE_SIZE counter runs, with the traffic per launch of each
+    attention kernel scaled by what the counters read for the plain copy (to stdout)."""
+    lines = ["# Commands (one MI355X, repository root as working copy; rocprofv3 runs with TMPDIR=/tmp)"]
     lines += [f"#   {c}" for c in commands]
     lines.append("")
-    st = glob.glob(os.path.join(stats_dir, "*kernel_stats.csv"))[0]
+    db = _rocpd(stats_dir)
     lines.append("## Kernel time (rocprofv3 --kernel-trace --stats)")
     lines.append(f"{'kernel':44s} {'calls':>6s} {'avg ms':>10s} {'total %':>8s}")
-    import re
-    for r in csv.DictReader(open(st)):
-        m = re.search(r"::(k_\w+)", r["Name"])
-        n = m.group(1) if m else r["Name"][:44]
-        lines.append(f"{n:44s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e6:10.4f} {float(r['Percentage']):8.2f}")
+    for name, calls, _tot, avg, pct in db.execute(
+            "select name, total_calls, total_duration, average, percentage from top_kernels"):
+        # the database's summary view gives durations in microseconds
+        lines.append(f"{_short(name):44s} {int(calls):6d} {float(avg) / 1e3:10.4f} {float(pct):8.2f}")
     lines.append("")
-    per = {}
-    for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-        f = glob.glob(os.path.join(d, "*counter_collection*.csv"))[0]
-        acc = {}
-        for r in csv.DictReader(open(f)):
-            if r["Counter_Name"] != cname:
+    if fetch_dir and write_dir:
+        per = {}
+        for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            acc = {}
+            for kname, disp, val in _rocpd(d).execute(
+                    "select kernel_name, dispatch_id, counter_value from counters_collection where counter_name = ?",
+                    (cname,)):
+                a = acc.setdefault(_short(kname), [0.0, set()])
+                a[0] += float(val)
+                a[1].add(disp)
+            per[cname] = {n: v[0] / len(v[1]) for n, v in acc.items()}   # KiB per dispatch
+        cn = "neg_kernel (calibration)"
+        if cn not in per["FETCH_SIZE"]:
+            raise SystemExit("no calibration pass in the counter runs (run the benchmark with --copy-mib 256)")
+        ref_kib = COPY_MIB * 1024.0
+        sf = ref_kib / per["FETCH_SIZE"][cn]
+        sw = ref_kib / per["WRITE_SIZE"][cn]
+        lines.append("## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)")
+        lines.append(f"calibration: {cn} of {COPY_MIB} MiB reads FETCH_SIZE {per['FETCH_SIZE'][cn]:.0f} KiB and "
+                     f"WRITE_SIZE {per['WRITE_SIZE'][cn]:.0f} KiB per dispatch -> scale fetch x{sf:.3f}, write x{sw:.3f}")
+        lines.append(f"{'kernel':44s} {'FETCH KiB':>14s} {'WRITE KiB':>12s} {'scaled GB':>10s}")
+        for n in sorted(per["FETCH_SIZE"]):
+            if not n.startswith("k_"):
                 continue
-            m = re.search(r"::(k_\w+)", r["Kernel_Name"])
-            n = m.group(1) if m else ("neg_kernel (calibration)" if "neg_kernel" in r["Kernel_Name"]
-                                      else r["Kernel_Name"][:44])
-            a = acc.setdefault(n, [0.0, set()])
-            a[0] += float(r["Counter_Value"])
-            a[1].add(r["Dispatch_Id"])
-        per[cname] = {n: v[0] / len(v[1]) for n, v in acc.items()}   # KiB per dispatch
-    copy = [n for n in per["FETCH_SIZE"] if n == "neg_kernel (calibration)"]
-    if len(copy) != 1:
-        raise SystemExit("no calibration pass in the counter runs (run the benchmark with --copy-mib 256)")
-    cn = copy[0]
-    ref_kib = COPY_MIB * 1024.0
-    sf = ref_kib / per["FETCH_SIZE"][cn]
-    sw = ref_kib / per["WRITE_SIZE"][cn]
-    lines.append("## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE; KiB per dispatch)")
-    lines.append(f"calibration: {cn} of {COPY_MIB} MiB reads FETCH_SIZE {per['FETCH_SIZE'][cn]:.0f} KiB and "
-                 f"WRITE_SIZE {per['WRITE_SIZE'][cn]:.0f} KiB per dispatch -> scale fetch x{sf:.3f}, write x{sw:.3f}")
-    lines.append(f"{'kernel':44s} {'FETCH KiB':>14s} {'WRITE KiB':>12s} {'scaled GB':>10s}")
-    for n in sorted(per["FETCH_SIZE"]):
-        if not n.startswith("k_"):
-            continue
-        fk, wk = per["FETCH_SIZE"][n], per["WRITE_SIZE"].get(n, 0.0)
-        tb = (fk * sf + wk * sw) * 1024.0
-        lines.append(f"{n:44s} {fk:14.0f} {wk:12.0f} {tb / 1e9:10.3f}")
-    lines.append("")
-    lines.append("## Machine-readable (read by bench.py for roofline.traffic)")
-    lines.append(f"source_sha256 {attn_source_sha256()}")
-    for bench_name, sym in KERNEL_SYMBOL.items():
-        if sym in per["FETCH_SIZE"]:
-            tb = (per["FETCH_SIZE"][sym] * sf + per["WRITE_SIZE"].get(sym, 0.0) * sw) * 1024.0
-            lines.append(f"traffic_bytes_per_launch {bench_name} {int(round(tb))}")
+            fk, wk = per["FETCH_SIZE"][n], per["WRITE_SIZE"].get(n, 0.0)
+            lines.append(f"{n:44s} {fk:14.0f} {wk:12.0f} {(fk * sf + wk * sw) * 1024.0 / 1e9:10.3f}")
+        lines.append("")
+        lines.append("## Machine-readable (read by bench.py for roofline.traffic)")
+        lines.append(f"source_sha256 {attn_source_sha256()}")
+        for bench_name, sym in KERNEL_SYMBOL.items():
+            if sym in per["FETCH_SIZE"]:
+                tb = (per["FETCH_SIZE"][sym] * sf + per["WRITE_SIZE"].get(sym, 0.0) * sw) * 1024.0
+                lines.append(f"traffic_bytes_per_launch {bench_name} {int(round(tb))}")
     print("\n".join(lines))
 
 
@@ -293,17 +304,34 @@ def run_gpu(args):
     stream = torch.cuda.current_stream()
 
     fwd_only = args.forward_only
+    fused_a2v = args.a2v == "fused"
+    if fused_a2v:
+        # the model's audio-to-video cross-attention (video queries over audio keys and
+        # values drawn N(0, 1)) run by the library's kernel, which writes its output rows
+        # and the per-token norm; the statistics read the norm map instead of the rows
+        ga = torch.Generator().manual_seed(1000 + args.workload)
+        ka, va = (torch.randn(w.B, w.heads, w.n_audio, w.d, generator=ga).to(torch.bfloat16).to(dev) for _ in range(2))
+        o_a2v = torch.empty_like(q)
+        a2v_nrm = torch.empty(w.B, w.heads, w.N, dtype=torch.float32, device=dev)
 
     def stats_and_shapes():
         if shape_ids is None:
-            L.zone_stats(feat, a2v)
+            if fused_a2v:
+                api.prism_a2v_attn_norm(q, ka, va, L.scale, a2v_nrm, o=o_a2v)
+                L.zone_stats_from_norm(feat, a2v_nrm)
+            else:
+                L.zone_stats(feat, a2v)
             L.assign_shapes()
         else:
             L.shape_id.copy_(shape_ids)
 
     def step(ev=None):
         if ev is None:
-            L.forward(q, k, v, a2v, shape_id=shape_ids)
+            if fused_a2v and shape_ids is None:
+                api.prism_a2v_attn_norm(q, ka, va, L.scale, a2v_nrm, o=o_a2v)
+                L.forward(q, k, v, a2v_norm=a2v_nrm)
+            else:
+                L.forward(q, k, v, a2v, shape_id=shape_ids)
             if not fwd_only:
                 L.backward(do)
             return
@@ -404,8 +432,20 @@ def run_gpu(args):
                   ("unpermute_grads", lambda: (L.permute(g["dqp"], g["dq"], inverse=True),
                                                L.permute(g["dkp"], g["dk"], inverse=True),
                                                L.permute(g["dvp"], g["dv"], inverse=True)))]
+    a2v_info = None
+    if fused_a2v:
+        calls[0] = ("a2v_attn_norm", lambda: api.prism_a2v_attn_norm(q, ka, va, L.scale, a2v_nrm, o=o_a2v))
+        calls.insert(1, ("zone_stats_from_norm", lambda: L.zone_stats_from_norm(feat, a2v_nrm)))
     stage = time_stages(L, calls, args.stage_reps, flush_buf)
     log(f"[bench] stages (ms, cold cache): {stage}")
+    if fused_a2v:
+        rows = time_stages(L, [("zone_stats_from_rows", lambda: L.zone_stats(feat, o_a2v))], args.stage_reps,
+                           flush_buf)["zone_stats_from_rows"]
+        a2v_info = dict(mode="fused", a2v_attn_ms=stage["a2v_attn_norm"],
+                        zone_stats_from_norm_ms=stage["zone_stats_from_norm"], zone_stats_from_rows_ms=rows,
+                        stats_ms_saved=round(rows - stage["zone_stats_from_norm"], 4),
+                        stats_bytes_saved=int(w.B * w.heads * w.N * (w.d * 2 - 4)))
+        log(f"[bench] a2v: {a2v_info}")
     del flush_buf
 
     # measured ceilings: the matrix-core peak and clock, and the forward's tile traffic alone
@@ -504,6 +544,7 @@ def run_gpu(args):
         attn_ms=dict(fwd=round(t_fwd, 4), bwd_pre=round(t_pre, 4), bwd_dkdv=round(t_dkdv, 4), bwd_dq=round(t_dq, 4)),
         select_ms=round(t_select, 4),
         stage_ms=stage,
+        **({"a2v": a2v_info} if a2v_info else {}),
         dense=dense,
         speedup_vs_dense=None if dense is None else dense["speedup"],
         roofline=dict(bound="mfma", kernel=dom, achieved=round(achieved, 2), peak=MI355X_BF16_DENSE_TFLOPS,
@@ -615,6 +656,10 @@ def main():
                          "variance=global (comma-separated)")
     ap.add_argument("--forward-only", action="store_true",
                     help="time the forward chain only (inference; e.g. --workload 5)")
+    ap.add_argument("--a2v", choices=("rows", "fused"), default="rows",
+                    help="rows: the statistics read the A2V cross-attention output (an input); fused: the step runs "
+                         "the A2V cross-attention kernel, which also writes the per-token norm, and the statistics "
+                         "read the norm map")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true",
                     help="skip the measured ceilings (matrix-core peak and clock, forward tile gather)")
@@ -622,13 +667,15 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=16)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one elementwise pass y = -x over this many MiB after warm-up (counter calibration)")
-    ap.add_argument("--summarize-profile", nargs=3, metavar=("STATS_DIR", "FETCH_DIR", "WRITE_DIR"),
-                    help="print a text summary of rocprofv3 output directories and exit (no GPU)")
+    ap.add_argument("--summarize-profile", nargs="+", metavar="DIR",
+                    help="print a text summary of rocprofv3 output directories and exit (no GPU): STATS_DIR "
+                         "[FETCH_DIR WRITE_DIR]")
     ap.add_argument("--profile-command", action="append", default=[],
                     help="command line recorded in the summary (repeatable)")
     args = ap.parse_args()
     if args.summarize_profile:
-        summarize_profile(*args.summarize_profile, args.profile_command)
+        dirs = list(args.summarize_profile) + [None, None]
+        summarize_profile(dirs[0], dirs[1], dirs[2], args.profile_command)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: every Prism step is independent per head, so a multi-GPU "

@@ -283,12 +283,13 @@ hipError_t launch_attn_bwd_generic(const AttnArgs& a, prism_dtype dt, hipEvent_t
 
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 size_t attn_mfma_sched_bytes(const AttnArgs& a);
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd_mfma(const AttnArgs& a, int32_t* sched, hipEvent_t* marks, hipStream_t s);
 
-// Forward workspace: the matrix-core path's workgroup schedule (sparse mode), else none.
+// Forward workspace: on the matrix-core path the workgroup schedule (sparse mode) and the
+// fp16 copy of V with its per-head scales; none on the scalar path.
 size_t attn_fwd_ws_bytes(const AttnArgs& a, prism_dtype dt) {
-  return attn_mfma_supported(a, dt) ? attn_mfma_sched_bytes(a) : 0;
+  return attn_mfma_supported(a, dt) ? attn_mfma_fwd_ws_bytes(a) : 0;
 }
 
 // Backward workspace: D = rowsum(dO * O) per row, then (matrix-core path, sparse mode)
@@ -299,7 +300,7 @@ size_t attn_bwd_ws_bytes(const AttnArgs& a, prism_dtype dt) {
 }
 
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s) {
-  if (attn_mfma_supported(a, dt)) return launch_attn_fwd_mfma(a, static_cast<int32_t*>(ws), s);
+  if (attn_mfma_supported(a, dt)) return launch_attn_fwd_mfma(a, ws, s);
   return launch_attn_fwd_generic(a, dt, s);
 }
 

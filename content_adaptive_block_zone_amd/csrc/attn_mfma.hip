@@ -22,8 +22,9 @@
 // p holds row p with bits 2 and 3 swapped.  The matching A operand is the streamed tile
 // transposed with its rows in that order, read from the row-major tile with gfx950's
 // transposing LDS read (ds_read_b64_tr_b16), two 8-byte reads per operand.
-// All accumulation is fp32; the forward's P V product takes P as a bf16 head plus a bf16
-// remainder.
+// All accumulation is fp32.  The forward's P V product runs in fp16: P (below 2^8 under
+// the lazy rescaling) is rounded to fp16, and V comes from an fp16 copy made once per
+// launch and scaled per head by a power of two, in which every bf16 value is exact.
 // In sparse mode the workgroups take their owner blocks longest list first within each
 // head (k_schedule), which balances the launch and lets workgroups resident together
 // share tiles in L2.
@@ -34,7 +35,7 @@ namespace prism {
 
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 size_t attn_mfma_sched_bytes(const AttnArgs& a);
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd_mfma(const AttnArgs& a, int32_t* sched, hipEvent_t* marks, hipStream_t s);
 hipError_t launch_gather_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
 
@@ -46,6 +47,7 @@ constexpr int NT = 256;       // 4 wavefronts
 constexpr float LOG2E = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -168,11 +170,11 @@ struct BlockList {
   int cnt;
   bool in_lds;
 };
-template <int CAP = kMetaCap>
+template <int CAP = kMetaCap, int NTH = NT>
 __device__ __forceinline__ BlockList load_list(const AttnArgs& a, int bh, const int32_t* lst, int cnt, int* meta) {
   BlockList L{lst, cnt, !a.dense && cnt <= CAP && a.nb < 65536};
   if (L.in_lds)
-    for (int k = threadIdx.x; k < cnt; k += NT) {
+    for (int k = threadIdx.x; k < cnt; k += NTH) {
       const int J = clampi(lst[k], 0, a.nb - 1);
       meta[k] = J | (nrows_of(a, bh, J) << 16);
     }
@@ -221,6 +223,9 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mma32h(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 // value of lane l ^ 32 (v_permlane32_swap: a VALU exchange of the two 32-lane halves)
 __device__ __forceinline__ float xor32(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -233,6 +238,13 @@ __device__ __forceinline__ f32x16 zero16() {
   return z;
 }
 __device__ __forceinline__ int acc_row32(int e, int g) { return 8 * (e >> 2) + 4 * g + (e & 3); }
+// accumulator registers 8s..8s+7 rounded to fp16 (round to nearest even)
+__device__ __forceinline__ f16x8 pack8h(const f32x16& c, int s) {
+  f16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (_Float16)c[8 * s + e];
+  return r;
+}
 __device__ __forceinline__ bf16x8 pack8(const f32x16& c, int s) {
   bf16x8 r;
 #pragma unroll
@@ -263,10 +275,11 @@ __device__ __forceinline__ void copy16_to_lds(const void* base, uint32_t off, co
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m));
 }
 // tile <- rows 0..63 of src (wave-uniform); rows past n repeat row n-1 (finite; their
-// products are masked).  Wave w writes rows 16w..16w+15, 4 rows (1 KB) per instruction.
+// products are masked).  Wave w (0..3 of the waves sharing the tile) writes rows
+// 16w..16w+15, 4 rows (1 KB) per instruction.
 // (Copying only the valid rows, with the other lanes inactive, measured 2-3 % slower.)
-__device__ __forceinline__ void load_tile(const bf16_t* src, int n, uint16_t* tile) {
-  const int l = threadIdx.x & 63, w = threadIdx.x >> 6;
+__device__ __forceinline__ void load_tile(const bf16_t* src, int n, uint16_t* tile, int w = threadIdx.x >> 6) {
+  const int l = threadIdx.x & 63;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * i + (l >> 4);
@@ -280,8 +293,7 @@ __device__ __forceinline__ void load_tile(const bf16_t* src, int n, uint16_t* ti
 // 4k + i/4 address (k = 0..3); so lane 16b + 4q + c of half g addresses row
 // 16j + 8h + 4g + q, columns 32t + 16b + 4c.., and receives column 32t + 16b + 4q + c of
 // rows 16j + 8h + 4g + 0..3, which are kappa32 positions 8g + 4h + 0..3.
-__device__ __forceinline__ bf16x8 ldtr(const uint16_t* tile, int t, int j) {
-  const int l = threadIdx.x & 63;
+__device__ __forceinline__ bf16x8 ldtr(const uint16_t* tile, int t, int j, int l = threadIdx.x & 63) {
   const int c = 32 * t + 16 * ((l >> 4) & 1) + 4 * (l & 3);
   const int r = 16 * j + 4 * (l >> 5) + ((l & 15) >> 2);
   const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)(tile + tofs(r, c)));
@@ -299,10 +311,14 @@ __device__ __forceinline__ void store4_32(bf16_t* p, const f32x16& c, int j, flo
 // Owner: query block I.  Wave w = (qh = w&1, kh = w>>1) takes queries 32qh.. against keys
 // 32kh.. of every streamed key block and keeps its own online softmax (running max m, sum
 // l and O^T) over its key half; the two halves are merged once at the end through LDS.
-// K and V tiles stream through two LDS stages as in the backward kernels.  The P V product
-// runs in bf16 on P split into a bf16 head and a bf16 remainder (P = hi + lo to about 16
-// bits), i.e. two products, which keeps the probabilities' rounding well below the
-// output's own bf16 rounding.
+// K and V tiles stream through two LDS stages as in the backward kernels.
+// P V precision.  The probabilities must be carried to well below the output's own bf16
+// rounding: rounded to bf16 (8 bits) they cost up to half a bf16 ulp of a large output.
+//   H = true: P rounded to fp16 (11 bits) against the fp16 copy of V (per-head scale
+//     2^s, exact for bf16 values; undone in the epilogue): one product per 16 keys.
+//   H = false: P split into a bf16 head and a bf16 remainder (about 16 bits) against the
+//     bf16 V: two products.  Used by the audio-to-video cross-attention, whose call takes
+//     no workspace for the fp16 copy.
 // P split into bf16 head and remainder, accumulator registers 8s..8s+7
 __device__ __forceinline__ void split8(const f32x16& c, int s, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
@@ -313,6 +329,7 @@ __device__ __forceinline__ void split8(const f32x16& c, int s, bf16x8& hi, bf16x
   }
 }
 constexpr float kLazy = 8.f;  // log2 units
+template <bool H>
 __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB];
   __shared__ int sMeta[kMetaCap];
@@ -324,10 +341,12 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   const size_t q0 = row0_of(a, bh, I);
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
   const bf16_t* K = static_cast<const bf16_t*>(a.k);
-  const bf16_t* V = static_cast<const bf16_t*>(a.v);
+  // the V tile's 16-bit elements: fp16 (H) or bf16; the copy moves them as bits
+  const bf16_t* V = static_cast<const bf16_t*>(H ? a.v16 : a.v);
   bf16_t* O = static_cast<bf16_t*>(a.out);
   const int cnt = a.dense ? a.nkb : (nI > 0 ? clampi(a.sel_cnt[size_t(bh) * a.nb + I], 0, a.k_max) : 0);
   const BlockList bl = load_list(a, bh, a.dense ? nullptr : a.sel_idx + (size_t(bh) * a.nb + I) * a.k_max, cnt, sMeta);
+  const float vscale = H ? a.vinv[bh] : 1.f;   // undoes the fp16 copy's per-head scale
   const int qrow = 32 * qh + l32;
   const bool qok = qrow < nI;
   bf16x8 qf[8];
@@ -398,15 +417,24 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
     }
     rs += xor32(rs);
     l += rs;
-    bf16x8 h0, r0_, h1, r1_;
-    split8(sc, 0, h0, r0_);
-    split8(sc, 1, h1, r1_);
+    if constexpr (H) {
+      const f16x8 p0 = pack8h(sc, 0), p1 = pack8h(sc, 1);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      o[t] = mma32(vt[t][0], h0, o[t]);
-      o[t] = mma32(vt[t][0], r0_, o[t]);
-      o[t] = mma32(vt[t][1], h1, o[t]);
-      o[t] = mma32(vt[t][1], r1_, o[t]);
+      for (int t = 0; t < 4; ++t) {
+        o[t] = mma32h(__builtin_bit_cast(f16x8, vt[t][0]), p0, o[t]);
+        o[t] = mma32h(__builtin_bit_cast(f16x8, vt[t][1]), p1, o[t]);
+      }
+    } else {
+      bf16x8 h0, r0_, h1, r1_;
+      split8(sc, 0, h0, r0_);
+      split8(sc, 1, h1, r1_);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        o[t] = mma32(vt[t][0], h0, o[t]);
+        o[t] = mma32(vt[t][0], r0_, o[t]);
+        o[t] = mma32(vt[t][1], h1, o[t]);
+        o[t] = mma32(vt[t][1], r1_, o[t]);
+      }
     }
   }
   // merge the key halves: waves with kh = 1 hand (m, l, O^T) to kh = 0 through LDS
@@ -438,7 +466,7 @@ __global__ __launch_bounds__(NT, 2) void k_fwd(AttnArgs a) {
   // cross-attention's per-token norm).  A row with nothing to attend (an empty list, or
   // lists of blocks without valid rows: l = 0) gets O = 0 and LSE = 0, as padding rows do.
   if (qok) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const float inv = l > 0.f ? vscale / l : 0.f;
     if (O) {
 #pragma unroll
       for (int t = 0; t < 4; ++t)
@@ -688,6 +716,62 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ fp16 copy of V
+// The forward's P V product runs in fp16 on a copy of V scaled per head by 2^s, with s
+// chosen so that the head's largest |V| lands in [2^14, 2^15): every bf16 value of the
+// head within a factor 2^29 of that maximum is then exact in fp16 (8 significant bits fit
+// the 11 of fp16) and nothing overflows.  The epilogue multiplies by 2^-s.  A head whose
+// maximum is 0 or not finite keeps s = 0 (NaN and infinity pass through as they would).
+// One pass finds the maxima (atomicMax on the bits of non-negative floats: the result
+// does not depend on the order), one writes the copy.
+__global__ void k_zero_u32(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+__global__ __launch_bounds__(256) void k_vmax(const u32x4* __restrict__ v, size_t chunks_per_head,
+                                              uint32_t* __restrict__ vmax) {
+  const int bh = blockIdx.y;
+  const u32x4* src = v + size_t(bh) * chunks_per_head;
+  float m = 0.f;
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < chunks_per_head; i += size_t(gridDim.x) * 256) {
+    const u32x4 u = src[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      m = fmaxf(m, fabsf(__uint_as_float(u[j] << 16)));
+      m = fmaxf(m, fabsf(__uint_as_float(u[j] & 0xffff0000u)));
+    }
+  }
+  m = wave_max(m);
+  if ((threadIdx.x & 63) == 0) atomicMax(vmax + bh, __float_as_uint(m));
+}
+__device__ __forceinline__ float v16_scale(uint32_t mbits) {
+  const float m = __uint_as_float(mbits);
+  if (!(m > 0.f) || !isfinite(m)) return 1.f;
+  int ex;
+  (void)frexpf(m, &ex);                       // m = f 2^ex, f in [0.5, 1)
+  return ldexpf(1.f, min(max(15 - ex, -100), 100));
+}
+__global__ __launch_bounds__(256) void k_v16(const u32x4* __restrict__ v, u32x4* __restrict__ v16,
+                                             size_t chunks_per_head, const uint32_t* __restrict__ vmax,
+                                             float* __restrict__ vinv) {
+  const int bh = blockIdx.y;
+  const float sc = v16_scale(vmax[bh]);
+  if (blockIdx.x == 0 && threadIdx.x == 0) vinv[bh] = 1.f / sc;  // a power of two: exact
+  const u32x4* src = v + size_t(bh) * chunks_per_head;
+  u32x4* dst = v16 + size_t(bh) * chunks_per_head;
+  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < chunks_per_head; i += size_t(gridDim.x) * 256) {
+    const u32x4 u = src[i];
+    u32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const _Float16 lo = (_Float16)(__uint_as_float(u[j] << 16) * sc);
+      const _Float16 hi = (_Float16)(__uint_as_float(u[j] & 0xffff0000u) * sc);
+      r[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
+    }
+    dst[i] = r;
+  }
+}
+
 // ------------------------------------------------------------------ tile-gather ceiling
 // A measurement kernel, not part of the path: the forward's launch (its schedule, grid,
 // workgroup size, LDS footprint and two LDS stages) moving the same bytes with no
@@ -752,14 +836,44 @@ int attn_mfma_supported(const AttnArgs& a, prism_dtype dt) {
 // Bytes of one workgroup schedule (sparse mode; dense mode needs none).
 size_t attn_mfma_sched_bytes(const AttnArgs& a) { return a.dense ? 0 : align256(size_t(a.BH) * a.nb * 4); }
 
-// sched: attn_mfma_sched_bytes() bytes of device scratch (sparse mode)
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a_in, int32_t* sched, hipStream_t s) {
+// Forward workspace: [schedule (sparse mode)] [max |V| bits per head] [inverse scale per
+// head] [fp16 copy of V, BH x nkrows x d].
+size_t attn_mfma_fwd_ws_bytes(const AttnArgs& a) {
+  return attn_mfma_sched_bytes(a) + 2 * align256(size_t(a.BH) * 4) + align256(size_t(a.BH) * a.nkrows * D * 2);
+}
+
+// ws: attn_mfma_fwd_ws_bytes() bytes of device scratch, or null for the bf16 P V path (no
+// copy of V; dense mode only, where no schedule is needed either).
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a_in, void* ws, hipStream_t s) {
   AttnArgs a = a_in;
+  char* p = static_cast<char*>(ws);
+  if (!ws && !a.dense) return hipErrorInvalidValue;  // the schedule needs the workspace
   if (!a.dense) {
-    a.order_q = sched;
-    hipLaunchKernelGGL(k_schedule, dim3(a.BH), dim3(kSchedThreads), 0, s, a, sched, nullptr);
+    a.order_q = reinterpret_cast<int32_t*>(p);
+    hipLaunchKernelGGL(k_schedule, dim3(a.BH), dim3(kSchedThreads), 0, s, a, const_cast<int32_t*>(a.order_q),
+                       nullptr);
+    p += attn_mfma_sched_bytes(a);
   }
-  hipLaunchKernelGGL(k_fwd, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
+  if (!ws) {
+    hipLaunchKernelGGL(k_fwd<false>, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
+    return hipGetLastError();
+  }
+  uint32_t* vmax = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(a.BH) * 4);
+  float* vinv = reinterpret_cast<float*>(p);
+  p += align256(size_t(a.BH) * 4);
+  a.v16 = p;
+  a.vinv = vinv;
+  const size_t cph = size_t(a.nkrows) * D / 8;  // 16-byte chunks per head
+  // about 2048 workgroups in all, each head's chunks split evenly over its share
+  const size_t per_head = a.BH >= 2048 ? 1 : size_t(2048 / a.BH);
+  const size_t need = (cph + 255) / 256;
+  const unsigned gx = unsigned(need < per_head ? need : per_head);
+  hipLaunchKernelGGL(k_zero_u32, dim3((a.BH + 255) / 256), dim3(256), 0, s, vmax, a.BH);
+  hipLaunchKernelGGL(k_vmax, dim3(gx, a.BH), dim3(256), 0, s, static_cast<const u32x4*>(a.v), cph, vmax);
+  hipLaunchKernelGGL(k_v16, dim3(gx, a.BH), dim3(256), 0, s, static_cast<const u32x4*>(a.v),
+                     static_cast<u32x4*>(const_cast<void*>(a.v16)), cph, vmax, vinv);
+  hipLaunchKernelGGL(k_fwd<true>, dim3(a.nb * a.BH), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -11,6 +11,7 @@
 
 using namespace prism;
 
+
 namespace {
 
 thread_local std::string g_err;

@@ -235,6 +235,10 @@ struct AttnArgs {
   // order_k); null = the kernels' own fixed order.  Set by the launchers.
   const int32_t* order_q;
   const int32_t* order_k;
+  // Matrix-core forward, fp16 P V path: V' as fp16 scaled per head by a power of two
+  // ([BH][nkrows][d]) and the inverse scale of each head.  Set by the launcher.
+  const void* v16;
+  const float* vinv;
 };
 
 // Launchers (each returns the first HIP error of its launches).
@@ -279,10 +283,15 @@ hipError_t launch_blocks_to_tiles(const int32_t* bvalid, const int32_t* sel_idx,
                                   int32_t* tile_valid, int32_t* tile_idx, int32_t* tile_cnt, int32_t* tile_rev_ptr,
                                   int32_t* tile_rev_idx, void* ws, hipStream_t s);
 // sched: device scratch for the workgroup schedule of a sparse launch (null in dense mode)
-hipError_t launch_attn_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
+// ws: attn_mfma_fwd_ws_bytes() bytes, or null (dense mode only) for the bf16 P V path
+hipError_t launch_attn_fwd_mfma(const AttnArgs& a, void* ws, hipStream_t s);
 int attn_mfma_supported(const AttnArgs& a, prism_dtype dt);
 hipError_t launch_attn_fwd(const AttnArgs& a, prism_dtype dt, void* ws, hipStream_t s);
 hipError_t launch_attn_bwd(const AttnArgs& a, prism_dtype dt, void* ws, hipEvent_t* marks, hipStream_t s);
+
+// Bytes of the matrix-core forward's workspace: the workgroup schedule (sparse mode), then
+// the fp16 copy of V and its per-head scales.
+size_t attn_mfma_fwd_ws_bytes(const AttnArgs& a);
 
 // Measurement kernels (not part of the path): the matrix-core peak and clock, and the
 // forward's tile traffic without arithmetic.

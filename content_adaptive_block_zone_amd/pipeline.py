@@ -248,12 +248,27 @@ class PrismLayer:
                 self.zone_stats(feat, a2v)
             self.assign_shapes()
         else:
+            self.check_shape_ids(shape_id)
             self.shape_id.copy_(shape_id)
         self.permute_qkv(q, k, v)
         self.select()
         self.attn_fwd()
         self.permute(self.op, self.o, inverse=True)
         return self.o
+
+    def check_shape_ids(self, shape_id: torch.Tensor) -> None:
+        """Given shapes (ablations) must name a candidate that tiles the zone; raises
+        otherwise (the permutation would map no token for such a zone)."""
+        ids = shape_id.detach().to("cpu", torch.int64).reshape(-1)
+        n = int(self.shapes.n)
+        if tuple(shape_id.shape) != (self.B, self.Hh, self.nZ):
+            raise ValueError(f"shape_id has shape {tuple(shape_id.shape)}, expected {(self.B, self.Hh, self.nZ)}")
+        if ids.numel() and (int(ids.min()) < 0 or int(ids.max()) >= n):
+            raise ValueError(f"shape ids must lie in [0, {n}), got [{int(ids.min())}, {int(ids.max())}]")
+        g = self.grid
+        bad = [c for c in range(n) if g.zt % self.shapes.bt[c] or g.zh % self.shapes.bh[c] or g.zw % self.shapes.bw[c]]
+        if bad and bool(torch.isin(ids, torch.tensor(bad)).any()):
+            raise ValueError(f"shape ids {bad} name candidates that do not tile the {g.zt}x{g.zh}x{g.zw} zone")
 
     def backward(self, do, marks=None):
         g = self._grads()

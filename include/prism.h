@@ -50,7 +50,15 @@ typedef enum {
   PRISM_ERR_LAUNCH = 4  /* the HIP runtime refused a launch */
 } prism_status;
 
-typedef enum { PRISM_F32 = 0, PRISM_BF16 = 1 } prism_dtype;
+/* The last two enumerators only widen the type to every 32-bit value, so that any value a
+ * caller passes is a valid prism_dtype object; the calls accept PRISM_F32 and PRISM_BF16
+ * and reject everything else with PRISM_ERR_DTYPE. */
+typedef enum {
+  PRISM_F32 = 0,
+  PRISM_BF16 = 1,
+  PRISM_DTYPE_NONE = -1,
+  PRISM_DTYPE_LAST = 0x7fffffff
+} prism_dtype;
 
 /* Flags of prism_zone_stats_ex. */
 enum { PRISM_STATS_GLOBAL_VARIANCE = 1, PRISM_STATS_FROM_NORM = 2 };
@@ -295,10 +303,15 @@ prism_status prism_blocks_to_tiles_mixed(const int32_t* block_valid, const int32
  *   O_i = softmax_j(scale q_i.k_j) v_j,  lse_i = ln sum_j exp(scale q_i.k_j).
  * op   out [B][Hh][nb*vol][d] (zeros at padding rows);  lse out float [B][Hh][nb*vol]
  * (0 at padding rows).  Requires vol <= 64 and d in {64, 128}; bf16 with vol = 64 and
- * d = 128 runs on the matrix cores.  workspace: prism_fwd_workspace_size() bytes of device
- * scratch: on the matrix-core path B*Hh*nb int32 (rounded up to 256 bytes), the order in
- * which workgroups take their query blocks (longest list first), which changes no output;
- * 0 bytes otherwise, and workspace may then be NULL.  Too small: PRISM_ERR_ARG. */
+ * d = 128 runs on the matrix cores, with the P V product in fp16: P (below 2^8) rounded
+ * to fp16 against a copy of V scaled per head by a power of two that keeps every bf16
+ * value exact in fp16 (those more than 2^29 below the head's largest |V| excepted, whose
+ * contribution is below the output's own rounding).  workspace:
+ * prism_fwd_workspace_size() bytes of device scratch: on the matrix-core path B*Hh*nb
+ * int32 (rounded up to 256 bytes), the order in which workgroups take their query blocks
+ * (longest list first, changes no output), then two per-head words and the fp16 copy of
+ * V (2 bytes per element of vp); 0 bytes otherwise, and workspace may then be NULL.
+ * Too small: PRISM_ERR_ARG. */
 size_t prism_fwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype);
 prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
                                    const int32_t* block_valid, const int32_t* sel_idx,
@@ -328,7 +341,8 @@ prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* v
 
 /* Dense attention comparator on unpermuted [B][Hh][N][d] tensors (every key attended),
  * the same kernels run with every block selected; used to measure the sparse path's
- * speedup.  lse float [B][Hh][N].  Requires d in {64, 128}. */
+ * speedup.  lse float [B][Hh][N].  Requires d in {64, 128}.  The forward's workspace holds
+ * the fp16 copy of V as for prism_sparse_attn_fwd (no schedule). */
 size_t prism_dense_fwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype);
 prism_status prism_dense_attn_fwd(const void* q, const void* k, const void* v, prism_dtype dtype,
                                   int B, int Hh, int N, int d, float scale, void* o, float* lse,

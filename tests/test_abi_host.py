@@ -74,20 +74,25 @@ def test_host_helpers_reject_bad_geometry(lib):
 
 
 def test_attention_workspace_holds_the_schedules(lib):
-    """The matrix-core path (bf16, 64-row blocks, d = 128) keeps its workgroup schedules in
-    the workspace: one int32 per (head, block) for the forward; D (one float per row) and
-    two schedules for the backward, each rounded up to 256 bytes.  Other paths need none."""
+    """The matrix-core path (bf16, 64-row blocks, d = 128) keeps in the workspace its
+    workgroup schedules (one int32 per (head, block), sparse mode only) and, for the
+    forward, the fp16 copy of V (2 bytes per element) with two per-head words (max |V|
+    bits, inverse scale); the backward holds D (one float per row) and two schedules.
+    Every part is rounded up to 256 bytes.  Other paths need no workspace for the forward
+    and D alone for the backward."""
     import torch
     from content_adaptive_block_zone_amd import api
     a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
     for B, Hh, nb in ((1, 4, 5760), (2, 3, 77)):
         sched = a256(B * Hh * nb * 4)
-        assert api.prism_fwd_workspace_size(B, Hh, nb, 64, 128, torch.bfloat16) == sched
+        v16 = 2 * a256(B * Hh * 4) + a256(B * Hh * nb * 64 * 128 * 2)
+        assert api.prism_fwd_workspace_size(B, Hh, nb, 64, 128, torch.bfloat16) == sched + v16
         assert api.prism_bwd_workspace_size(B, Hh, nb, 64, 128, torch.bfloat16) == a256(B * Hh * nb * 64 * 4) + 2 * sched
         assert api.prism_fwd_workspace_size(B, Hh, nb, 64, 64, torch.bfloat16) == 0           # generic path
         assert api.prism_fwd_workspace_size(B, Hh, nb, 16, 128, torch.bfloat16) == 0
         assert api.prism_bwd_workspace_size(B, Hh, nb, 64, 128, torch.float32) == a256(B * Hh * nb * 64 * 4)
-    assert api.prism_dense_fwd_workspace_size(1, 4, 1000, 128, torch.bfloat16) == 0         # dense: no schedule
+    # dense: no schedule, the fp16 copy of V only
+    assert api.prism_dense_fwd_workspace_size(1, 4, 1000, 128, torch.bfloat16) == 2 * 256 + a256(4 * 1000 * 128 * 2)
 
 
 def _status(fn, *args):
@@ -139,7 +144,7 @@ def test_calls_validate_before_launch(lib):
         ("prism_sparse_attn_fwd", (P, P, P, F32, P, P, P, 0, 1, 2, 16, 16, 64, 0.125, P, P, None, 0, None),
          E.PRISM_ERR_ARG),
         ("prism_sparse_attn_fwd", (P, P, P, BF16, P, P, P, 8, 1, 2, 16, 64, 128, 0.125, P, P, None, 0, None),
-         E.PRISM_ERR_ARG),                                                             # schedule needs a workspace
+         E.PRISM_ERR_ARG),                                                             # schedule and the fp16 copy of V need a workspace
         ("prism_sparse_attn_fwd", (P, P, P, BF16, P, P, P, 8, 1, 2, 16, 64, 128, 0.125, P, P, P, 127, None),
          E.PRISM_ERR_ARG),                                                             # workspace too small
         ("prism_sparse_attn_bwd", (P, P, P, P, P, P, BF16, P, P, P, 8, P, P, 1, 2, 16, 64, 128, 0.125, P, P, P,
@@ -188,3 +193,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load()
+
+
+def test_layer_rejects_invalid_shape_ids(lib):
+    """Given shapes (the random / fixed ablations) are checked on the host: an id outside
+    the candidate list, or a candidate that does not tile the zone, raises before any
+    launch (the shape check runs before the layer touches the GPU)."""
+    import torch
+    from content_adaptive_block_zone_amd.pipeline import PrismLayer
+    L = PrismLayer(1, 2, 64, (4, 8, 8), (2, 4, 8), [(1, 4, 4), (2, 2, 4), (2, 4, 2), (4, 2, 2)], 0.9, 2, 8,
+                   dtype=torch.float32, device="cpu")
+    ok = torch.zeros(1, 2, L.nZ, dtype=torch.int32)
+    L.check_shape_ids(ok)
+    with pytest.raises(ValueError, match="lie in"):
+        L.check_shape_ids(ok + 4)
+    with pytest.raises(ValueError, match="do not tile"):
+        L.check_shape_ids(ok + 3)                  # 4x2x2 has b_T = 4 > zone extent 2
+    with pytest.raises(ValueError, match="expected"):
+        L.check_shape_ids(torch.zeros(1, 1, L.nZ, dtype=torch.int32))

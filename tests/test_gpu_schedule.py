@@ -2,8 +2,9 @@
 workgroups of a sparse launch take their blocks (within each head, longest list first, in
 bins of bound // 2048 + 1 lengths, bound = k_max for the query-major order and nb for the
 key-major one).  The schedule sits in the entry points' workspace: the forward's first
-B*Hh*nb int32, the backward's two orders (query-major, then key-major, each rounded up to
-256 bytes) after its D buffer of B*Hh*nb*64 floats (rounded likewise).  Checked: each order
+B*Hh*nb int32 (then its fp16 copy of V), the backward's two orders (query-major, then
+key-major, each rounded up to 256 bytes) after its D buffer of B*Hh*nb*64 floats (rounded
+likewise).  Checked: each order
 is a permutation of the head's blocks, heads in order, lengths non-increasing by bin; and
 outputs of ordered launches over ragged lists (empty lists, dead blocks, lists of every
 length up to k_max) against the oracle on every block."""
@@ -80,7 +81,8 @@ def run(Hh, nb, k_max, seed, with_oracle: bool):
     op = torch.zeros_like(qd)
     lse = torch.zeros(shape[:3], dtype=torch.float32, device="cuda")
     wsf = torch.zeros(api.prism_fwd_workspace_size(1, Hh, nb, VOL, D), dtype=torch.uint8, device="cuda")
-    assert wsf.numel() == a256(Hh * nb * 4)
+    # the schedule first, then the fp16 copy of V (two per-head words, then the copy)
+    assert wsf.numel() == a256(Hh * nb * 4) + 2 * a256(Hh * 4) + a256(Hh * nb * VOL * D * 2)
     api.prism_sparse_attn_fwd(qd, kd, vd, i32(bv), i32(idx), i32(cnt), VOL, scale, op, lse, wsf)
     out = dict(q=q, k=k, v=v, do=do, bv=bv, sel=sel, scale=scale, op=op, lse=lse)
     op_in, lse_in = op, lse
