@@ -70,6 +70,8 @@ PROTOTYPES = {
     "prism_bwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "prism_sparse_attn_bwd": (c_int, [_P, _P, _P, _P, _P, _P, c_int, _P, _P, _P, c_int, _P, _P, c_int, c_int,
                                       c_int, c_int, c_int, c_float, _P, _P, _P, _P, c_size_t, _P, _P]),
+    "prism_sparse_attn_bwd_noalloc": (c_int, [_P, _P, _P, _P, _P, _P, c_int, _P, _P, _P, c_int, _P, _P, c_int,
+                                              c_int, c_int, c_int, c_int, c_float, _P, _P, _P, _P, _P]),
     "prism_dense_fwd_workspace_size": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
     "prism_dense_attn_fwd": (c_int, [_P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_float, _P, _P, _P,
                                      c_size_t, _P]),

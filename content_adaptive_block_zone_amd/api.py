@@ -360,6 +360,25 @@ def prism_sparse_attn_bwd(qp, kp, vp, op, dop, lse, block_valid, sel_idx, sel_cn
         mk, _stream(stream)), "prism_sparse_attn_bwd")
 
 
+def prism_sparse_attn_bwd_noalloc(qp, kp, vp, op, dop, lse, block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx,
+                                  vol: int, scale: float, dqp, dkp, dvp, marks=None, stream=None) -> None:
+    """prism_sparse_attn_bwd without a workspace argument: the library's static scratch."""
+    B, Hh, npad, d = qp.shape
+    nb = npad // vol
+    km = sel_idx.shape[-1]
+    dt = _same_dtype(qp, kp, vp, op, dop, dqp, dkp, dvp)
+    keep = _event_array(marks)
+    mk = None if keep is None else ctypes.cast(keep, ctypes.c_void_p)
+    check(load().prism_sparse_attn_bwd_noalloc(
+        _ptr(qp, name="qp"), _ptr(kp, shape=qp.shape, name="kp"), _ptr(vp, shape=qp.shape, name="vp"),
+        _ptr(op, shape=qp.shape, name="op"), _ptr(dop, shape=qp.shape, name="dop"),
+        _ptr(lse, torch.float32, (B, Hh, npad), "lse"), dt, _ptr(block_valid, torch.int32, (B, Hh, nb), "block_valid"),
+        _ptr(sel_idx, torch.int32, (B, Hh, nb, km), "sel_idx"), _ptr(sel_cnt, torch.int32, (B, Hh, nb), "sel_cnt"), km,
+        _ptr(rev_ptr, torch.int32, (B, Hh, nb + 1), "rev_ptr"), _ptr(rev_idx, torch.int32, (B, Hh, nb * km), "rev_idx"),
+        B, Hh, nb, vol, d, float(scale), _ptr(dqp, shape=qp.shape, name="dqp"), _ptr(dkp, shape=qp.shape, name="dkp"),
+        _ptr(dvp, shape=qp.shape, name="dvp"), mk, _stream(stream)), "prism_sparse_attn_bwd_noalloc")
+
+
 def prism_dense_attn_fwd(q, k, v, scale: float, o, lse, workspace=None, stream=None) -> None:
     B, Hh, N, d = q.shape
     dt = _same_dtype(q, k, v, o)

@@ -5,12 +5,19 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "prism_internal.h"
 
 using namespace prism;
 
+// Scratch of the allocation-free backward (prism_sparse_attn_bwd_noalloc): a file-scope
+// device array, one copy per GPU, held until the process ends.  Host code never passes
+// the array's name to a kernel (in host code it is only a stand-in for the symbol): the
+// device address of each GPU's copy is looked up once, with that GPU current, and kept.
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
 
 namespace {
 
@@ -390,6 +397,65 @@ prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* v
   a.dq = dqp; a.dk = dkp; a.dv = dvp;
   a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.rev_ptr = rev_ptr; a.rev_idx = rev_idx;
   return launched(launch_attn_bwd(a, dtype, workspace, marks, stream), "prism_sparse_attn_bwd");
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch`, looked up on the first call on
+// that GPU; the stream must belong to the current GPU.
+prism_status noalloc_scratch(const char* who, hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(PRISM_ERR_LAUNCH, "%s: hipGetDevice: %s", who, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PRISM_ERR_ARG, "%s: device %d out of range", who, dev);
+  if (stream) {
+    hipDevice_t sdev = -1;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return fail(PRISM_ERR_ARG, "%s: hipStreamGetDevice: %s", who, hipGetErrorString(e));
+    if (int(sdev) != dev)
+      return fail(PRISM_ERR_ARG, "%s: the stream belongs to device %d, the current device is %d", who, int(sdev), dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(PRISM_ERR_LAUNCH, "%s: hipGetSymbolAddress(scratch): %s", who, hipGetErrorString(e));
+    g_scratch_dev[dev] = ptr;
+  }
+  *out = g_scratch_dev[dev];
+  return PRISM_OK;
+}
+}  // namespace
+
+prism_status prism_sparse_attn_bwd_noalloc(const void* qp, const void* kp, const void* vp, const void* op,
+                                           const void* dop, const float* lse, prism_dtype dtype,
+                                           const int32_t* block_valid, const int32_t* sel_idx,
+                                           const int32_t* sel_cnt, int k_max, const int32_t* rev_ptr,
+                                           const int32_t* rev_idx, int B, int Hh, int nb, int vol, int d,
+                                           float scale, void* dqp, void* dkp, void* dvp, hipEvent_t* marks,
+                                           hipStream_t stream) {
+  const char* who = "prism_sparse_attn_bwd_noalloc";
+  if (!qp || !kp || !vp || !op || !dop || !lse || !block_valid || !sel_idx || !sel_cnt || !rev_ptr || !rev_idx ||
+      !dqp || !dkp || !dvp)
+    return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  prism_status st = check_attn_common(who, dtype, B, Hh, nb, vol, d, k_max, scale);
+  if (st != PRISM_OK) return st;
+  AttnArgs a = sparse_args(B, Hh, nb, vol, d, k_max, scale);
+  const size_t need = attn_bwd_ws_bytes(a, dtype);
+  if (need > kNoallocScratchBytes)
+    return fail(PRISM_ERR_SHAPE, "%s: needs %zu bytes of scratch; the static scratch holds %zu (use prism_sparse_attn_bwd)",
+                who, need, kNoallocScratchBytes);
+  void* ws = nullptr;
+  st = noalloc_scratch(who, stream, &ws);
+  if (st != PRISM_OK) return st;
+  a.q = qp; a.k = kp; a.v = vp; a.o = op; a.dout = dop; a.lse_in = lse;
+  a.dq = dqp; a.dk = dkp; a.dv = dvp;
+  a.bvalid = block_valid; a.sel_idx = sel_idx; a.sel_cnt = sel_cnt; a.rev_ptr = rev_ptr; a.rev_idx = rev_idx;
+  return launched(launch_attn_bwd(a, dtype, ws, marks, stream), who);
 }
 
 size_t prism_dense_fwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype) {

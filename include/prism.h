@@ -339,6 +339,25 @@ prism_status prism_sparse_attn_bwd(const void* qp, const void* kp, const void* v
                                    float scale, void* dqp, void* dkp, void* dvp, void* workspace,
                                    size_t ws_bytes, hipEvent_t* marks, hipStream_t stream);
 
+/* prism_sparse_attn_bwd for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): no workspace
+ * argument, and no allocation in the call.  Its scratch (D and the two workgroup
+ * schedules, prism_bwd_workspace_size() bytes) is a static device array of 32 MiB per
+ * GPU, held until the process ends; a call that needs more returns PRISM_ERR_SHAPE
+ * (about 8 million padded rows B*Hh*nb*vol).  The stream must belong to the current
+ * device (PRISM_ERR_ARG otherwise).  Every call on one GPU uses that GPU's one array:
+ * calls that overlap on a GPU (other streams, other host threads) race and must be
+ * ordered by the caller.  Nothing in the scratch needs to start at zero: every entry is
+ * written before it is read.  Arguments, outputs and other errors as
+ * prism_sparse_attn_bwd. */
+prism_status prism_sparse_attn_bwd_noalloc(const void* qp, const void* kp, const void* vp, const void* op,
+                                           const void* dop, const float* lse, prism_dtype dtype,
+                                           const int32_t* block_valid, const int32_t* sel_idx,
+                                           const int32_t* sel_cnt, int k_max, const int32_t* rev_ptr,
+                                           const int32_t* rev_idx, int B, int Hh, int nb, int vol, int d,
+                                           float scale, void* dqp, void* dkp, void* dvp, hipEvent_t* marks,
+                                           hipStream_t stream);
+
 /* Dense attention comparator on unpermuted [B][Hh][N][d] tensors (every key attended),
  * the same kernels run with every block selected; used to measure the sparse path's
  * speedup.  lse float [B][Hh][N].  Requires d in {64, 128}.  The forward's workspace holds

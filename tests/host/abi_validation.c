@@ -71,6 +71,9 @@ int main(void) {
                                                         F, P, 1, 0), PRISM_ERR_ARG);
   expect("bwd(vol 65)", prism_sparse_attn_bwd(P, P, P, P, P, F, PRISM_BF16, I, I, I, 8, I, I, 1, 1, 16, 65, 128, 0.1f,
                                               P, P, P, P, (size_t)-1, NULL, 0), PRISM_ERR_SHAPE);
+  expect("bwd_noalloc(past the scratch)",
+         prism_sparse_attn_bwd_noalloc(P, P, P, P, P, F, PRISM_BF16, I, I, I, 8, I, I, 64, 64, 1024, 64, 128, 0.1f, P,
+                                       P, P, NULL, 0), PRISM_ERR_SHAPE);
   expect("dense_fwd(N = 0)", prism_dense_attn_fwd(P, P, P, PRISM_BF16, 1, 1, 0, 128, 0.1f, P, F, P, (size_t)-1, 0),
          PRISM_ERR_ARG);
   expect("a2v_norm(Na overflow)", prism_a2v_attn_norm(P, P, P, PRISM_BF16, 1 << 16, 1 << 16, 64, 1 << 16, 128, 0.1f,

@@ -166,6 +166,10 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_ARG),
         ("prism_dense_attn_bwd", (P, P, P, P, P, P, F32, 1, 2, 256, 64, float("nan"), P, P, P, P, 1 << 30,
                                   None, None), E.PRISM_ERR_ARG),
+        ("prism_sparse_attn_bwd_noalloc", (P, P, P, P, P, P, BF16, P, P, P, 8, P, P, 1, 1, (1 << 17) + 1, 64, 128,
+                                           0.1, P, P, P, None, None), E.PRISM_ERR_SHAPE),   # past the static scratch
+        ("prism_sparse_attn_bwd_noalloc", (P, P, P, P, P, None, BF16, P, P, P, 8, P, P, 1, 1, 16, 64, 128,
+                                           0.1, P, P, P, None, None), E.PRISM_ERR_ARG),
         ("prism_permute_pool", (P, P, F32, 1, 2, 64, g, s, P, None, None, None), E.PRISM_ERR_ARG),   # no pooled
         ("prism_permute_pool", (P, P, BF16, 1, 2, 24, g, s, P, None, P, None), E.PRISM_ERR_DTYPE),  # 48-byte rows
         ("prism_permute_pool", (P, P, F32, 1, 2, 64, g, s, P, None, P, None), E.PRISM_ERR_ARG),     # x aliases y
