@@ -64,7 +64,7 @@ def kernel_bytes(sums, d):
 
 
 # kernel (bench name) -> symbol of its HIP kernel
-KERNEL_SYMBOL = {"sparse_attn_fwd": "k_fwd", "sparse_attn_bwd_dkdv": "k_dkdv32", "sparse_attn_bwd_dq": "k_dq32"}
+KERNEL_SYMBOL = {"sparse_attn_fwd": "k_fwd<true>", "sparse_attn_bwd_dkdv": "k_dkdv32", "sparse_attn_bwd_dq": "k_dq32"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernels_2k_like_traffic.txt")
 # Counter calibration: one elementwise pass y = -x over 256 MiB of fp32 (reads and writes
 # 256 MiB each); FETCH_SIZE and WRITE_SIZE are scaled by what they report for it.
@@ -135,7 +135,7 @@ def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
         for cname, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             acc = {}
             for kname, disp, val in _rocpd(d).execute(
-                    "select kernel_name, dispatch_id, counter_value from counters_collection where counter_name = ?",
+                    "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?",
                     (cname,)):
                 a = acc.setdefault(_short(kname), [0.0, set()])
                 a[0] += float(val)
