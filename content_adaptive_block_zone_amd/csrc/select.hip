@@ -3,15 +3,20 @@
 // caption; Table 7 caption: Top-p keeps the smallest set of key blocks whose cumulative
 // attention weight exceeds the threshold).
 //
-//   k_pool    mean of each block's valid rows (float32)           HBM-bound
-//   k_scores  scale * Qbar Kbar^T per head, 128x128 tiles, 8x8 per thread   fp32 ALU
-//   k_select_reg  per query block, the row of scores in registers: softmax over live
-//             key blocks, then the hybrid count found by bitwise search on the float bits
-//             of the probabilities (no sort): the Top-p threshold is the largest
-//             probability v whose "sum of probabilities >= v" still exceeds p; the Top-k
-//             clamp is a count search.  The kept set is emitted in ascending block order
-//             and marked in a bitmap for the reverse index.
-//   k_rev_*   deterministic transpose of the selection via that bitmap: count, scan, fill.
+//   k_pool     mean of each block's valid rows (float32)                 HBM-bound
+//   k_scores   scale * Qbar Kbar^T for one chunk of query blocks, float32 matrix-core
+//              products (v_mfma_f32_32x32x2_f32), 64x64 tiles
+//   k_select   per query block, the row of scores in registers: softmax over live key
+//              blocks, then the hybrid count found by bitwise search on the float bits
+//              of the probabilities (no sort): the Top-p threshold is the largest
+//              probability v whose "sum of probabilities >= v" still exceeds p; the Top-k
+//              clamp is a count search.  Once few values remain in the searched range
+//              they move to LDS and one wavefront finishes the search.  The kept set is
+//              emitted in ascending block order, with a row of selection bits.
+//   k_col_*    reverse index from those rows of bits, chunk by chunk: counts, then (after
+//              k_rev_scan) ascending lists; no atomics, every output has one writer.
+// Only one chunk of scores exists at a time (at most 256 MB), so no nb x nb matrix is
+// ever formed.
 #include "prism_internal.h"
 
 namespace prism {
@@ -23,30 +28,12 @@ struct SelWs {
   float* qbar;
   float* kbar;
   float* scores;
-  uint32_t* bitmap;
+  uint32_t* rowbits;
   int32_t* rcnt;
+  int32_t* cursor;
 };
 
 __host__ __device__ inline int words32(int nb) { return (nb + 31) / 32; }
-
-// Workspace layout: [pooled Q, pooled K,] scores, bitmap, reverse counts.  The pooled
-// means are absent when the caller passes them in (prism_select_blocks_pooled).
-SelWs carve(void* ws, int BH, int nb, int d, bool with_pooled) {
-  char* p = static_cast<char*>(ws);
-  SelWs w{};
-  if (with_pooled) {
-    w.qbar = reinterpret_cast<float*>(p);
-    p += align256(size_t(BH) * nb * d * 4);
-    w.kbar = reinterpret_cast<float*>(p);
-    p += align256(size_t(BH) * nb * d * 4);
-  }
-  w.scores = reinterpret_cast<float*>(p);
-  p += align256(size_t(BH) * nb * nb * 4);
-  w.bitmap = reinterpret_cast<uint32_t*>(p);
-  p += align256(size_t(BH) * nb * words32(nb) * 4);
-  w.rcnt = reinterpret_cast<int32_t*>(p);
-  return w;
-}
 
 __global__ void k_fill_u32(uint32_t* __restrict__ p, size_t n, uint32_t val) {
   for (size_t i = blockIdx.x * size_t(blockDim.x) + threadIdx.x; i < n; i += size_t(gridDim.x) * blockDim.x)
@@ -116,130 +103,114 @@ void launch_pool(const void* qp, const void* kp, const int32_t* bvalid, int BH, 
   }
 }
 
-// scores[bh][I][J] = scale * sum_c qbar[bh][I][c] kbar[bh][J][c]
-// Dead key blocks (no valid token) get the score -inf.
-// 128x128 tile per workgroup, 8x8 per thread (rows ty + 16i, columns tx + 16j), c in
-// chunks of 16 staged in LDS: four FMAs per LDS value read.  Each score sums its d
-// products in order of c, one fused multiply-add at a time.
-constexpr int kScT = 128;
+// Scores of one chunk of query rows: out[bh][I - I0][J] = scale * sum_c qbar[bh][I][c]
+// kbar[bh][J][c] for I0 <= I < I0 + rows; dead key blocks (no valid token) get -inf.
+// 64x64 tile per workgroup; wave (wi, wj) forms rows 32wi.., columns 32wj.. with
+// v_mfma_f32_32x32x2_f32 (float32 products and sums), c in chunks of 16 staged in LDS
+// (rows padded to 17 floats: the 32 rows one product reads fall in distinct banks).
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+constexpr int kScT = 64, kScK = 16;
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                 const int32_t* __restrict__ bvalid, int nb, int d, float scale,
-                                                float* __restrict__ scores) {
-  __shared__ float As[16][kScT];
-  __shared__ float Bs[16][kScT];
+                                                int I0, int rows, int CH, float* __restrict__ out) {
+  __shared__ float As[kScT][kScK + 1];
+  __shared__ float Bs[kScT][kScK + 1];
   const int bh = blockIdx.z;
-  const int I0 = blockIdx.y * kScT, J0 = blockIdx.x * kScT;
-  const float* Q = qbar + size_t(bh) * nb * d;
+  const int r0 = blockIdx.y * kScT;   // first row of the tile, relative to I0
+  const int j0 = blockIdx.x * kScT;
+  const float* Q = qbar + (size_t(bh) * nb + I0) * d;
   const float* K = kbar + size_t(bh) * nb * d;
-  const int t = threadIdx.x, ty = t / 16, tx = t % 16;
-  const int lr = t / 4, lc = (t % 4) * 4;  // staging: rows lr and lr + 64, columns lc..lc+3
-  float acc[8][8];
+  const int t = threadIdx.x, l = t & 63, w = t >> 6, wi = w & 1, wj = w >> 1;
+  const int sr = t >> 2, sc = (t & 3) * 4;  // staging: row sr, columns sc..sc+3 of each operand
+  f32x16 acc;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = 0.f;
-  for (int k0 = 0; k0 < d; k0 += 16) {
-    float4 a[2], b[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = lr + 64 * h;
-      a[h] = I0 + r < nb ? *reinterpret_cast<const float4*>(Q + size_t(I0 + r) * d + k0 + lc) : make_float4(0.f, 0.f, 0.f, 0.f);
-      b[h] = J0 + r < nb ? *reinterpret_cast<const float4*>(K + size_t(J0 + r) * d + k0 + lc) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  for (int k0 = 0; k0 < d; k0 += kScK) {
+    const float4 a = r0 + sr < rows ? *reinterpret_cast<const float4*>(Q + size_t(r0 + sr) * d + k0 + sc)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 b = j0 + sr < nb ? *reinterpret_cast<const float4*>(K + size_t(j0 + sr) * d + k0 + sc)
+                                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    As[sr][sc] = a.x; As[sr][sc + 1] = a.y; As[sr][sc + 2] = a.z; As[sr][sc + 3] = a.w;
+    Bs[sr][sc] = b.x; Bs[sr][sc + 1] = b.y; Bs[sr][sc + 2] = b.z; Bs[sr][sc + 3] = b.w;
     __syncthreads();
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int r = lr + 64 * h;
-      As[lc + 0][r] = a[h].x; As[lc + 1][r] = a[h].y; As[lc + 2][r] = a[h].z; As[lc + 3][r] = a[h].w;
-      Bs[lc + 0][r] = b[h].x; Bs[lc + 1][r] = b[h].y; Bs[lc + 2][r] = b[h].z; Bs[lc + 3][r] = b[h].w;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-      float ar[8], br[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ar[i] = As[kk][ty + 16 * i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) br[j] = Bs[kk][tx + 16 * j];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(ar[i], br[j], acc[i][j]);
+    for (int kk = 0; kk < kScK; kk += 2) {
+      const float av = As[32 * wi + (l & 31)][kk + (l >> 5)];
+      const float bv = Bs[32 * wj + (l & 31)][kk + (l >> 5)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
   }
-  const int32_t* bv = bvalid + size_t(bh) * nb;
-  bool live[8];
+  // lane l, register e: row 8(e/4) + 4(l/32) + e%4, column l%32 of the wave's 32x32 tile
+  const int J = j0 + 32 * wj + (l & 31);
+  if (J >= nb) return;
+  const bool live = bvalid[size_t(bh) * nb + J] > 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int J = J0 + tx + 16 * j;
-    live[j] = J < nb && bv[J] > 0;
-  }
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int I = I0 + ty + 16 * i;
-    if (I >= nb) continue;
-    float* row = scores + (size_t(bh) * nb + I) * nb;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int J = J0 + tx + 16 * j;
-      if (J < nb) row[J] = live[j] ? acc[i][j] * scale : -INFINITY;
-    }
+  for (int e = 0; e < 16; ++e) {
+    const int r = r0 + 32 * wi + 8 * (e >> 2) + 4 * (l >> 5) + (e & 3);
+    if (r < rows) out[(size_t(bh) * CH + r) * nb + J] = live ? acc[e] * scale : -INFINITY;
   }
 }
 
-
-// One workgroup per query block, the row held in registers: thread t of a TPB-thread
-// workgroup keeps key blocks t, t + TPB, t + 2 TPB, ... (VPT of them), so that the 31-step
-// searches are register passes.  Sums run over each thread's blocks in that order, then
-// across the workgroup, so results are deterministic.  Ascending emission uses wave
-// ballots per round of TPB blocks.  Used for nb <= TPB * VPT (at most 1024 * 32).
+// One workgroup per query block of the chunk, the row held in registers: thread t of a
+// TPB-thread workgroup keeps key blocks t, t + TPB, t + 2 TPB, ... (VPT of them).
+// Probabilities are searched as keys kk = bits(P) + 1 (live) or 0 (dead), bit by bit from
+// the top.  A pass tests one candidate key over the whole row and also counts the values
+// left in the range that the next bits can still split; once that range holds at most
+// kCand values they are compacted to LDS (in thread and register order) and one
+// wavefront finishes the remaining bits over them, adding the fixed total of the values
+// above the range.  Every sum runs in a fixed order, so results are deterministic.
+// Ascending emission uses wave ballots per round of TPB blocks.  nb <= TPB * VPT.
+constexpr int kCand = 64;  // one per lane of the finishing wavefront
 __device__ __forceinline__ int below(uint64_t mask) {  // set bits of mask below this lane
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0));
 }
 template <int TPB, int VPT>
-__global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ scores, const int32_t* __restrict__ bvalid,
-                                                   int nb, prism_select_params prm, int k_max,
-                                                   int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
-                                                   float* __restrict__ sel_margin, uint32_t* __restrict__ bitmap) {
+__global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores, const int32_t* __restrict__ bvalid,
+                                               int nb, int I0, int CH, prism_select_params prm, int k_max,
+                                               int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
+                                               float* __restrict__ sel_margin, uint32_t* __restrict__ rowbits) {
   constexpr int NW = TPB / 64;
   __shared__ float redf[NW];
-  __shared__ int redi[NW];
-  __shared__ float pf[2][NW];  // the search passes alternate between two slots, so one
-  __shared__ int pi[2][NW];    // barrier per pass orders each write after the last reads
-  int par = 0;
-  auto pass_sum = [&](float v) {
-    v = wave_sum(v);
-    if ((threadIdx.x & 63) == 0) pf[par][threadIdx.x >> 6] = v;
-    __syncthreads();
-    float t = 0.f;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) t += pf[par][w2];
-    par ^= 1;
-    return t;
-  };
-  auto pass_sum_i = [&](int v) {
-    v = wave_sum_i(v);
-    if ((threadIdx.x & 63) == 0) pi[par][threadIdx.x >> 6] = v;
-    __syncthreads();
-    int t = 0;
-#pragma unroll
-    for (int w2 = 0; w2 < NW; ++w2) t += pi[par][w2];
-    par ^= 1;
-    return t;
-  };
-  __shared__ int wcnt[2][NW][VPT];  // per wave and round: equal-key count, taken count
-  const int I = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  __shared__ int redi[NW + 1];
+  __shared__ float pv[2][NW][3];  // the passes alternate between two slots, so one barrier
+  int par = 0;                    // per pass orders each write after the last reads
+  __shared__ float cand[kCand];
+  __shared__ float found[4];
+  const int I = I0 + blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* bv = bvalid + size_t(bh) * nb;
   int32_t* out = sel_idx + (size_t(bh) * nb + I) * k_max;
-  if (bv[I] == 0) {
+  if (bv[I] == 0) {  // a dead query block selects nothing: its list and its row of bits
     for (int s = tid; s < k_max; s += TPB) out[s] = -1;
+    uint32_t* rb = rowbits + (size_t(bh) * CH + blockIdx.x) * words32(nb);
+    for (int s = tid; s < words32(nb); s += TPB) rb[s] = 0u;
     if (tid == 0) {
       sel_cnt[size_t(bh) * nb + I] = 0;
       if (sel_margin) sel_margin[size_t(bh) * nb + I] = 1.f;
     }
     return;
   }
-  const float* row = scores + (size_t(bh) * nb + I) * nb;
+  // three sums per pass, each over the workgroup in a fixed order
+  auto pass3 = [&](float& a, float& b, float& c) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    c = wave_sum(c);
+    if (lane == 0) {
+      pv[par][wv][0] = a;
+      pv[par][wv][1] = b;
+      pv[par][wv][2] = c;
+    }
+    __syncthreads();
+    a = b = c = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2) {
+      a += pv[par][w2][0];
+      b += pv[par][w2][1];
+      c += pv[par][w2][2];
+    }
+    par ^= 1;
+  };
+  const float* row = scores + (size_t(bh) * CH + blockIdx.x) * nb;
   float q[VPT];  // logit, then exp, then probability; -1 for dead (or absent) key blocks
   float mx = -INFINITY;
   int nl = 0;
@@ -273,43 +244,127 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
   // Top-p at p >= 1 keeps every live block: no proper prefix of weights summing to 1
   // exceeds 1, and a float32 total that rounds above 1 must not cut the tail.
   const bool cut_p = p < 1.f && tot > p;
-  // The searches run over keys kk = bits(P) + 1 for live blocks and 0 for dead ones, so
-  // they find key + 1.  Probabilities are never -0 and the bit patterns of non-negative
-  // floats are ordered like their values, so for a live block kk >= c is P >= at(c - 1)
-  // and kk == c is P == at(c - 1) (at(u): the float with bits u); a dead block's -1 fails
-  // every such comparison, as its kk = 0 does (c >= 1 throughout).  The searches never
-  // accept a key above that of 1.0, so every threshold compared is finite.  The
-  // comparisons therefore run on q itself and no keys are kept.
+  // For a live block kk >= c is P >= at(c - 1) and kk == c is P == at(c - 1) (at(u): the
+  // float with bits u; probabilities are never -0 and the bit patterns of non-negative
+  // floats are ordered like their values); a dead block's -1 fails every such test, as
+  // its kk = 0 does (c >= 1 throughout).  The searches never accept a key above that of
+  // 1.0 (when the target is at least one block), so every threshold compared is finite.
   auto at = [](uint32_t u) { return __uint_as_float(u); };
+
+  // The largest key T with metric(T) > target (sum of P over kk >= T; top-p) or
+  // metric(T) >= target (count of kk >= T; a count cut), and over kk > T the sum (sg) and
+  // count (cg) and at kk == T the count (ce).  Counts come from wave ballots (exact, and
+  // scalar work); the number of live keys in the open range [Tk, hi) follows from the
+  // counts at its two ends.
+  auto wcount = [&](bool pred) { return int(__builtin_popcountll(__builtin_amdgcn_ballot_w64(pred))); };
+  auto search = [&](bool use_sum, float target, uint32_t& T_out, float& sg, float& cg, float& ce) {
+    auto pass_ok = [&](float m) { return use_sum ? m > target : m >= target; };
+    uint32_t Tk = 0, hi = 0x80000000u;  // the answer lies in [Tk, hi)
+    float c_lo = float(nlive), c_hi = 0.f;  // live keys at or above Tk, at or above hi
+    int bit = 30;
+    bool small = false;
+    for (; bit >= 0; --bit) {
+      const uint32_t cnd = Tk | (1u << bit);
+      const float c = at(cnd - 1u);
+      float m = 0.f, unused = 0.f;
+      int cwi = 0;  // wave-uniform: scalar work
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const bool ge = q[i] >= c;
+        if (use_sum) m += ge ? q[i] : 0.f;
+        cwi += wcount(ge);
+      }
+      float cw = lane == 0 ? float(cwi) : 0.f;
+      pass3(m, cw, unused);
+      if (pass_ok(use_sum ? m : cw)) {
+        Tk = cnd;
+        c_lo = cw;
+      } else {
+        hi = cnd;
+        c_hi = cw;
+      }
+      if (bit > 0 && c_lo - c_hi <= float(kCand)) {
+        small = true;
+        --bit;
+        break;
+      }
+    }
+    if (!small) {  // every bit decided over the registers
+      const float above = at(Tk), equal = at(Tk - 1u);
+      float s1 = 0.f;
+      int c1i = 0, e1i = 0;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        s1 += q[i] >= above ? q[i] : 0.f;
+        c1i += wcount(q[i] >= above);
+        e1i += wcount(q[i] == equal);
+      }
+      float c1 = lane == 0 ? float(c1i) : 0.f, e1 = lane == 0 ? float(e1i) : 0.f;
+      pass3(s1, c1, e1);
+      T_out = Tk;
+      sg = s1;
+      cg = c1;
+      ce = e1;
+      return;
+    }
+    // compact the live values in [Tk, hi) (c_lo - c_hi of them); fs: sum of those above
+    const float lo_v = Tk ? at(Tk - 1u) : 0.f;
+    const bool hi_all = hi > 0x3F800001u;  // every live key is below hi
+    const float hi_v = hi_all ? 0.f : at(hi - 1u);
+    auto in_range = [&](float v) { return v >= 0.f && v >= lo_v && (hi_all || v < hi_v); };
+    int mine = 0;
+    float fs = 0.f, u1 = 0.f, u2 = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      mine += in_range(q[i]);
+      fs += !hi_all && q[i] >= hi_v ? q[i] : 0.f;
+    }
+    int total;
+    int off = block_excl_scan<TPB>(mine, redi, &total);
+    total = min(total, kCand);  // at most c_lo - c_hi <= kCand; NaN scores only lower it
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (in_range(q[i]) && off < kCand) cand[off++] = q[i];
+    pass3(fs, u1, u2);  // its barrier also publishes cand
+    if (wv == 0) {
+      const float v = lane < total ? cand[lane] : -1.f;
+      uint32_t T = Tk;
+      for (int b = bit; b >= 0; --b) {
+        const uint32_t cnd = T | (1u << b);
+        const float c = at(cnd - 1u);
+        const float m = wave_sum(v >= c ? (use_sum ? v : 1.f) : 0.f) + (use_sum ? fs : c_hi);
+        if (pass_ok(m)) T = cnd;
+      }
+      const float above = at(T), equal = at(T - 1u);
+      float s1 = v >= above ? v : 0.f, c1 = v >= above ? 1.f : 0.f, e1 = v == equal ? 1.f : 0.f;
+      s1 = wave_sum(s1) + fs;
+      c1 = wave_sum(c1) + c_hi;
+      e1 = wave_sum(e1);
+      if (lane == 0) {
+        found[0] = __uint_as_float(T);
+        found[1] = s1;
+        found[2] = c1;
+        found[3] = e1;
+      }
+    }
+    __syncthreads();
+    T_out = __float_as_uint(found[0]);
+    sg = found[1];
+    cg = found[2];
+    ce = found[3];
+    __syncthreads();  // found[] and cand[] are free again
+  };
 
   // ---- Top-p: largest key v with sum(P >= v) > p
   int n_p = nlive, need_p = 0;
   uint32_t vstar = 0;
   float sum_gt_p = 0.f;
   if (cut_p) {
-    uint32_t Tk = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = Tk | (1u << bit);
-      const float c = at(cand - 1u);
-      float sm = 0.f;
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) sm += q[i] >= c ? q[i] : 0.f;
-      sm = pass_sum(sm);
-      if (sm > p) Tk = cand;
-    }
+    uint32_t Tk;
+    float sg, cgf, cef;
+    search(true, p, Tk, sg, cgf, cef);
     vstar = Tk - 1u;  // Tk >= 1: all live blocks have kk >= 1 and sum to tot > p
-    float sg = 0.f;
-    int cg = 0, ce = 0;
-    const float above = at(Tk), equal = at(Tk - 1u);  // kk > Tk, kk == Tk
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      sg += q[i] >= above ? q[i] : 0.f;
-      cg += q[i] >= above;
-      ce += q[i] == equal;
-    }
-    sg = block_sum<TPB>(sg, redf);
-    cg = block_sum_i<TPB>(cg, redi);
-    ce = block_sum_i<TPB>(ce, redi);
+    const int cg = int(cgf), ce = int(cef);
     const float v = __uint_as_float(vstar);
     int m = 1;
     while (m < ce && !(sg + float(m) * v > p)) ++m;
@@ -326,22 +381,9 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
     Tcut = vstar + 1u;
     need_eq = need_p;
   } else {
-    uint32_t Tk = 0;
-    for (int bit = 30; bit >= 0; --bit) {
-      const uint32_t cand = Tk | (1u << bit);
-      const float cf = at(cand - 1u);
-      int c = 0;
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) c += q[i] >= cf;
-      c = pass_sum_i(c);
-      if (c >= n) Tk = cand;
-    }
-    Tcut = Tk;
-    int cg = 0;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) cg += q[i] >= at(Tk);
-    cg = block_sum_i<TPB>(cg, redi);
-    need_eq = n - cg;
+    float sg, cgf, cef;
+    search(false, float(n), Tcut, sg, cgf, cef);
+    need_eq = n - int(cgf);
   }
 
   // ---- emit ascending.  Block order is (round i, wave, lane).  Each wave counts its
@@ -349,6 +391,7 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
   // such blocks that precede round i of this wave (a scan over rounds plus the earlier
   // waves of round i), which the lanes of round i read back with readlane.  The same is
   // done for the taken blocks.
+  __shared__ int wcnt[2][NW][VPT];  // per wave and round: equal-key count, taken count
   auto offsets = [&](int k2) {  // lane i < VPT: blocks of kind k2 before (round i, this wave)
     int tot_i = 0, before_i = 0;
     if (lane < VPT) {
@@ -395,15 +438,20 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
   }
   tot_sel = wave_sum_i(tot_sel);
   float pmin_sel = INFINITY, pmax_uns = -INFINITY;
-  uint32_t* bm = bitmap + size_t(bh) * nb * words32(nb);
+  // this query block's row of the chunk's bit matrix: bit J of words32(nb) words, written
+  // whole by the wave whose 64 lanes hold key blocks J0 .. J0 + 63 (J0 a multiple of 64)
+  const int WN = words32(nb);
+  uint32_t* rbits = rowbits + (size_t(bh) * CH + blockIdx.x) * WN;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
     const bool tk = take_at(i);
-    const int pos = __builtin_amdgcn_readlane(tko, i) + below(__builtin_amdgcn_ballot_w64(tk));
+    const uint64_t tkm = __builtin_amdgcn_ballot_w64(tk);
+    const int pos = __builtin_amdgcn_readlane(tko, i) + below(tkm);
     const int J = tid + TPB * i;
+    const int wd = (J - lane) / 32 + (lane >> 5);  // lane 0: low word, lane 32: high word
+    if ((lane & 31) == 0 && wd < WN) rbits[wd] = lane ? uint32_t(tkm >> 32) : uint32_t(tkm);
     if (tk) {
       out[pos] = J;
-      atomicOr(bm + size_t(J) * words32(nb) + (I >> 5), 1u << (I & 31));
       pmin_sel = fminf(pmin_sel, q[i]);
     } else if (q[i] >= 0.f) {  // live
       pmax_uns = fmaxf(pmax_uns, q[i]);
@@ -429,15 +477,29 @@ __global__ __launch_bounds__(TPB) void k_select_reg(const float* __restrict__ sc
   }
 }
 
-__global__ void k_rev_count(const uint32_t* __restrict__ bitmap, int nb, int total_rows,
-                            int32_t* __restrict__ rcnt) {
-  const int r = blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= total_rows) return;
-  const int W = words32(nb);
-  const uint32_t* row = bitmap + size_t(r) * W;
-  int c = 0;
-  for (int w = 0; w < W; ++w) c += __popc(row[w]);
-  rcnt[r] = c;
+// Reverse index, built chunk by chunk.  The selection kernel leaves each query block's
+// selected key blocks as a row of bits (rowbits [BH][CH][words32(nb)]).  One wavefront
+// per (head, 32 key blocks) reads the matching word of every row of the chunk, 64 rows
+// at a time, and turns them into columns with one ballot per key block: lane j then
+// holds the 64 bits of key block 32 gj + j for those rows.  Pass one counts them into the
+// key block's total; pass two (after the scan) lists them.  Every output has one writer.
+__global__ __launch_bounds__(256) void k_col_count(const uint32_t* __restrict__ rowbits, int nb, int CH, int rows,
+                                                   int32_t* __restrict__ rcnt) {
+  const int WN = words32(nb), lane = threadIdx.x & 63;
+  const int gj = blockIdx.x * 4 + (threadIdx.x >> 6), bh = blockIdx.y;
+  if (gj >= WN) return;
+  const uint32_t* rb = rowbits + size_t(bh) * CH * WN + gj;
+  int cnt = 0;
+  for (int r0 = 0; r0 < rows; r0 += 64) {
+    const uint32_t w = r0 + lane < rows ? rb[size_t(r0 + lane) * WN] : 0u;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int c = __builtin_popcountll(__builtin_amdgcn_ballot_w64((w >> j) & 1u));
+      if (lane == j) cnt += c;
+    }
+  }
+  const int J = 32 * gj + lane;
+  if (lane < 32 && J < nb) rcnt[size_t(bh) * nb + J] += cnt;
 }
 
 __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ rcnt, int nb,
@@ -459,76 +521,153 @@ __global__ __launch_bounds__(1024) void k_rev_scan(const int32_t* __restrict__ r
   if (threadIdx.x == 0) rp[nb] = tot;
 }
 
-// One wavefront per (key block, head): lists the set bits of the key block's bitmap row.
-__global__ __launch_bounds__(64) void k_rev_fill(const uint32_t* __restrict__ bitmap, const int32_t* __restrict__ rev_ptr,
-                                                 int nb, int k_max, int32_t* __restrict__ rev_idx) {
-  const int J = blockIdx.x, bh = blockIdx.y, lane = threadIdx.x;
-  const int W = words32(nb);
-  const uint32_t* row = bitmap + (size_t(bh) * nb + J) * W;
-  int base = rev_ptr[size_t(bh) * (nb + 1) + J];
-  int32_t* out = rev_idx + size_t(bh) * nb * k_max;
-  for (int w0 = 0; w0 < W; w0 += 64) {
-    const int w = w0 + lane;
-    const uint32_t word = w < W ? row[w] : 0u;
-    const int pc = __popc(word);
-    int incl = pc;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int nn = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += nn;
-    }
-    int pos = base + incl - pc;
-    uint32_t bits = word;
-    while (bits) {
-      const int b = __ffs(bits) - 1;
-      out[pos++] = w * 32 + b;
-      bits &= bits - 1;
-    }
-    base += __shfl(incl, 63, 64);
+// Pass two: a query block's row of bits again, from its selection list, built in LDS.
+template <int MAXW>
+__global__ __launch_bounds__(256) void k_rowbits(const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+                                                int nb, int k_max, int I0, int CH, uint32_t* __restrict__ rowbits) {
+  __shared__ uint32_t sb[MAXW];
+  const int r = blockIdx.x, bh = blockIdx.y, I = I0 + r;
+  const int WN = words32(nb);
+  for (int w = threadIdx.x; w < WN; w += 256) sb[w] = 0u;
+  __syncthreads();
+  const int n = clampi(sel_cnt[size_t(bh) * nb + I], 0, k_max);
+  const int32_t* lst = sel_idx + (size_t(bh) * nb + I) * k_max;
+  for (int s2 = threadIdx.x; s2 < n; s2 += 256) {
+    const int J = lst[s2];
+    if (J >= 0 && J < nb) atomicOr(&sb[J >> 5], 1u << (J & 31));
   }
+  __syncthreads();
+  uint32_t* out = rowbits + (size_t(bh) * CH + r) * WN;
+  for (int w = threadIdx.x; w < WN; w += 256) out[w] = sb[w];
+}
+
+// As k_col_count, then lane j appends the chunk's query blocks of key block 32 gj + j
+// (ascending) at its cursor.  Chunks run in ascending order of I0, so every reverse list
+// comes out ascending.
+__global__ __launch_bounds__(256) void k_col_fill(const uint32_t* __restrict__ rowbits, const int32_t* __restrict__ rev_ptr,
+                                                  int32_t* __restrict__ cursor, int nb, int k_max, int I0, int CH,
+                                                  int rows, int32_t* __restrict__ rev_idx) {
+  const int WN = words32(nb), lane = threadIdx.x & 63;
+  const int gj = blockIdx.x * 4 + (threadIdx.x >> 6), bh = blockIdx.y;
+  if (gj >= WN) return;
+  const int J = 32 * gj + lane;
+  const bool owner = lane < 32 && J < nb;
+  const uint32_t* rb = rowbits + size_t(bh) * CH * WN + gj;
+  int32_t* out = rev_idx + size_t(bh) * nb * k_max;
+  const int cur = owner ? cursor[size_t(bh) * nb + J] : 0;
+  int pos = owner ? rev_ptr[size_t(bh) * (nb + 1) + J] + cur : 0;
+  int added = 0;
+  for (int r0 = 0; r0 < rows; r0 += 64) {
+    const uint32_t w = r0 + lane < rows ? rb[size_t(r0 + lane) * WN] : 0u;
+    uint64_t col = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64((w >> j) & 1u);
+      if (lane == j) col = m;
+    }
+    if (owner) {
+      while (col) {
+        const int b = __builtin_ctzll(col);
+        out[pos++] = I0 + r0 + b;
+        ++added;
+        col &= col - 1;
+      }
+    }
+  }
+  if (owner) cursor[size_t(bh) * nb + J] = cur + added;
 }
 
 }  // namespace
 
-size_t select_ws_bytes(int BH, int nb, int d, bool with_pooled) {
-  return (with_pooled ? 2 * align256(size_t(BH) * nb * d * 4) : 0) + align256(size_t(BH) * nb * nb * 4) +
-         align256(size_t(BH) * nb * words32(nb) * 4) + align256(size_t(BH) * nb * 4);
+// Query blocks per chunk of the selection (every head at once): as many as keep the
+// chunk's scores, [BH][CH][nb] float32, within 256 MB (the size of the last-level cache,
+// where they stay between the score and the selection kernels), in multiples of 64 and
+// never fewer than 512.  The workspace is therefore bounded by max(256 MB, 2 KB * BH *
+// nb) plus terms linear in nb: it grows linearly with nb, never as nb^2.
+constexpr size_t kSelChunkBytes = size_t(256) << 20;
+constexpr int kSelChunkMin = 512;
+static int sel_chunk(int BH, int nb) {
+  const size_t fit = kSelChunkBytes / (size_t(BH) * nb * 4) / 64 * 64;
+  const int ch = int(fit > size_t(kSelChunkMin) ? (fit < size_t(nb) ? fit : size_t(nb)) : size_t(kSelChunkMin));
+  return ch < nb ? ch : nb;
 }
 
-// Scores, hybrid cut and reverse index from pooled means qbar, kbar [BH][nb][d] float32.
+// Workspace layout: [pooled Q, pooled K,] chunk scores, chunk row bits, reverse counts,
+// reverse cursors.  The pooled means are absent when the caller
+// passes them in (prism_select_blocks_pooled).
+static SelWs carve(void* ws, int BH, int nb, int d, bool with_pooled) {
+  char* p = static_cast<char*>(ws);
+  const int CH = sel_chunk(BH, nb);
+  SelWs w{};
+  if (with_pooled) {
+    w.qbar = reinterpret_cast<float*>(p);
+    p += align256(size_t(BH) * nb * d * 4);
+    w.kbar = reinterpret_cast<float*>(p);
+    p += align256(size_t(BH) * nb * d * 4);
+  }
+  w.scores = reinterpret_cast<float*>(p);
+  p += align256(size_t(BH) * CH * nb * 4);
+  w.rowbits = reinterpret_cast<uint32_t*>(p);
+  p += align256(size_t(BH) * CH * words32(nb) * 4);
+  w.rcnt = reinterpret_cast<int32_t*>(p);
+  p += align256(size_t(BH) * nb * 4);
+  w.cursor = reinterpret_cast<int32_t*>(p);
+  return w;
+}
+
+size_t select_ws_bytes(int BH, int nb, int d, bool with_pooled) {
+  const int CH = sel_chunk(BH, nb);
+  return (with_pooled ? 2 * align256(size_t(BH) * nb * d * 4) : 0) + align256(size_t(BH) * CH * nb * 4) +
+         align256(size_t(BH) * CH * words32(nb) * 4) + 2 * align256(size_t(BH) * nb * 4);
+}
+
+template <int TPB, int VPT>
+static void launch_select_chunk(const SelWs& w, const int32_t* bvalid, int BH, int nb, int I0, int rows, int CH,
+                                const prism_select_params& p, int32_t* sel_idx, int32_t* sel_cnt, float* sel_margin,
+                                hipStream_t s) {
+  hipLaunchKernelGGL((k_select<TPB, VPT>), dim3(rows, BH), dim3(TPB), 0, s, w.scores, bvalid, nb, I0, CH, p, p.k_max,
+                     sel_idx, sel_cnt, sel_margin, w.rowbits);
+}
+
+// Scores, hybrid cut and reverse index from pooled means qbar, kbar [BH][nb][d] float32,
+// one chunk of query blocks at a time.
 static void launch_select_core(const float* qbar, const float* kbar, const int32_t* bvalid, int BH, int nb, int d,
                                float scale, const prism_select_params& p, int32_t* sel_idx, int32_t* sel_cnt,
                                int32_t* rev_ptr, int32_t* rev_idx, float* sel_margin, const SelWs& w, hipStream_t s) {
-  const size_t nbits = size_t(BH) * nb * words32(nb);
-  hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, w.bitmap, nbits, 0u);
+  const int CH = sel_chunk(BH, nb), WN = words32(nb), rows_all = BH * nb;
+  const dim3 cols((WN + 3) / 4, BH);  // one wavefront per 32 key blocks
+  hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(w.rcnt), size_t(rows_all), 0u);
+  hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(w.cursor), size_t(rows_all),
+                     0u);
   hipLaunchKernelGGL(k_fill_u32, dim3(1024), dim3(256), 0, s, reinterpret_cast<uint32_t*>(rev_idx),
                      size_t(BH) * nb * p.k_max, 0xffffffffu);
-  const int tiles = (nb + kScT - 1) / kScT;
-  hipLaunchKernelGGL(k_scores, dim3(tiles, tiles, BH), dim3(256), 0, s, qbar, kbar, bvalid, nb, d, scale, w.scores);
-  // Workgroup shapes as measured fastest: 256 lanes up to 32 blocks each, then 512 lanes of
-  // 32 (at 64 per lane the register file allows one wave per SIMD), then 1024 lanes of 32
-  // (at most 128 registers per lane, which the kernel fits).  nb <= 1024 * 32 is checked
-  // by the caller.
-  const dim3 sg(nb, BH);
-  if (nb <= 256 * 8)
-    hipLaunchKernelGGL((k_select_reg<256, 8>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
-                       sel_cnt, sel_margin, w.bitmap);
-  else if (nb <= 256 * 16)
-    hipLaunchKernelGGL((k_select_reg<256, 16>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
-                       sel_cnt, sel_margin, w.bitmap);
-  else if (nb <= 256 * 32)
-    hipLaunchKernelGGL((k_select_reg<256, 32>), sg, dim3(256), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
-                       sel_cnt, sel_margin, w.bitmap);
-  else if (nb <= 512 * 32)
-    hipLaunchKernelGGL((k_select_reg<512, 32>), sg, dim3(512), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
-                       sel_cnt, sel_margin, w.bitmap);
-  else
-    hipLaunchKernelGGL((k_select_reg<1024, 32>), sg, dim3(1024), 0, s, w.scores, bvalid, nb, p, p.k_max, sel_idx,
-                       sel_cnt, sel_margin, w.bitmap);
-  const int rows = BH * nb;
-  hipLaunchKernelGGL(k_rev_count, dim3((rows + 255) / 256), dim3(256), 0, s, w.bitmap, nb, rows, w.rcnt);
+  for (int I0 = 0; I0 < nb; I0 += CH) {
+    const int rows = min(CH, nb - I0);
+    hipLaunchKernelGGL(k_scores, dim3((nb + kScT - 1) / kScT, (rows + kScT - 1) / kScT, BH), dim3(256), 0, s, qbar,
+                       kbar, bvalid, nb, d, scale, I0, rows, CH, w.scores);
+    // Workgroup shapes as measured fastest: 256 lanes up to 32 blocks each, then 512 lanes
+    // of 32 (at 64 per lane the register file allows one wave per SIMD), then 1024 lanes of
+    // 32.  nb <= 1024 * 32 is checked by the caller.
+    if (nb <= 256 * 8)
+      launch_select_chunk<256, 8>(w, bvalid, BH, nb, I0, rows, CH, p, sel_idx, sel_cnt, sel_margin, s);
+    else if (nb <= 256 * 16)
+      launch_select_chunk<256, 16>(w, bvalid, BH, nb, I0, rows, CH, p, sel_idx, sel_cnt, sel_margin, s);
+    else if (nb <= 256 * 32)
+      launch_select_chunk<256, 32>(w, bvalid, BH, nb, I0, rows, CH, p, sel_idx, sel_cnt, sel_margin, s);
+    else if (nb <= 512 * 32)
+      launch_select_chunk<512, 32>(w, bvalid, BH, nb, I0, rows, CH, p, sel_idx, sel_cnt, sel_margin, s);
+    else
+      launch_select_chunk<1024, 32>(w, bvalid, BH, nb, I0, rows, CH, p, sel_idx, sel_cnt, sel_margin, s);
+    hipLaunchKernelGGL(k_col_count, cols, dim3(256), 0, s, w.rowbits, nb, CH, rows, w.rcnt);
+  }
   hipLaunchKernelGGL(k_rev_scan, dim3(BH), dim3(1024), 0, s, w.rcnt, nb, rev_ptr);
-  hipLaunchKernelGGL(k_rev_fill, dim3(nb, BH), dim3(64), 0, s, w.bitmap, rev_ptr, nb, p.k_max, rev_idx);
+  for (int I0 = 0; I0 < nb; I0 += CH) {
+    const int rows = min(CH, nb - I0);
+    hipLaunchKernelGGL(k_rowbits<kMaxSelectNb / 32>, dim3(rows, BH), dim3(256), 0, s, sel_idx, sel_cnt, nb, p.k_max,
+                       I0, CH, w.rowbits);
+    hipLaunchKernelGGL(k_col_fill, cols, dim3(256), 0, s, w.rowbits, rev_ptr, w.cursor, nb, p.k_max, I0, CH, rows,
+                       rev_idx);
+  }
 }
 
 hipError_t launch_select(const void* qp, const void* kp, prism_dtype dt, const int32_t* bvalid,

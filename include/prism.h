@@ -232,7 +232,10 @@ prism_status prism_permute_pool(const void* x, void* y, prism_dtype dtype, int B
  *          block, the query blocks that selected it, ascending (-1 padded).
  * sel_margin optional out float [B][Hh][nb]: smallest relative distance of the row's
  *          decision from flipping (gap at the cut, distance of the cumulative sum to p).
- * workspace    device scratch of prism_select_workspace_size() bytes. */
+ * workspace    device scratch of prism_select_workspace_size() bytes: the pooled means,
+ *          the float32 scores of one chunk of query blocks at a time (as many per head as
+ *          fit 256 MB, at least 512), that chunk's selection bits and two ints per key
+ *          block; linear in nb (no nb x nb matrix is formed). */
 size_t prism_select_workspace_size(int B, int Hh, int nb, int d);
 prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dtype,
                                  const int32_t* block_valid, int B, int Hh, int nb, int vol, int d,

@@ -95,6 +95,24 @@ def test_attention_workspace_holds_the_schedules(lib):
     assert api.prism_dense_fwd_workspace_size(1, 4, 1000, 128, torch.bfloat16) == 2 * 256 + a256(4 * 1000 * 128 * 2)
 
 
+def test_select_workspace_is_linear_in_nb(lib):
+    """Selection scores one chunk of query blocks at a time: as many per head as keep
+    the chunk's scores ([B*Hh][CH][nb] float32) within 256 MB, in multiples of 64, never
+    fewer than 512 (or nb).  With that chunk's selection bits (a row of words32(nb) words
+    per query block), plus reverse counts and cursors (one int each per key block), the
+    workspace grows linearly with nb, never as nb^2."""
+    from content_adaptive_block_zone_amd import api
+    a256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    w32 = lambda x: (x + 31) // 32  # noqa: E731
+    for BH, nb in ((4, 5760), (4, 15360), (2, 300), (4, 32768)):
+        ch = min(nb, max(512, (256 << 20) // (BH * nb * 4) // 64 * 64))
+        want = a256(BH * ch * nb * 4) + a256(BH * ch * w32(nb) * 4) + 2 * a256(BH * nb * 4)
+        assert api.prism_select_pooled_workspace_size(1, BH, nb) == want
+        assert api.prism_select_workspace_size(1, BH, nb, 128) == want + 2 * a256(BH * nb * 128 * 4)
+    assert api.prism_select_pooled_workspace_size(1, 4, 32768) <= 2.01 * api.prism_select_pooled_workspace_size(1, 4, 16384)
+    assert api.prism_select_pooled_workspace_size(1, 4, 15360) < (280 << 20)   # the scores: 256 MB at most
+
+
 def _status(fn, *args):
     return fn(*args)
 
