@@ -166,6 +166,57 @@ def summarize_profile(stats_dir, fetch_dir, write_dir, commands):
     print("\n".join(lines))
 
 
+def summarize_counters(sqa, sqb, l2, lat, pairs, commands):
+    """Text summary of the four counter runs of the benchmark (two passes of SQ counters,
+    L2 hits and misses, L2-to-fabric read requests with their in-flight level) for the
+    attention kernels, per launch, averaged over the launches (to stdout)."""
+    per = {}
+    for d in (sqa, sqb, l2, lat):
+        for kname, disp, cname, val in _rocpd(d).execute(
+                "select kernel_name, dispatch_id, counter_name, value from counters_collection"):
+            k = per.setdefault(_short(kname), {})
+            c = k.setdefault(cname, {})
+            c[disp] = c.get(disp, 0.0) + float(val)
+    avg = {k: {c: sum(v.values()) / len(v) for c, v in cs.items()} for k, cs in per.items()}
+    lines = ["# Commands (one MI355X, repository root as working copy; rocprofv3 runs with TMPDIR=/tmp)"]
+    lines += [f"#   {c}" for c in commands]
+    lines += [f"# 2K-like workload ({pairs:,} selected block pairs), per launch, averaged over the launches.",
+              "# GRBM_GUI_ACTIVE is summed over the 8 XCDs: cycles = GRBM_GUI_ACTIVE / 8.",
+              "#   MFMA check    = SQ_INSTS_MFMA / (pairs x products per pair: 64 forward, 128 dK/dV, 96 dQ)",
+              "#   MFMA busy     = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles)",
+              "#   LDS active    = SQ_LDS_IDX_ACTIVE / (256 CUs x cycles)",
+              "#   LDS conflicts = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE",
+              "#   wait any      = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES (wave cycles waiting on a dependency)",
+              "#   wait LDS      = SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES",
+              "#   L2 hit        = TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum)",
+              "#   read latency  = TCC_EA0_RDREQ_LEVEL_sum / TCC_EA0_RDREQ_sum (mean cycles an L2 read miss is in flight)"]
+    hdr = (f"{'kernel':12s} {'cycles':>10s} {'MFMA check':>10s} {'MFMA busy':>9s} {'LDS active':>10s} "
+           f"{'LDS confl':>9s} {'wait any':>8s} {'wait LDS':>8s} {'LDS FIFO full':>13s} {'L2 hit':>6s} "
+           f"{'read lat':>8s}")
+    lines.append(hdr)
+    raw = []
+    for bench_name, sym in KERNEL_SYMBOL.items():
+        a = avg.get(sym)
+        if not a:
+            continue
+        g = lambda c: a.get(c, float("nan"))  # noqa: E731
+        cyc = g("GRBM_GUI_ACTIVE") / 8.0
+        mchk = g("SQ_INSTS_MFMA") / (pairs * MFMA_PER_PAIR[bench_name])
+        hit = g("TCC_HIT_sum") / (g("TCC_HIT_sum") + g("TCC_MISS_sum"))
+        lat = g("TCC_EA0_RDREQ_LEVEL_sum") / g("TCC_EA0_RDREQ_sum")
+        lines.append(f"{sym:12s} {cyc:10.3e} {mchk:10.4f} {g('SQ_VALU_MFMA_BUSY_CYCLES') / (1024 * cyc):9.3f} "
+                     f"{g('SQ_LDS_IDX_ACTIVE') / (256 * cyc):10.3f} "
+                     f"{g('SQ_LDS_BANK_CONFLICT') / g('SQ_LDS_IDX_ACTIVE'):9.4f} "
+                     f"{g('SQ_WAIT_INST_ANY') / g('SQ_WAVE_CYCLES'):8.3f} "
+                     f"{g('SQ_WAIT_INST_LDS') / g('SQ_WAVE_CYCLES'):8.3f} {g('SQ_LDS_DATA_FIFO_FULL'):13.3e} "
+                     f"{hit:6.3f} {lat:8.0f}")
+        raw.append(f"# {sym}: " + ", ".join(f"{c} {v:.4e}" for c, v in sorted(a.items())))
+    lines.append("")
+    lines.append("# Raw counters per launch")
+    lines += raw
+    print("\n".join(lines))
+
+
 def parse_ablation(spec: str, w):
     """Layer settings for an ablation run (Table 7: Top-k only / Top-p only; Table 9:
     fixed or random shapes, query/key features, global variance), comma-separated:
@@ -216,10 +267,10 @@ def density(L):
     return float(per_head.mean().item())
 
 
-MFMA_PER_PAIR = {"sparse_attn_fwd": 96, "sparse_attn_bwd_dkdv": 128, "sparse_attn_bwd_dq": 96}
-"""v_mfma_f32_32x32x16_bf16 products (32768 flops each) issued per selected 64x64 block pair:
-forward 2 x 32 (S, then P V with P as a bf16 head and remainder: 64), dK/dV 128 (S, dP,
-dV, dK), dQ 96 (S and dP recomputed, then dQ)."""
+MFMA_PER_PAIR = {"sparse_attn_fwd": 64, "sparse_attn_bwd_dkdv": 128, "sparse_attn_bwd_dq": 96}
+"""32x32x16 matrix-core products (32768 flops each) issued per selected 64x64 block pair:
+forward 64 (32 for S in bf16, 32 for P V in fp16), dK/dV 128 (S, dP, dV, dK), dQ 96 (S
+and dP recomputed, then dQ)."""
 
 
 def flush_cache(buf):
@@ -667,12 +718,18 @@ def main():
     ap.add_argument("--cpu-blocks", type=int, default=16)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one elementwise pass y = -x over this many MiB after warm-up (counter calibration)")
+    ap.add_argument("--summarize-counters", nargs=5, metavar=("SQA", "SQB", "L2", "LAT", "PAIRS"),
+                    help="print the counter summary of four rocprofv3 --pmc runs of the benchmark")
     ap.add_argument("--summarize-profile", nargs="+", metavar="DIR",
                     help="print a text summary of rocprofv3 output directories and exit (no GPU): STATS_DIR "
                          "[FETCH_DIR WRITE_DIR]")
     ap.add_argument("--profile-command", action="append", default=[],
                     help="command line recorded in the summary (repeatable)")
     args = ap.parse_args()
+    if args.summarize_counters:
+        d = args.summarize_counters
+        summarize_counters(d[0], d[1], d[2], d[3], int(d[4]), args.profile_command)
+        return
     if args.summarize_profile:
         dirs = list(args.summarize_profile) + [None, None]
         summarize_profile(dirs[0], dirs[1], dirs[2], args.profile_command)
