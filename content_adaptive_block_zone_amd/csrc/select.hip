@@ -106,10 +106,10 @@ void launch_pool(const void* qp, const void* kp, const int32_t* bvalid, int BH, 
 // Scores of one chunk of query rows: out[bh][I - I0][J] = scale * sum_c qbar[bh][I][c]
 // kbar[bh][J][c] for I0 <= I < I0 + rows; dead key blocks (no valid token) get -inf.
 // 64x64 tile per workgroup; wave (wi, wj) forms rows 32wi.., columns 32wj.. with
-// v_mfma_f32_32x32x2_f32 (float32 products and sums), c in chunks of 16 staged in LDS
-// (rows padded to 17 floats: the 32 rows one product reads fall in distinct banks).
+// v_mfma_f32_32x32x2_f32 (float32 products and sums), c in chunks of 32 staged in LDS
+// (rows padded to 33 floats: the 32 rows one product reads fall in distinct banks).
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int kScT = 64, kScK = 16;
+constexpr int kScT = 64, kScK = 32;
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                 const int32_t* __restrict__ bvalid, int nb, int d, float scale,
                                                 int I0, int rows, int CH, float* __restrict__ out) {
@@ -121,18 +121,29 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
   const float* Q = qbar + (size_t(bh) * nb + I0) * d;
   const float* K = kbar + size_t(bh) * nb * d;
   const int t = threadIdx.x, l = t & 63, w = t >> 6, wi = w & 1, wj = w >> 1;
-  const int sr = t >> 2, sc = (t & 3) * 4;  // staging: row sr, columns sc..sc+3 of each operand
+  const int sr = t >> 3, sc = (t & 7) * 4;  // staging: rows sr, sr + 32, columns sc..sc+3
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
   for (int k0 = 0; k0 < d; k0 += kScK) {
-    const float4 a = r0 + sr < rows ? *reinterpret_cast<const float4*>(Q + size_t(r0 + sr) * d + k0 + sc)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
-    const float4 b = j0 + sr < nb ? *reinterpret_cast<const float4*>(K + size_t(j0 + sr) * d + k0 + sc)
+    // d is a multiple of 16: the second half of a 32-column stage may be past d
+    const bool cin = k0 + sc < d;
+    float4 a[2], b[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = sr + 32 * h;
+      a[h] = cin && r0 + r < rows ? *reinterpret_cast<const float4*>(Q + size_t(r0 + r) * d + k0 + sc)
                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+      b[h] = cin && j0 + r < nb ? *reinterpret_cast<const float4*>(K + size_t(j0 + r) * d + k0 + sc)
+                                : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
     __syncthreads();
-    As[sr][sc] = a.x; As[sr][sc + 1] = a.y; As[sr][sc + 2] = a.z; As[sr][sc + 3] = a.w;
-    Bs[sr][sc] = b.x; Bs[sr][sc + 1] = b.y; Bs[sr][sc + 2] = b.z; Bs[sr][sc + 3] = b.w;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int r = sr + 32 * h;
+      As[r][sc] = a[h].x; As[r][sc + 1] = a[h].y; As[r][sc + 2] = a[h].z; As[r][sc + 3] = a[h].w;
+      Bs[r][sc] = b[h].x; Bs[r][sc + 1] = b[h].y; Bs[r][sc + 2] = b[h].z; Bs[r][sc + 3] = b[h].w;
+    }
     __syncthreads();
 #pragma unroll
     for (int kk = 0; kk < kScK; kk += 2) {
@@ -224,23 +235,32 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
   }
   mx = block_max<TPB>(mx, redf);
   const int nlive = block_sum_i<TPB>(nl, redi);
+  // exp on the hardware base-2 unit and one reciprocal: a few ulps from the correctly
+  // rounded softmax, far inside the 1e-4 relative margin below which a decision counts as
+  // a near-tie
+  constexpr float kLog2e = 1.4426950408889634f;
   float se = 0.f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i) {
-    const float e = q[i] == -INFINITY ? -1.f : expf(q[i] - mx);
+    const float e = q[i] == -INFINITY ? -1.f : __builtin_amdgcn_exp2f((q[i] - mx) * kLog2e);
     q[i] = e;
     if (e >= 0.f) se += e;
   }
   se = block_sum<TPB>(se, redf);
-  float tot = 0.f;
+  const float rse = __builtin_amdgcn_rcpf(se);
+  float tot = 0.f, pmin = INFINITY, pmax = 0.f;
 #pragma unroll
   for (int i = 0; i < VPT; ++i)
     if (q[i] >= 0.f) {
-      q[i] = q[i] / se;
+      q[i] = q[i] * rse;
       tot += q[i];
+      pmin = fminf(pmin, q[i]);
+      pmax = fmaxf(pmax, q[i]);
     }
   const float p = prm.top_p;
   tot = block_sum<TPB>(tot, redf);
+  pmin = -block_max<TPB>(-pmin, redf);
+  pmax = block_max<TPB>(pmax, redf);
   // Top-p at p >= 1 keeps every live block: no proper prefix of weights summing to 1
   // exceeds 1, and a float32 total that rounds above 1 must not cut the tail.
   const bool cut_p = p < 1.f && tot > p;
@@ -262,6 +282,20 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     uint32_t Tk = 0, hi = 0x80000000u;  // the answer lies in [Tk, hi)
     float c_lo = float(nlive), c_hi = 0.f;  // live keys at or above Tk, at or above hi
     int bit = 30;
+    // When the target is met at key 1 (a Top-p cut, or a count of at least one block) the
+    // answer is the key of one of the row's probabilities, so it lies in [key(pmin),
+    // key(pmax)]: the bits these two keys share are the answer's, and the search starts
+    // below them.  Every live key is then at or above Tk and none reaches hi.
+    if (nlive > 0 && (use_sum || target >= 1.f)) {
+      const uint32_t klo = __float_as_uint(pmin) + 1u, khi = __float_as_uint(pmax) + 1u;
+      const int b0 = 31 - __builtin_clz(klo ^ khi | 1u);  // highest differing bit
+      const uint32_t span = b0 >= 31 ? 0u : (1u << (b0 + 1));
+      if (b0 < 30) {
+        Tk = klo & ~(span - 1u);
+        hi = Tk + span;
+        bit = b0;
+      }
+    }
     bool small = false;
     for (; bit >= 0; --bit) {
       const uint32_t cnd = Tk | (1u << bit);
