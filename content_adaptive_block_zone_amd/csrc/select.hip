@@ -4,8 +4,8 @@
 // attention weight exceeds the threshold).
 //
 //   k_pool     mean of each block's valid rows (float32)                 HBM-bound
-//   k_scores   scale * Qbar Kbar^T for one chunk of query blocks, float32 matrix-core
-//              products (v_mfma_f32_32x32x2_f32), 64x64 tiles
+//   k_scores   scale * Qbar Kbar^T for one chunk of query blocks, on the bf16 matrix
+//              cores with float32 accuracy (three-way bf16 split), 64x64 tiles
 //   k_select   per query block, the row of scores in registers: softmax over live key
 //              blocks, then the hybrid count found by bitwise search on the float bits
 //              of the probabilities (no sort): the Top-p threshold is the largest
@@ -105,16 +105,22 @@ void launch_pool(const void* qp, const void* kp, const int32_t* bvalid, int BH, 
 
 // Scores of one chunk of query rows: out[bh][I - I0][J] = scale * sum_c qbar[bh][I][c]
 // kbar[bh][J][c] for I0 <= I < I0 + rows; dead key blocks (no valid token) get -inf.
-// 64x64 tile per workgroup; wave (wi, wj) forms rows 32wi.., columns 32wj.. with
-// v_mfma_f32_32x32x2_f32 (float32 products and sums), c in chunks of 32 staged in LDS
-// (rows padded to 33 floats: the 32 rows one product reads fall in distinct banks).
+// 64x64 tile per workgroup; wave (wi, wj) forms rows 32wi.., columns 32wj.. on the bf16
+// matrix cores (v_mfma_f32_32x32x16_bf16) with float32 accuracy: each float32 operand x
+// is split into three bf16 pieces, x0 = bf16(x), x1 = bf16(x - x0), x2 = bf16(x - x0 -
+// x1) (24 significant bits between them), and a product takes the six piece products
+// x_i y_j with i + j <= 2, each exact in float32 and summed in float32; the terms left
+// out are below 2^-24 of the product.  c runs in chunks of 32, split once while staged in
+// LDS (three planes per operand, rows padded to 80 bytes: the 16-byte reads of the 32
+// rows of one product fall on distinct banks).
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-constexpr int kScT = 64, kScK = 32;
+typedef __bf16 bf16x8s __attribute__((ext_vector_type(8)));
+constexpr int kScT = 64, kScK = 32, kScRow = kScK + 8;
 __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, const float* __restrict__ kbar,
                                                 const int32_t* __restrict__ bvalid, int nb, int d, float scale,
                                                 int I0, int rows, int CH, float* __restrict__ out) {
-  __shared__ float As[kScT][kScK + 1];
-  __shared__ float Bs[kScT][kScK + 1];
+  __shared__ __attribute__((aligned(16))) __bf16 As[3][kScT][kScRow];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[3][kScT][kScRow];
   const int bh = blockIdx.z;
   const int r0 = blockIdx.y * kScT;   // first row of the tile, relative to I0
   const int j0 = blockIdx.x * kScT;
@@ -122,6 +128,12 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
   const float* K = kbar + size_t(bh) * nb * d;
   const int t = threadIdx.x, l = t & 63, w = t >> 6, wi = w & 1, wj = w >> 1;
   const int sr = t >> 3, sc = (t & 7) * 4;  // staging: rows sr, sr + 32, columns sc..sc+3
+  auto split = [](float x, __bf16 (&pc)[3]) {
+    pc[0] = (__bf16)x;
+    const float r1 = x - (float)pc[0];
+    pc[1] = (__bf16)r1;
+    pc[2] = (__bf16)(r1 - (float)pc[1]);
+  };
   f32x16 acc;
 #pragma unroll
   for (int e = 0; e < 16; ++e) acc[e] = 0.f;
@@ -141,15 +153,36 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int r = sr + 32 * h;
-      As[r][sc] = a[h].x; As[r][sc + 1] = a[h].y; As[r][sc + 2] = a[h].z; As[r][sc + 3] = a[h].w;
-      Bs[r][sc] = b[h].x; Bs[r][sc + 1] = b[h].y; Bs[r][sc + 2] = b[h].z; Bs[r][sc + 3] = b[h].w;
+      const float av[4] = {a[h].x, a[h].y, a[h].z, a[h].w}, bv[4] = {b[h].x, b[h].y, b[h].z, b[h].w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        __bf16 pa[3], pb[3];
+        split(av[c], pa);
+        split(bv[c], pb);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          As[i][r][sc + c] = pa[i];
+          Bs[i][r][sc + c] = pb[i];
+        }
+      }
     }
     __syncthreads();
 #pragma unroll
-    for (int kk = 0; kk < kScK; kk += 2) {
-      const float av = As[32 * wi + (l & 31)][kk + (l >> 5)];
-      const float bv = Bs[32 * wj + (l & 31)][kk + (l >> 5)];
-      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
+    for (int s16 = 0; s16 < kScK; s16 += 16) {
+      const int col = s16 + 8 * (l >> 5);
+      bf16x8s x[3], y[3];
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        x[i] = *reinterpret_cast<const bf16x8s*>(&As[i][32 * wi + (l & 31)][col]);
+        y[i] = *reinterpret_cast<const bf16x8s*>(&Bs[i][32 * wj + (l & 31)][col]);
+      }
+      // smallest terms first
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[2], y[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[1], y[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[0], y[2], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[1], y[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[0], y[1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x[0], y[0], acc, 0, 0, 0);
     }
   }
   // lane l, register e: row 8(e/4) + 4(l/32) + e%4, column l%32 of the wave's 32x32 tile
