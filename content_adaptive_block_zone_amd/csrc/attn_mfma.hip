@@ -596,9 +596,17 @@ __global__ __launch_bounds__(NT, 2) void k_dq32(AttnArgs a) {
 // queries 32x.. of each streamed query block for S and dP.  Wave (kh, 0) accumulates dV^T
 // and wave (kh, 1) dK^T of those 32 keys over all 64 queries: after the softmax step the
 // pair swaps halves through LDS (x = 0 hands over its dS, x = 1 its P), so neither keeps a
-// partial sum of the other's output and no reduction is left for the end.  Q, dO, LSE and
-// D stream through two LDS stages, copied without passing through registers.
+// partial sum of the other's output and no reduction is left for the end.  Each wave adds
+// its own query half first, then its partner's.  Q, dO, LSE and D stream through two LDS
+// stages, copied without passing through registers.  The role x is a compile-time
+// parameter of the pair loop (one copy per role), so choosing between P and dS, or Q and
+// dO, costs no instructions; query rows past a block's valid rows get LSE = +inf, so
+// their P and dS come out as exact zeros from the exponential itself.
 constexpr int kMetaCapKV = 1280;  // keeps two workgroups per CU within 160 KB of LDS
+template <int X>
+struct Role {
+  static constexpr int x = X;
+};
 __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char smem[4 * TB + 4 * 2048];
   __shared__ __attribute__((aligned(16))) float sLD[2][4][TR];  // [stage][LSE*log2(e), D, .., ..][row]
@@ -606,8 +614,9 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
   bf16x8* xbuf = reinterpret_cast<bf16x8*>(smem + 4 * TB);  // 2 KB per wave
   int J, bh;
   owner_of<64>(a, a.order_k, J, bh);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
-  const int kh = w & 1, x = w >> 1;
+  const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
+            g = lane >> 5;
+  const int kh = w & 1;
   const int nJ = nrows_of(a, bh, J);
   const size_t k0 = row0_of(a, bh, J);
   const bf16_t* Q = static_cast<const bf16_t*>(a.q);
@@ -632,88 +641,94 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
     kf[s] = gld8(K + (k0 + key) * D + 16 * s + 8 * g, kok);
     vf[s] = gld8(V + (k0 + key) * D + 16 * s + 8 * g, kok);
   }
-  f32x16 acc[4];  // x = 0: dV^T, x = 1: dK^T (rows d = 32t + acc_row32, column key)
-#pragma unroll
-  for (int t = 0; t < 4; ++t) acc[t] = zero16();
   const float sl2 = a.scale * LOG2E;
 
-  // stage st: Q tile at 2st, dO tile at 2st+1 (copied to LDS directly); the LSE or D value
-  // of row `lane` comes through a register (odd waves D, even waves LSE) and is written to
-  // sLD[st][w] before the barrier that opens the stage.
-  float ld = 0.f;
-  int pre = list_first(bl, sMeta);
-  auto issue = [&](int k, int st) {
-    int Ib, n;
-    list_next(a, bh, bl, sMeta, k, pre, Ib, n, a.nrows);
-    const size_t r0 = row0_of(a, bh, Ib);
-    load_tile(Q + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
-    load_tile(Gd + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
-    ld = ((w & 1) ? a.Dbuf : a.lse_in)[r0 + max(min(lane, n - 1), 0)];
-    return n;
+  auto run = [&](auto role) {
+    constexpr int x = decltype(role)::x;
+    f32x16 acc[4];  // x = 0: dV^T, x = 1: dK^T (rows d = 32t + acc_row32, column key)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) acc[t] = zero16();
+    // stage st: Q tile at 2st, dO tile at 2st+1 (copied to LDS directly); the LSE or D
+    // value of row `lane` comes through a register (odd waves D, even waves LSE) and is
+    // written to sLD[st][w] before the barrier that opens the stage.
+    float ld = 0.f;
+    int pre = list_first(bl, sMeta);
+    auto issue = [&](int k, int st) {
+      int Ib, n;
+      list_next(a, bh, bl, sMeta, k, pre, Ib, n, a.nrows);
+      const size_t r0 = row0_of(a, bh, Ib);
+      load_tile(Q + r0 * D, n, reinterpret_cast<uint16_t*>(smem + 2 * st * TB));
+      load_tile(Gd + r0 * D, n, reinterpret_cast<uint16_t*>(smem + (2 * st + 1) * TB));
+      ld = ((w & 1) ? a.Dbuf : a.lse_in)[r0 + max(min(lane, n - 1), 0)];
+      return n;
+    };
+    int n_next = cnt > 0 ? issue(0, 0) : 0;
+    for (int it = 0; it < cnt; ++it) {
+      const int st = it & 1, nIn = n_next;
+      wait_loads();
+      // rows past the valid ones repeat the last valid row (finite); LSE = +inf gives them P = 0
+      sLD[st][w][lane] = (w & 1) ? ld : (lane < nIn ? ld * LOG2E : INFINITY);
+      __syncthreads();
+      if (it + 1 < cnt) n_next = issue(it + 1, st ^ 1);
+      const uint16_t* sQ = reinterpret_cast<const uint16_t*>(smem + 2 * st * TB);
+      const uint16_t* sG = reinterpret_cast<const uint16_t*>(smem + (2 * st + 1) * TB);
+      // LSE and D of this lane's 16 rows (4 runs of 4), read before the products
+      f32x4 lr[4], dr[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        lr[q] = *reinterpret_cast<const f32x4*>(&sLD[st][0][32 * x + 8 * q + 4 * g]);
+        dr[q] = *reinterpret_cast<const f32x4*>(&sLD[st][1][32 * x + 8 * q + 4 * g]);
+      }
+      // S, dP: rows = queries 32x + acc_row32(e, g), column = key
+      f32x16 s_ = zero16(), dp = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        s_ = mma32(lds8<bf16x8>(sQ + tofs(32 * x + l32, 16 * s + 8 * g)), kf[s], s_);
+        dp = mma32(lds8<bf16x8>(sG + tofs(32 * x + l32, 16 * s + 8 * g)), vf[s], dp);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = exp2_fast(s_[e] * sl2 - lr[e >> 2][e & 3]);
+        s_[e] = p;
+        dp[e] = p * (dp[e] - dr[e >> 2][e & 3]);
+      }
+      // own: the operand this wave keeps (P for dV, dS for dK); give: the one its partner needs
+      const f32x16& ownf = x == 0 ? s_ : dp;
+      const f32x16& givef = x == 0 ? dp : s_;
+      const bf16x8 own0 = pack8(ownf, 0), own1 = pack8(ownf, 1);
+      const bf16x8 give0 = pack8(givef, 0), give1 = pack8(givef, 1);
+      // the transposed operands: dO^T for dV, Q^T for dK; rows of the own query half are
+      // the 16-row groups 2x, 2x+1, the partner's 2(1-x), 2(1-x)+1.  The first ones do not
+      // depend on the swap: read them before its barrier, so their LDS latency overlaps the wait
+      const uint16_t* At = x == 0 ? sG : sQ;
+      constexpr int jo = 2 * x, jp = 2 * (1 - x);
+      const auto pre0 = ldtr(At, 0, jo), pre1 = ldtr(At, 0, jo + 1), pre2 = ldtr(At, 0, jp), pre3 = ldtr(At, 0, jp + 1);
+      xbuf[w * 128 + lane] = give0;
+      xbuf[w * 128 + 64 + lane] = give1;
+      __syncthreads();
+      const bf16x8 got0 = xbuf[(w ^ 2) * 128 + lane], got1 = xbuf[(w ^ 2) * 128 + 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] = mma32(t == 0 ? pre0 : ldtr(At, t, jo), own0, acc[t]);
+        acc[t] = mma32(t == 0 ? pre1 : ldtr(At, t, jo + 1), own1, acc[t]);
+        acc[t] = mma32(t == 0 ? pre2 : ldtr(At, t, jp), got0, acc[t]);
+        acc[t] = mma32(t == 0 ? pre3 : ldtr(At, t, jp + 1), got1, acc[t]);
+      }
+    }
+    if (kok || (!a.dense && key < TR)) {
+      const float sc = kok ? (x == 1 ? a.scale : 1.f) : 0.f;
+      bf16_t* out = static_cast<bf16_t*>(x == 1 ? a.dk : a.dv);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) store4_32(out + (k0 + key) * D + 32 * t + 8 * j + 4 * g, acc[t], j, sc);
+    }
   };
-  int n_next = cnt > 0 ? issue(0, 0) : 0;
-  for (int it = 0; it < cnt; ++it) {
-    const int st = it & 1, nIn = n_next;
-    wait_loads();
-    sLD[st][w][lane] = (w & 1) ? ld : ld * LOG2E;
-    __syncthreads();
-    if (it + 1 < cnt) n_next = issue(it + 1, st ^ 1);
-    const uint16_t* sQ = reinterpret_cast<const uint16_t*>(smem + 2 * st * TB);
-    const uint16_t* sG = reinterpret_cast<const uint16_t*>(smem + (2 * st + 1) * TB);
-    // LSE and D of this lane's 16 rows (4 runs of 4), read before the products
-    f32x4 lr[4], dr[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      lr[q] = *reinterpret_cast<const f32x4*>(&sLD[st][0][32 * x + 8 * q + 4 * g]);
-      dr[q] = *reinterpret_cast<const f32x4*>(&sLD[st][1][32 * x + 8 * q + 4 * g]);
-    }
-    // S, dP: rows = queries 32x + acc_row32(e, g), column = key
-    f32x16 s_ = zero16(), dp = zero16();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      s_ = mma32(lds8<bf16x8>(sQ + tofs(32 * x + l32, 16 * s + 8 * g)), kf[s], s_);
-      dp = mma32(lds8<bf16x8>(sG + tofs(32 * x + l32, 16 * s + 8 * g)), vf[s], dp);
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      // rows past nIn repeat row nIn-1 (finite); their p is set to 0
-      const int r = 32 * x + acc_row32(e, g);
-      const float p0 = exp2_fast(s_[e] * sl2 - lr[e >> 2][e & 3]);
-      const float p = r < nIn ? p0 : 0.f;
-      s_[e] = p;
-      dp[e] = p * (dp[e] - dr[e >> 2][e & 3]);
-    }
-    // own: the operand this wave keeps; give: the one its partner (w ^ 2) needs
-    const bf16x8 P0 = pack8(s_, 0), P1 = pack8(s_, 1), S0 = pack8(dp, 0), S1 = pack8(dp, 1);
-    const bf16x8 own0 = x == 0 ? P0 : S0, own1 = x == 0 ? P1 : S1;
-    const bf16x8 give0 = x == 0 ? S0 : P0, give1 = x == 0 ? S1 : P1;
-    // the first transposed operands of the dV/dK products do not depend on the swap: read
-    // them before its barrier, so their LDS latency overlaps the wait
-    const uint16_t* At = x == 0 ? sG : sQ;  // dO^T for dV, Q^T for dK
-    const auto pre0 = ldtr(At, 0, 0), pre1 = ldtr(At, 0, 1), pre2 = ldtr(At, 0, 2), pre3 = ldtr(At, 0, 3);
-    xbuf[w * 128 + lane] = give0;
-    xbuf[w * 128 + 64 + lane] = give1;
-    __syncthreads();
-    const bf16x8 got0 = xbuf[(w ^ 2) * 128 + lane], got1 = xbuf[(w ^ 2) * 128 + 64 + lane];
-    // query half 0 comes from wave x = 0, half 1 from x = 1
-    const bf16x8 lo0 = x == 0 ? own0 : got0, lo1 = x == 0 ? own1 : got1;
-    const bf16x8 hi0 = x == 0 ? got0 : own0, hi1 = x == 0 ? got1 : own1;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      acc[t] = mma32(t == 0 ? pre0 : ldtr(At, t, 0), lo0, acc[t]);
-      acc[t] = mma32(t == 0 ? pre1 : ldtr(At, t, 1), lo1, acc[t]);
-      acc[t] = mma32(t == 0 ? pre2 : ldtr(At, t, 2), hi0, acc[t]);
-      acc[t] = mma32(t == 0 ? pre3 : ldtr(At, t, 3), hi1, acc[t]);
-    }
-  }
-  if (kok || (!a.dense && key < TR)) {
-    const float sc = kok ? (x == 1 ? a.scale : 1.f) : 0.f;
-    bf16_t* out = static_cast<bf16_t*>(x == 1 ? a.dk : a.dv);
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) store4_32(out + (k0 + key) * D + 32 * t + 8 * j + 4 * g, acc[t], j, sc);
-  }
+  // the role is uniform over each wave; both copies pass the same barriers in the same order
+  if ((w >> 1) == 0)
+    run(Role<0>{});
+  else
+    run(Role<1>{});
 }
 
 // ------------------------------------------------------------------ fp16 copy of V
