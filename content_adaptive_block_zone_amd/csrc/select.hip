@@ -200,10 +200,12 @@ __global__ __launch_bounds__(256) void k_scores(const float* __restrict__ qbar, 
 // TPB-thread workgroup keeps key blocks t, t + TPB, t + 2 TPB, ... (VPT of them).
 // Probabilities are searched as keys kk = bits(P) + 1 (live) or 0 (dead), bit by bit from
 // the top.  A pass tests one candidate key over the whole row and also counts the values
-// left in the range that the next bits can still split; once that range holds at most
-// kCand values they are compacted to LDS (in thread and register order) and one
-// wavefront finishes the remaining bits over them, adding the fixed total of the values
-// above the range.  Every sum runs in a fixed order, so results are deterministic.
+// left in the range that the next bits can still split.  Once that range holds at most
+// 4 TPB values they are compacted to LDS (in thread and register order) and the passes
+// continue over them, four per thread, with the fixed sum and count of the values above
+// the range added; once it holds at most kCand, they are compacted again and one
+// wavefront finishes the remaining bits with wave sums.  Every sum runs in a fixed order,
+// so results are deterministic.
 // Ascending emission uses wave ballots per round of TPB blocks.  nb <= TPB * VPT.
 constexpr int kCand = 64;  // one per lane of the finishing wavefront
 __device__ __forceinline__ int below(uint64_t mask) {  // set bits of mask below this lane
@@ -220,6 +222,8 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
   __shared__ float pv[2][NW][3];  // the passes alternate between two slots, so one barrier
   int par = 0;                    // per pass orders each write after the last reads
   __shared__ float cand[kCand];
+  constexpr int NBV = 4, kMid = NBV * TPB;  // middle stage: NBV values per thread
+  __shared__ float mid[kMid];
   __shared__ float found[4];
   const int I = I0 + blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int32_t* bv = bvalid + size_t(bh) * nb;
@@ -329,20 +333,24 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
         bit = b0;
       }
     }
-    bool small = false;
-    for (; bit >= 0; --bit) {
+    // One pass: the metric at candidate key cnd over the values of `vals` (plus the fixed
+    // sum fs0 and count ch0 of the values above them), then the range update.
+    auto step = [&](const auto& vals, float fs0, float ch0) {
+      constexpr int N = sizeof(vals) / sizeof(vals[0]);
       const uint32_t cnd = Tk | (1u << bit);
       const float c = at(cnd - 1u);
       float m = 0.f, unused = 0.f;
       int cwi = 0;  // wave-uniform: scalar work
 #pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        const bool ge = q[i] >= c;
-        if (use_sum) m += ge ? q[i] : 0.f;
+      for (int i = 0; i < N; ++i) {
+        const bool ge = vals[i] >= c;
+        if (use_sum) m += ge ? vals[i] : 0.f;
         cwi += wcount(ge);
       }
       float cw = lane == 0 ? float(cwi) : 0.f;
       pass3(m, cw, unused);
+      m += fs0;
+      cw += ch0;
       if (pass_ok(use_sum ? m : cw)) {
         Tk = cnd;
         c_lo = cw;
@@ -350,76 +358,127 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
         hi = cnd;
         c_hi = cw;
       }
+    };
+    // every bit decided: the sums and counts at the answer
+    auto conclude = [&](const auto& vals, float fs0, float ch0) {
+      constexpr int N = sizeof(vals) / sizeof(vals[0]);
+      const float above = at(Tk), equal = at(Tk - 1u);
+      float s1 = 0.f;
+      int c1i = 0, e1i = 0;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        s1 += vals[i] >= above ? vals[i] : 0.f;
+        c1i += wcount(vals[i] >= above);
+        e1i += wcount(vals[i] == equal);
+      }
+      float c1 = lane == 0 ? float(c1i) : 0.f, e1 = lane == 0 ? float(e1i) : 0.f;
+      pass3(s1, c1, e1);
+      T_out = Tk;
+      sg = s1 + fs0;
+      cg = c1 + ch0;
+      ce = e1;
+    };
+    // the values of `vals` in [Tk, hi) to dst[0 .. cap) in thread and register order; the
+    // sum of those at or above hi is added to fs.  Returns how many were written.
+    auto compact = [&](const auto& vals, float* dst, int cap, float& fs) {
+      constexpr int N = sizeof(vals) / sizeof(vals[0]);
+      const float lo_v = Tk ? at(Tk - 1u) : 0.f;
+      const bool hi_all = hi > 0x3F800001u;  // every live key is below hi
+      const float hi_v = hi_all ? 0.f : at(hi - 1u);
+      auto in_range = [&](float v) { return v >= 0.f && v >= lo_v && (hi_all || v < hi_v); };
+      int mine = 0;
+      float up = 0.f, u1 = 0.f, u2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        mine += in_range(vals[i]);
+        up += !hi_all && vals[i] >= hi_v ? vals[i] : 0.f;
+      }
+      int total;
+      int off = block_excl_scan<TPB>(mine, redi, &total);
+      total = min(total, cap);  // at most c_lo - c_hi <= cap; NaN scores only lower it
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+        if (in_range(vals[i]) && off < cap) dst[off++] = vals[i];
+      pass3(up, u1, u2);  // its barrier also publishes dst
+      fs += up;
+      return total;
+    };
+    // at most kCand values left in range, in cand[]: one wavefront decides the remaining
+    // bits with wave sums, adding the fixed sum fs and count c_hi of the values above
+    auto finish = [&](int total, float fs) {
+      if (wv == 0) {
+        const float v = lane < total ? cand[lane] : -1.f;
+        uint32_t T = Tk;
+        for (int b = bit; b >= 0; --b) {
+          const uint32_t cnd = T | (1u << b);
+          const float c = at(cnd - 1u);
+          const float m = wave_sum(v >= c ? (use_sum ? v : 1.f) : 0.f) + (use_sum ? fs : c_hi);
+          if (pass_ok(m)) T = cnd;
+        }
+        const float above = at(T), equal = at(T - 1u);
+        float s1 = v >= above ? v : 0.f, c1 = v >= above ? 1.f : 0.f, e1 = v == equal ? 1.f : 0.f;
+        s1 = wave_sum(s1) + fs;
+        c1 = wave_sum(c1) + c_hi;
+        e1 = wave_sum(e1);
+        if (lane == 0) {
+          found[0] = __uint_as_float(T);
+          found[1] = s1;
+          found[2] = c1;
+          found[3] = e1;
+        }
+      }
+      __syncthreads();
+      T_out = __float_as_uint(found[0]);
+      sg = found[1];
+      cg = found[2];
+      ce = found[3];
+      __syncthreads();  // found[] and cand[] are free again
+    };
+
+    // Passes over the whole row until at most kMid values remain in range
+    bool done = true;
+    for (; bit >= 0; --bit) {
+      step(q, 0.f, 0.f);
+      if (bit > 0 && c_lo - c_hi <= float(kMid)) {
+        done = false;
+        --bit;
+        break;
+      }
+    }
+    if (done) {
+      conclude(q, 0.f, 0.f);
+      return;
+    }
+    float fs = 0.f;
+    if (c_lo - c_hi <= float(kCand)) {
+      const int ncand = compact(q, cand, kCand, fs);
+      finish(ncand, fs);
+      return;
+    }
+    // then over those values, NBV per thread, the ones above them a fixed sum and count
+    const int nmid = compact(q, mid, kMid, fs);
+    float vb[NBV];
+#pragma unroll
+    for (int k = 0; k < NBV; ++k) {
+      const int j = tid + TPB * k;
+      vb[k] = j < nmid ? mid[j] : -1.f;
+    }
+    const float fs0 = fs, ch0 = c_hi;
+    bool small = false;
+    for (; bit >= 0; --bit) {
+      step(vb, fs0, ch0);
       if (bit > 0 && c_lo - c_hi <= float(kCand)) {
         small = true;
         --bit;
         break;
       }
     }
-    if (!small) {  // every bit decided over the registers
-      const float above = at(Tk), equal = at(Tk - 1u);
-      float s1 = 0.f;
-      int c1i = 0, e1i = 0;
-#pragma unroll
-      for (int i = 0; i < VPT; ++i) {
-        s1 += q[i] >= above ? q[i] : 0.f;
-        c1i += wcount(q[i] >= above);
-        e1i += wcount(q[i] == equal);
-      }
-      float c1 = lane == 0 ? float(c1i) : 0.f, e1 = lane == 0 ? float(e1i) : 0.f;
-      pass3(s1, c1, e1);
-      T_out = Tk;
-      sg = s1;
-      cg = c1;
-      ce = e1;
+    if (!small) {
+      conclude(vb, fs0, ch0);
       return;
     }
-    // compact the live values in [Tk, hi) (c_lo - c_hi of them); fs: sum of those above
-    const float lo_v = Tk ? at(Tk - 1u) : 0.f;
-    const bool hi_all = hi > 0x3F800001u;  // every live key is below hi
-    const float hi_v = hi_all ? 0.f : at(hi - 1u);
-    auto in_range = [&](float v) { return v >= 0.f && v >= lo_v && (hi_all || v < hi_v); };
-    int mine = 0;
-    float fs = 0.f, u1 = 0.f, u2 = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      mine += in_range(q[i]);
-      fs += !hi_all && q[i] >= hi_v ? q[i] : 0.f;
-    }
-    int total;
-    int off = block_excl_scan<TPB>(mine, redi, &total);
-    total = min(total, kCand);  // at most c_lo - c_hi <= kCand; NaN scores only lower it
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (in_range(q[i]) && off < kCand) cand[off++] = q[i];
-    pass3(fs, u1, u2);  // its barrier also publishes cand
-    if (wv == 0) {
-      const float v = lane < total ? cand[lane] : -1.f;
-      uint32_t T = Tk;
-      for (int b = bit; b >= 0; --b) {
-        const uint32_t cnd = T | (1u << b);
-        const float c = at(cnd - 1u);
-        const float m = wave_sum(v >= c ? (use_sum ? v : 1.f) : 0.f) + (use_sum ? fs : c_hi);
-        if (pass_ok(m)) T = cnd;
-      }
-      const float above = at(T), equal = at(T - 1u);
-      float s1 = v >= above ? v : 0.f, c1 = v >= above ? 1.f : 0.f, e1 = v == equal ? 1.f : 0.f;
-      s1 = wave_sum(s1) + fs;
-      c1 = wave_sum(c1) + c_hi;
-      e1 = wave_sum(e1);
-      if (lane == 0) {
-        found[0] = __uint_as_float(T);
-        found[1] = s1;
-        found[2] = c1;
-        found[3] = e1;
-      }
-    }
-    __syncthreads();
-    T_out = __float_as_uint(found[0]);
-    sg = found[1];
-    cg = found[2];
-    ce = found[3];
-    __syncthreads();  // found[] and cand[] are free again
+    const int ncand = compact(vb, cand, kCand, fs);
+    finish(ncand, fs);
   };
 
   // ---- Top-p: largest key v with sum(P >= v) > p
