@@ -748,14 +748,24 @@ __global__ __launch_bounds__(256) void k_vmax(const u32x4* __restrict__ v, size_
   const int bh = blockIdx.y;
   const u32x4* src = v + size_t(bh) * chunks_per_head;
   float m = 0.f;
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < chunks_per_head; i += size_t(gridDim.x) * 256) {
-    const u32x4 u = src[i];
+  auto take = [&](const u32x4& u) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       m = fmaxf(m, fabsf(__uint_as_float(u[j] << 16)));
       m = fmaxf(m, fabsf(__uint_as_float(u[j] & 0xffff0000u)));
     }
+  };
+  // four independent loads in flight per thread, then the remainder one at a time
+  const size_t stride = size_t(gridDim.x) * 256;
+  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 3 * stride < chunks_per_head; i += 4 * stride) {
+    u32x4 u[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) take(u[k]);
   }
+  for (; i < chunks_per_head; i += stride) take(src[i]);
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) atomicMax(vmax + bh, __float_as_uint(m));
 }
@@ -774,8 +784,7 @@ __global__ __launch_bounds__(256) void k_v16(const u32x4* __restrict__ v, u32x4*
   if (blockIdx.x == 0 && threadIdx.x == 0) vinv[bh] = 1.f / sc;  // a power of two: exact
   const u32x4* src = v + size_t(bh) * chunks_per_head;
   u32x4* dst = v16 + size_t(bh) * chunks_per_head;
-  for (size_t i = size_t(blockIdx.x) * 256 + threadIdx.x; i < chunks_per_head; i += size_t(gridDim.x) * 256) {
-    const u32x4 u = src[i];
+  auto conv = [&](const u32x4& u) {
     u32x4 r;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -783,8 +792,18 @@ __global__ __launch_bounds__(256) void k_v16(const u32x4* __restrict__ v, u32x4*
       const _Float16 hi = (_Float16)(__uint_as_float(u[j] & 0xffff0000u) * sc);
       r[j] = uint32_t(__builtin_bit_cast(uint16_t, lo)) | (uint32_t(__builtin_bit_cast(uint16_t, hi)) << 16);
     }
-    dst[i] = r;
+    return r;
+  };
+  const size_t stride = size_t(gridDim.x) * 256;
+  size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  for (; i + 3 * stride < chunks_per_head; i += 4 * stride) {
+    u32x4 u[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) u[k] = src[i + k * stride];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) dst[i + k * stride] = conv(u[k]);
   }
+  for (; i < chunks_per_head; i += stride) dst[i] = conv(src[i]);
 }
 
 // ------------------------------------------------------------------ tile-gather ceiling
