@@ -517,11 +517,45 @@ def run_gpu(args):
             gt.append(e0.elapsed_time(e1))
         del gop
         g_ms = sorted(gt)[1]
+        # The statistics stage against a contiguous read of its input bytes (V and the A2V
+        # output): both with clean caches (median of 3 after an untimed call), and the read
+        # again after the write flush that precedes each stage timing above (dirty lines
+        # then drain to HBM during the read, as after the gradient writes inside the layer).
+        sink = torch.empty(api.PRISM_BENCH_STREAM_SINK, dtype=torch.int32, device=dev)
+        fb = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+
+        def med3(fn, flush=False):
+            fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(3):
+                if flush:
+                    flush_cache(fb)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return sorted(ts)[1]
+        sb = a2v if a2v.numel() * a2v.element_size() == feat.numel() * feat.element_size() else feat
+        s_bytes = 2 * feat.numel() * feat.element_size()
+        s_clean = med3(lambda: api.prism_bench_stream_read(feat, sb, sink))
+        s_flush = med3(lambda: api.prism_bench_stream_read(feat, sb, sink), flush=True)
+        z_clean = med3(lambda: L.zone_stats(feat, sb))
+        del sink, fb
         ceil = dict(mfma_peak_tflops=pk, mfma_peak_frac_of_spec=round(pk / MI355X_BF16_DENSE_TFLOPS, 4),
                     shader_clock_mhz=mhz,
                     fwd_tile_gather_ms=round(g_ms, 4),
                     fwd_tile_gather_gbps=round(kb["sparse_attn_fwd"] / (g_ms * 1e-3) / 1e9, 1),
-                    fwd_over_gather=round(t_fwd / g_ms, 3))
+                    fwd_over_gather=round(t_fwd / g_ms, 3),
+                    stats_read_bytes=int(s_bytes),
+                    stats_stream_ms=round(s_clean, 4),
+                    stats_stream_gbps=round(s_bytes / (s_clean * 1e-3) / 1e9, 1),
+                    stats_stream_after_flush_ms=round(s_flush, 4),
+                    zone_stats_clean_ms=round(z_clean, 4),
+                    zone_stats_clean_gbps=round(s_bytes / (z_clean * 1e-3) / 1e9, 1),
+                    zone_stats_over_stream=round(z_clean / s_clean, 3))
         log(f"[bench] ceilings: {ceil}")
 
     # dense comparator on the same (unpermuted) inputs, per kernel
@@ -713,7 +747,7 @@ def main():
                          "read the norm map")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-microbench", action="store_true",
-                    help="skip the measured ceilings (matrix-core peak and clock, forward tile gather)")
+                    help="skip the measured ceilings (matrix-core peak and clock, forward tile gather, statistics read)")
     ap.add_argument("--stage-reps", type=int, default=3, help="cold-cache runs per stage for stage_ms")
     ap.add_argument("--cpu-blocks", type=int, default=16)
     ap.add_argument("--copy-mib", type=int, default=0,

@@ -81,6 +81,7 @@ PROTOTYPES = {
     "prism_bench_mfma_peak": (c_int, [c_int, c_int, _P, _P, _P]),
     "prism_bench_tile_gather": (c_int, [_P, _P, _P, c_int, _P, _P, _P, c_int, c_int, c_int, c_int, c_int, c_int, _P,
                                         _P, c_size_t, _P]),
+    "prism_bench_stream_read": (c_int, [_P, _P, c_size_t, _P, _P]),
     "prism_last_error": (c_char_p, []),
 }
 

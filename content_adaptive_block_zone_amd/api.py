@@ -432,6 +432,20 @@ def prism_bench_mfma_peak(workgroups: int, iters: int, clocks: torch.Tensor, sin
           "prism_bench_mfma_peak")
 
 
+PRISM_BENCH_STREAM_SINK = 8192
+
+
+def prism_bench_stream_read(a: torch.Tensor, b: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Reads every byte of a and of b (same size, a multiple of 16 bytes); sink int32
+    [PRISM_BENCH_STREAM_SINK] receives per-wavefront checksums."""
+    nbytes = a.numel() * a.element_size()
+    if b.numel() * b.element_size() != nbytes:
+        raise ValueError("a and b must hold the same number of bytes")
+    check(load().prism_bench_stream_read(_ptr(a, name="a"), _ptr(b, name="b"), nbytes,
+                                         _ptr(sink, torch.int32, (PRISM_BENCH_STREAM_SINK,), "sink"),
+                                         _stream(stream)), "prism_bench_stream_read")
+
+
 def prism_bench_tile_gather(qp, kp, vp, block_valid, sel_idx, sel_cnt, vol: int, op, workspace, stream=None) -> None:
     B, Hh, npad, d = qp.shape
     nb = npad // vol

@@ -529,6 +529,14 @@ prism_status prism_bench_mfma_peak(int workgroups, int iters, uint64_t* clocks, 
   return launched(launch_mfma_peak(workgroups, iters, reinterpret_cast<unsigned long long*>(clocks), sink, stream), who);
 }
 
+prism_status prism_bench_stream_read(const void* a, const void* b, size_t bytes, uint32_t* sink,
+                                    hipStream_t stream) {
+  const char* who = "prism_bench_stream_read";
+  if (!a || !b || !sink) return fail(PRISM_ERR_ARG, "%s: null pointer", who);
+  if (bytes == 0 || bytes % 16 != 0) return fail(PRISM_ERR_ARG, "%s: bytes must be a positive multiple of 16", who);
+  return launched(launch_stream_read(a, b, bytes, sink, stream), who);
+}
+
 prism_status prism_bench_tile_gather(const void* qp, const void* kp, const void* vp, prism_dtype dtype,
                                      const int32_t* block_valid, const int32_t* sel_idx, const int32_t* sel_cnt,
                                      int k_max, int B, int Hh, int nb, int vol, int d, void* op, void* workspace,

@@ -296,6 +296,7 @@ size_t attn_mfma_fwd_ws_bytes(const AttnArgs& a);
 // Measurement kernels (not part of the path): the matrix-core peak and clock, and the
 // forward's tile traffic without arithmetic.
 hipError_t launch_mfma_peak(int workgroups, int iters, unsigned long long* clocks, float* sink, hipStream_t s);
+hipError_t launch_stream_read(const void* a, const void* b, size_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_gather_fwd_mfma(const AttnArgs& a, int32_t* sched, hipStream_t s);
 size_t attn_mfma_sched_bytes(const AttnArgs& a);
 

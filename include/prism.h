@@ -399,6 +399,16 @@ prism_status prism_bench_tile_gather(const void* qp, const void* kp, const void*
                                      int k_max, int B, int Hh, int nb, int vol, int d, void* op, void* workspace,
                                      size_t ws_bytes, hipStream_t stream);
 
+/* prism_bench_stream_read: reads `bytes` bytes of device buffer a and of device buffer b
+ * front to back (2048 workgroups of 256 threads, grid-stride, 16-byte loads, two per
+ * buffer in flight per thread): a plain contiguous read of 2 * bytes, the ceiling that a
+ * memory-bound stage reading as many bytes (zone statistics: V and the A2V output) is
+ * measured against.  sink (device, uint32 [PRISM_BENCH_STREAM_SINK]) receives a checksum
+ * per wavefront, so the loads cannot be removed.  Errors: null pointers, bytes zero or not
+ * a multiple of 16 -> PRISM_ERR_ARG. */
+#define PRISM_BENCH_STREAM_SINK 8192
+prism_status prism_bench_stream_read(const void* a, const void* b, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* Message of the last failed call on this thread ("" if none). */
 const char* prism_last_error(void);
 

@@ -84,6 +84,8 @@ int main(void) {
   expect("tiles_mixed(max_units 65)",
          prism_blocks_to_tiles_mixed(I, I, I, I, I, 1, 1, 16, 8, 65, I, I, I, I, P, (size_t)-1, 0), PRISM_ERR_ARG);
   expect("bench_mfma(workgroups 0)", prism_bench_mfma_peak(0, 1, (uint64_t*)P, F, 0), PRISM_ERR_ARG);
+  expect("bench_stream(bytes not a multiple of 16)", prism_bench_stream_read(P, P, 1000, (uint32_t*)P, 0), PRISM_ERR_ARG);
+  expect("bench_stream(null sink)", prism_bench_stream_read(P, P, 1 << 20, NULL, 0), PRISM_ERR_ARG);
   printf("%d unexpected statuses\n", failures);
   return failures ? 1 : 0;
 }

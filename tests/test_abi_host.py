@@ -202,6 +202,9 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_ARG),                                                             # workspace too small
         ("prism_select_blocks_pooled", (P, P, P, 1, 2, 32769, 64, 0.125, sel, P, P, P, P, None, P, 1 << 44, None),
          E.PRISM_ERR_SHAPE),
+        ("prism_bench_stream_read", (P, None, 1 << 20, P, None), E.PRISM_ERR_ARG),
+        ("prism_bench_stream_read", (P, P, 1000, P, None), E.PRISM_ERR_ARG),            # not a multiple of 16
+        ("prism_bench_stream_read", (P, P, 0, P, None), E.PRISM_ERR_ARG),
     ]
     for name, args, want in cases:
         st = getattr(lib, name)(*args)
