@@ -217,7 +217,6 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
                                                int32_t* __restrict__ sel_idx, int32_t* __restrict__ sel_cnt,
                                                float* __restrict__ sel_margin, uint32_t* __restrict__ rowbits) {
   constexpr int NW = TPB / 64;
-  __shared__ float redf[NW];
   __shared__ int redi[NW + 1];
   __shared__ float pv[2][NW][3];  // the passes alternate between two slots, so one barrier
   int par = 0;                    // per pass orders each write after the last reads
@@ -238,26 +237,33 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     }
     return;
   }
-  // three sums per pass, each over the workgroup in a fixed order
-  auto pass3 = [&](float& a, float& b, float& c) {
-    a = wave_sum(a);
-    b = wave_sum(b);
-    c = wave_sum(c);
+  // three reductions over the workgroup behind one barrier (op 0: sum, 1: max, 2: min);
+  // sums run over the waves in a fixed order
+  auto wred = [&](float v, int op) { return op == 0 ? wave_sum(v) : op == 1 ? wave_max(v) : -wave_max(-v); };
+  auto comb = [](float acc, float v, int op) { return op == 0 ? acc + v : op == 1 ? fmaxf(acc, v) : fminf(acc, v); };
+  auto red3 = [&](float& a, float& b, float& c, int oa, int ob, int oc) {
+    a = wred(a, oa);
+    b = wred(b, ob);
+    c = wred(c, oc);
     if (lane == 0) {
       pv[par][wv][0] = a;
       pv[par][wv][1] = b;
       pv[par][wv][2] = c;
     }
     __syncthreads();
-    a = b = c = 0.f;
+    auto init = [](int op) { return op == 0 ? 0.f : op == 1 ? -INFINITY : INFINITY; };
+    a = init(oa);
+    b = init(ob);
+    c = init(oc);
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) {
-      a += pv[par][w2][0];
-      b += pv[par][w2][1];
-      c += pv[par][w2][2];
+      a = comb(a, pv[par][w2][0], oa);
+      b = comb(b, pv[par][w2][1], ob);
+      c = comb(c, pv[par][w2][2], oc);
     }
     par ^= 1;
   };
+  auto pass3 = [&](float& a, float& b, float& c) { red3(a, b, c, 0, 0, 0); };
   const float* row = scores + (size_t(bh) * CH + blockIdx.x) * nb;
   float q[VPT];  // logit, then exp, then probability; -1 for dead (or absent) key blocks
   float mx = -INFINITY;
@@ -270,8 +276,9 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     mx = fmaxf(mx, l);
     nl += l != -INFINITY;
   }
-  mx = block_max<TPB>(mx, redf);
-  const int nlive = block_sum_i<TPB>(nl, redi);
+  float nlf = float(nl), unused0 = 0.f;  // counts up to 32768: exact in float
+  red3(mx, nlf, unused0, 1, 0, 0);
+  const int nlive = int(nlf);
   // exp on the hardware base-2 unit and one reciprocal: a few ulps from the correctly
   // rounded softmax, far inside the 1e-4 relative margin below which a decision counts as
   // a near-tie
@@ -283,7 +290,10 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     q[i] = e;
     if (e >= 0.f) se += e;
   }
-  se = block_sum<TPB>(se, redf);
+  {
+    float u1 = 0.f, u2 = 0.f;
+    pass3(se, u1, u2);
+  }
   const float rse = __builtin_amdgcn_rcpf(se);
   float tot = 0.f, pmin = INFINITY, pmax = 0.f;
 #pragma unroll
@@ -295,9 +305,7 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
       pmax = fmaxf(pmax, q[i]);
     }
   const float p = prm.top_p;
-  tot = block_sum<TPB>(tot, redf);
-  pmin = -block_max<TPB>(-pmin, redf);
-  pmax = block_max<TPB>(pmax, redf);
+  red3(tot, pmin, pmax, 0, 2, 1);
   // Top-p at p >= 1 keeps every live block: no proper prefix of weights summing to 1
   // exceeds 1, and a float32 total that rounds above 1 must not cut the tail.
   const bool cut_p = p < 1.f && tot > p;
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
   };
 
   // ---- Top-p: largest key v with sum(P >= v) > p
-  int n_p = nlive, need_p = 0;
+  int n_p = nlive, need_p = 0, ce_p = 0;
   uint32_t vstar = 0;
   float sum_gt_p = 0.f;
   if (cut_p) {
@@ -491,6 +499,7 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     search(true, p, Tk, sg, cgf, cef);
     vstar = Tk - 1u;  // Tk >= 1: all live blocks have kk >= 1 and sum to tot > p
     const int cg = int(cgf), ce = int(cef);
+    ce_p = ce;
     const float v = __uint_as_float(vstar);
     int m = 1;
     while (m < ce && !(sg + float(m) * v > p)) ++m;
@@ -502,14 +511,16 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
 
   // ---- cut threshold (as kk) for exactly n kept blocks
   uint32_t Tcut;
-  int need_eq;
+  int need_eq, ce_cut;  // blocks to keep at the cut's key, and how many have it
   if (n == n_p && cut_p) {
     Tcut = vstar + 1u;
     need_eq = need_p;
+    ce_cut = ce_p;
   } else {
     float sg, cgf, cef;
     search(false, float(n), Tcut, sg, cgf, cef);
     need_eq = n - int(cgf);
+    ce_cut = int(cef);
   }
 
   // ---- emit ascending.  Block order is (round i, wave, lane).  Each wave counts its
@@ -537,15 +548,22 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     return incl - tot_i + before_i;
   };
   const float cut_eq = at(Tcut - 1u), cut_above = at(Tcut);  // kk == Tcut, kk > Tcut
+  // When every block at the cut's key is kept (all but exact ties split by the cut), the
+  // taken set is P >= cut_eq and the ranks of the equal keys are not needed.
+  const bool all_eq = need_eq >= ce_cut;
+  int eqo = 0;
+  if (!all_eq) {
 #pragma unroll
-  for (int i = 0; i < VPT; ++i) {
-    const uint64_t eq = __builtin_amdgcn_ballot_w64(q[i] == cut_eq);
-    if (lane == 0) wcnt[0][wv][i] = __builtin_popcountll(eq);
+    for (int i = 0; i < VPT; ++i) {
+      const uint64_t eq = __builtin_amdgcn_ballot_w64(q[i] == cut_eq);
+      if (lane == 0) wcnt[0][wv][i] = __builtin_popcountll(eq);
+    }
+    __syncthreads();
+    eqo = offsets(0);
   }
-  __syncthreads();
-  const int eqo = offsets(0);
   // taken: above the cut, or at it and among the first need_eq such blocks in block order
   auto take_at = [&](int i) {
+    if (all_eq) return q[i] >= cut_eq;
     const bool isq = q[i] == cut_eq;
     const int rank = __builtin_amdgcn_readlane(eqo, i) + below(__builtin_amdgcn_ballot_w64(isq));
     return q[i] >= cut_above || (isq && rank < need_eq);
@@ -585,8 +603,8 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
   }
   for (int s = tot_sel + tid; s < k_max; s += TPB) out[s] = -1;
   if (sel_margin) {
-    pmin_sel = -block_max<TPB>(-pmin_sel, redf);
-    pmax_uns = block_max<TPB>(pmax_uns, redf);
+    float u = 0.f;
+    red3(pmin_sel, pmax_uns, u, 2, 1, 0);
   }
   if (tid == 0) {
     sel_cnt[size_t(bh) * nb + I] = tot_sel;
