@@ -698,19 +698,23 @@ __global__ __launch_bounds__(NT, 2) void k_dkdv32(AttnArgs a) {
       const bf16x8 own0 = pack8(ownf, 0), own1 = pack8(ownf, 1);
       const bf16x8 give0 = pack8(givef, 0), give1 = pack8(givef, 1);
       // the transposed operands: dO^T for dV, Q^T for dK; rows of the own query half are
-      // the 16-row groups 2x, 2x+1, the partner's 2(1-x), 2(1-x)+1.  The first ones do not
-      // depend on the swap: read them before its barrier, so their LDS latency overlaps the wait
+      // the 16-row groups 2x, 2x+1, the partner's 2(1-x), 2(1-x)+1.  The products with the
+      // own half do not depend on the swap: they run before its barrier, so the matrix
+      // cores work through the wait; the partner's half follows it.
       const uint16_t* At = x == 0 ? sG : sQ;
       constexpr int jo = 2 * x, jp = 2 * (1 - x);
-      const auto pre0 = ldtr(At, 0, jo), pre1 = ldtr(At, 0, jo + 1), pre2 = ldtr(At, 0, jp), pre3 = ldtr(At, 0, jp + 1);
       xbuf[w * 128 + lane] = give0;
       xbuf[w * 128 + 64 + lane] = give1;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        acc[t] = mma32(ldtr(At, t, jo), own0, acc[t]);
+        acc[t] = mma32(ldtr(At, t, jo + 1), own1, acc[t]);
+      }
+      const auto pre2 = ldtr(At, 0, jp), pre3 = ldtr(At, 0, jp + 1);
       __syncthreads();
       const bf16x8 got0 = xbuf[(w ^ 2) * 128 + lane], got1 = xbuf[(w ^ 2) * 128 + 64 + lane];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        acc[t] = mma32(t == 0 ? pre0 : ldtr(At, t, jo), own0, acc[t]);
-        acc[t] = mma32(t == 0 ? pre1 : ldtr(At, t, jo + 1), own1, acc[t]);
         acc[t] = mma32(t == 0 ? pre2 : ldtr(At, t, jp), got0, acc[t]);
         acc[t] = mma32(t == 0 ? pre3 : ldtr(At, t, jp + 1), got1, acc[t]);
       }
