@@ -376,8 +376,8 @@ prism_status prism_dense_attn_bwd(const void* q, const void* k, const void* v, c
                                   void* workspace, size_t ws_bytes, hipEvent_t* marks,
                                   hipStream_t stream);
 
-/* Measurement kernels.  They are not steps of the method: they measure the ceilings the
- * attention kernels are measured against on the GPU at hand.
+/* Measurement kernels.  They are not steps of the method: they give the ceilings that the
+ * attention and statistics kernels are compared with on the GPU at hand.
  *
  * prism_bench_mfma_peak: `workgroups` workgroups of 4 wavefronts, each wave issuing
  * `iters` rounds of four independent v_mfma_f32_32x32x16_bf16 products (32768 flops
