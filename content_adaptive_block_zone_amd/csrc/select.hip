@@ -333,7 +333,7 @@ __global__ __launch_bounds__(TPB) void k_select(const float* __restrict__ scores
     // below them.  Every live key is then at or above Tk and none reaches hi.
     if (nlive > 0 && (use_sum || target >= 1.f)) {
       const uint32_t klo = __float_as_uint(pmin) + 1u, khi = __float_as_uint(pmax) + 1u;
-      const int b0 = 31 - __builtin_clz(klo ^ khi | 1u);  // highest differing bit
+      const int b0 = 31 - __builtin_clz((klo ^ khi) | 1u);  // highest differing bit
       const uint32_t span = b0 >= 31 ? 0u : (1u << (b0 + 1));
       if (b0 < 30) {
         Tk = klo & ~(span - 1u);
