@@ -100,6 +100,15 @@ prism_status check_shapes(const prism_shapes* s, const Geo& g, ShapeTab* out) {
   return PRISM_OK;
 }
 
+// B*Hh heads times `units` workgroups (zones, blocks) per head must fit the launches'
+// 32-bit grid and the kernels' 32-bit per-launch indices
+prism_status check_heads(const char* who, int B, int Hh, int64_t units) {
+  if (int64_t(B) * Hh * units > int64_t(INT32_MAX))
+    return fail(PRISM_ERR_SHAPE, "%s: B*Hh = %lld heads of %lld units each exceed 2^31 - 1 in all", who,
+                (long long)(int64_t(B) * Hh), (long long)units);
+  return PRISM_OK;
+}
+
 bool supported_attn_d(int d) { return d == 64 || d == 128; }
 bool supported_stats_d(int d) { return d == 32 || d == 64 || d == 128 || d == 256; }
 
@@ -132,6 +141,8 @@ static prism_status zone_stats_common(const char* who, bool global_variance, boo
   if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "%s: d=%d not in {32,64,128,256}", who, d);
   Geo g;
   prism_status st = check_grid(grid, &g);
+  if (st != PRISM_OK) return st;
+  st = check_heads(who, B, Hh, g.nZ);
   if (st != PRISM_OK) return st;
   return launched(launch_zone_stats(v, aux, dtype, B * Hh, d, g, global_variance, from_norm, stats, vact, stream),
                   who);
@@ -174,6 +185,8 @@ prism_status prism_assign_shapes(const float* stats, int B, int Hh, const prism_
   ShapeTab t;
   st = check_shapes(shapes, g, &t);
   if (st != PRISM_OK) return st;
+  st = check_heads("prism_assign_shapes", B, Hh, g.nZ);
+  if (st != PRISM_OK) return st;
   if (!t.uniform) return fail(PRISM_ERR_SHAPE, "prism_assign_shapes: candidates of several volumes (use prism_assign_shapes_multi)");
   const prism_shape_params p = *params;
   if (!std::isfinite(p.alpha) || !std::isfinite(p.tau_lo) || !std::isfinite(p.tau_hi) || !(p.tau_hi > p.tau_lo))
@@ -193,6 +206,8 @@ prism_status prism_assign_shapes_multi(const float* stats, const float* vact, in
   if (st != PRISM_OK) return st;
   ShapeTab t;
   st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  st = check_heads(who, B, Hh, g.nZ);
   if (st != PRISM_OK) return st;
   bool unit_feasible = false;
   for (int c = 0; c < t.n; ++c) {
@@ -223,6 +238,8 @@ prism_status prism_block_heads(const int32_t* unit_valid, const int32_t* shape_i
   ShapeTab t;
   st = check_shapes(shapes, g, &t);
   if (st != PRISM_OK) return st;
+  st = check_heads(who, B, Hh, int64_t(g.nZ) * (g.Vz / t.vol));
+  if (st != PRISM_OK) return st;
   return launched(launch_block_heads(unit_valid, shape_id, B * Hh, g, t, block_valid, stream), who);
 }
 
@@ -240,6 +257,8 @@ prism_status prism_permute(const void* x, void* y, prism_dtype dtype, int B, int
   if (st != PRISM_OK) return st;
   ShapeTab t;
   st = check_shapes(shapes, g, &t);
+  if (st != PRISM_OK) return st;
+  st = check_heads("prism_permute", B, Hh, int64_t(g.nZ) * (g.Vz / t.vol));
   if (st != PRISM_OK) return st;
   return launched(launch_permute(x, y, dtype, B * Hh, d, g, t, shape_id, inverse, block_valid, nullptr, stream),
                   "prism_permute");
@@ -264,6 +283,8 @@ prism_status prism_permute_pool(const void* x, void* y, prism_dtype dtype, int B
   st = check_shapes(shapes, g, &t);
   if (st != PRISM_OK) return st;
   if (!t.uniform) return fail(PRISM_ERR_SHAPE, "%s: candidates of several volumes (blocks span several units)", who);
+  st = check_heads(who, B, Hh, int64_t(g.nZ) * (g.Vz / t.vol));
+  if (st != PRISM_OK) return st;
   return launched(launch_permute(x, y, dtype, B * Hh, d, g, t, shape_id, 0, block_valid, pooled, stream), who);
 }
 
@@ -286,6 +307,7 @@ prism_status prism_select_blocks(const void* qp, const void* kp, prism_dtype dty
     return fail(PRISM_ERR_ARG, "prism_select_blocks: null pointer");
   if (B < 1 || Hh < 1 || nb < 1 || vol < 1) return fail(PRISM_ERR_ARG, "prism_select_blocks: sizes must be >= 1");
   if (nb > kMaxSelectNb) return fail(PRISM_ERR_SHAPE, "prism_select_blocks: nb=%d exceeds %d", nb, kMaxSelectNb);
+  if (check_heads("prism_select_blocks", B, Hh, nb) != PRISM_OK) return PRISM_ERR_SHAPE;
   if (!valid_dtype(dtype)) return fail(PRISM_ERR_DTYPE, "prism_select_blocks: unknown dtype %d", int(dtype));
   if (!supported_stats_d(d)) return fail(PRISM_ERR_DTYPE, "prism_select_blocks: d=%d not in {32,64,128,256}", d);
   const prism_select_params p = *params;
@@ -309,6 +331,7 @@ prism_status prism_select_blocks_pooled(const float* qbar, const float* kbar, co
     return fail(PRISM_ERR_ARG, "%s: null pointer", who);
   if (B < 1 || Hh < 1 || nb < 1) return fail(PRISM_ERR_ARG, "%s: sizes must be >= 1", who);
   if (nb > kMaxSelectNb) return fail(PRISM_ERR_SHAPE, "%s: nb=%d exceeds %d", who, nb, kMaxSelectNb);
+  if (check_heads(who, B, Hh, nb) != PRISM_OK) return PRISM_ERR_SHAPE;
   if (d < 1 || d % 16 != 0 || d > 4096) return fail(PRISM_ERR_DTYPE, "%s: d=%d must be a multiple of 16 up to 4096", who, d);
   const prism_select_params p = *params;
   if (!(p.top_p > 0.f && p.top_p <= 1.f)) return fail(PRISM_ERR_ARG, "%s: top_p must be in (0, 1]", who);

@@ -29,6 +29,9 @@
  *              on that thread).  No C++ exception crosses this interface.
  *   dtypes     PRISM_BF16 (bfloat16 storage, float32 accumulation) or PRISM_F32.
  *              Statistics, pooled means, scores, LSE and D are always float32.
+ *   Sizes      B*Hh heads times the zones, blocks or rows a call handles per head must
+ *              stay below 2^31 (the launches' grids and per-launch indices are 32-bit);
+ *              larger calls return PRISM_ERR_SHAPE.
  */
 #ifndef PRISM_H
 #define PRISM_H

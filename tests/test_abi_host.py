@@ -202,6 +202,13 @@ def test_calls_validate_before_launch(lib):
          E.PRISM_ERR_ARG),                                                             # workspace too small
         ("prism_select_blocks_pooled", (P, P, P, 1, 2, 32769, 64, 0.125, sel, P, P, P, P, None, P, 1 << 44, None),
          E.PRISM_ERR_SHAPE),
+        # B*Hh heads x zones (or blocks) per head past 2^31 - 1: the 32-bit launch grids would wrap
+        ("prism_zone_stats", (P, P, F32, 1 << 16, 1 << 14, 64, g, P, None), E.PRISM_ERR_SHAPE),
+        ("prism_assign_shapes", (P, 1 << 16, 1 << 14, g, s, sp, P, None, None), E.PRISM_ERR_SHAPE),
+        ("prism_permute", (P, ctypes.c_void_p(128), F32, 1 << 16, 1 << 12, 64, g, s, P, 0, None, None),
+         E.PRISM_ERR_SHAPE),
+        ("prism_select_blocks_pooled", (P, P, P, 1 << 16, 1 << 8, 1 << 8, 64, 0.125, sel, P, P, P, P, None, P,
+                                        1 << 62, None), E.PRISM_ERR_SHAPE),
         ("prism_bench_stream_read", (P, None, 1 << 20, P, None), E.PRISM_ERR_ARG),
         ("prism_bench_stream_read", (P, P, 1000, P, None), E.PRISM_ERR_ARG),            # not a multiple of 16
         ("prism_bench_stream_read", (P, P, 0, P, None), E.PRISM_ERR_ARG),
