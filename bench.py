@@ -749,7 +749,7 @@ def main():
     ap.add_argument("--no-microbench", action="store_true",
                     help="skip the measured ceilings (matrix-core peak and clock, forward tile gather, statistics read)")
     ap.add_argument("--stage-reps", type=int, default=3, help="cold-cache runs per stage for stage_ms")
-    ap.add_argument("--cpu-blocks", type=int, default=16)
+    ap.add_argument("--cpu-blocks", type=int, default=160)
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one elementwise pass y = -x over this many MiB after warm-up (counter calibration)")
     ap.add_argument("--summarize-counters", nargs=5, metavar=("SQA", "SQB", "L2", "LAT", "PAIRS"),
