@@ -102,8 +102,15 @@ prism_status check_shapes(const prism_shapes* s, const Geo& g, ShapeTab* out) {
 
 // B*Hh heads times `units` workgroups (zones, blocks) per head must fit the launches'
 // 32-bit grid and the kernels' 32-bit per-launch indices
+bool heads_fit(int B, int Hh, int64_t units) {
+  // each factor is bounded first, so that no product below can overflow int64
+  const int64_t heads = int64_t(B) * int64_t(Hh);
+  if (heads > int64_t(INT32_MAX) || units > int64_t(INT32_MAX)) return false;
+  return heads * units <= int64_t(INT32_MAX);
+}
+
 prism_status check_heads(const char* who, int B, int Hh, int64_t units) {
-  if (int64_t(B) * Hh * units > int64_t(INT32_MAX))
+  if (!heads_fit(B, Hh, units))
     return fail(PRISM_ERR_SHAPE, "%s: B*Hh = %lld heads of %lld units each exceed 2^31 - 1 in all", who,
                 (long long)(int64_t(B) * Hh), (long long)units);
   return PRISM_OK;
@@ -289,12 +296,12 @@ prism_status prism_permute_pool(const void* x, void* y, prism_dtype dtype, int B
 }
 
 size_t prism_select_workspace_size(int B, int Hh, int nb, int d) {
-  if (B < 1 || Hh < 1 || nb < 1 || d < 1) return 0;
+  if (B < 1 || Hh < 1 || nb < 1 || d < 1 || !heads_fit(B, Hh, nb)) return 0;
   return select_ws_bytes(B * Hh, nb, d, true);
 }
 
 size_t prism_select_pooled_workspace_size(int B, int Hh, int nb) {
-  if (B < 1 || Hh < 1 || nb < 1) return 0;
+  if (B < 1 || Hh < 1 || nb < 1 || !heads_fit(B, Hh, nb)) return 0;
   return select_ws_bytes(B * Hh, nb, 1, false);
 }
 
@@ -353,7 +360,7 @@ static prism_status check_attn_common(const char* who, prism_dtype dtype, int B,
   if ((size_t(vol) * d * esize(dtype)) % 16 != 0) return fail(PRISM_ERR_SHAPE, "%s: vol*d*sizeof(dtype) must be a multiple of 16", who);
   if (k_max < 1) return fail(PRISM_ERR_ARG, "%s: k_max must be >= 1", who);
   if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "%s: scale must be finite", who);
-  if (int64_t(B) * Hh * nb * vol > (int64_t(1) << 31)) return fail(PRISM_ERR_SHAPE, "%s: too many rows", who);
+  if (!heads_fit(B, Hh, int64_t(nb) * vol)) return fail(PRISM_ERR_SHAPE, "%s: too many rows", who);
   return PRISM_OK;
 }
 
@@ -375,7 +382,7 @@ static AttnArgs dense_args(int B, int Hh, int N, int d, float scale) {
 }
 
 size_t prism_fwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype) {
-  if (B < 1 || Hh < 1 || nb < 1 || vol < 1 || !valid_dtype(dtype)) return 0;
+  if (B < 1 || Hh < 1 || nb < 1 || vol < 1 || !valid_dtype(dtype) || !heads_fit(B, Hh, int64_t(nb) * vol)) return 0;
   return attn_fwd_ws_bytes(sparse_args(B, Hh, nb, vol, d, 1, 1.f), dtype);
 }
 
@@ -397,7 +404,7 @@ prism_status prism_sparse_attn_fwd(const void* qp, const void* kp, const void* v
 }
 
 size_t prism_bwd_workspace_size(int B, int Hh, int nb, int vol, int d, prism_dtype dtype) {
-  if (B < 1 || Hh < 1 || nb < 1 || vol < 1 || !valid_dtype(dtype)) return 0;
+  if (B < 1 || Hh < 1 || nb < 1 || vol < 1 || !valid_dtype(dtype) || !heads_fit(B, Hh, int64_t(nb) * vol)) return 0;
   return attn_bwd_ws_bytes(sparse_args(B, Hh, nb, vol, d, 1, 1.f), dtype);
 }
 
@@ -482,7 +489,7 @@ prism_status prism_sparse_attn_bwd_noalloc(const void* qp, const void* kp, const
 }
 
 size_t prism_dense_fwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype) {
-  if (B < 1 || Hh < 1 || N < 1 || !valid_dtype(dtype)) return 0;
+  if (B < 1 || Hh < 1 || N < 1 || !valid_dtype(dtype) || !heads_fit(B, Hh, int64_t(N) + kTileRows)) return 0;
   return attn_fwd_ws_bytes(dense_args(B, Hh, N, d, 1.f), dtype);
 }
 
@@ -503,7 +510,7 @@ prism_status prism_dense_attn_fwd(const void* q, const void* k, const void* v, p
 }
 
 size_t prism_dense_bwd_workspace_size(int B, int Hh, int N, int d, prism_dtype dtype) {
-  if (B < 1 || Hh < 1 || N < 1 || !valid_dtype(dtype)) return 0;
+  if (B < 1 || Hh < 1 || N < 1 || !valid_dtype(dtype) || !heads_fit(B, Hh, int64_t(N) + kTileRows)) return 0;
   return attn_bwd_ws_bytes(dense_args(B, Hh, N, d, 1.f), dtype);
 }
 
@@ -533,7 +540,7 @@ prism_status prism_a2v_attn_norm(const void* q, const void* ka, const void* va, 
   if (B < 1 || Hh < 1 || N < 1 || Na < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, N, Na must be >= 1", who);
   if (dtype != PRISM_BF16 || d != 128) return fail(PRISM_ERR_DTYPE, "%s: needs bf16 and d = 128", who);
   if (!std::isfinite(scale)) return fail(PRISM_ERR_ARG, "%s: scale must be finite", who);
-  if (int64_t(B) * Hh * N > (int64_t(1) << 31) || int64_t(B) * Hh * Na > (int64_t(1) << 31))
+  if (!heads_fit(B, Hh, int64_t(N) + kTileRows) || !heads_fit(B, Hh, int64_t(Na) + kTileRows))
     return fail(PRISM_ERR_SHAPE, "%s: too many rows", who);
   AttnArgs a = dense_args(B, Hh, N, d, scale);
   a.nkrows = Na;
@@ -579,7 +586,8 @@ prism_status prism_bench_tile_gather(const void* qp, const void* kp, const void*
 }
 
 size_t prism_tiles_workspace_size(int B, int Hh, int nb, int vol) {
-  if (B < 1 || Hh < 1 || nb < 1 || vol < kTileRows || vol % kTileRows != 0) return 0;
+  if (B < 1 || Hh < 1 || nb < 1 || vol < kTileRows || vol % kTileRows != 0 || !heads_fit(B, Hh, int64_t(nb) * vol))
+    return 0;
   return tiles_ws_bytes(B * Hh, nb, vol);
 }
 
@@ -596,7 +604,7 @@ prism_status prism_blocks_to_tiles(const int32_t* block_valid, const int32_t* se
   if (vol < kTileRows || vol % kTileRows != 0 || vol > 4096)
     return fail(PRISM_ERR_SHAPE, "%s: vol=%d must be a multiple of %d in [%d, 4096]", who, vol, kTileRows, kTileRows);
   const int g = vol / kTileRows;
-  if (int64_t(B) * Hh * nb * g * int64_t(k_max) * g > (int64_t(1) << 31))
+  if (int64_t(B) * Hh * nb * g * int64_t(k_max) * g > int64_t(INT32_MAX))
     return fail(PRISM_ERR_SHAPE, "%s: tile lists exceed 2^31 entries", who);
   if (ws_bytes < tiles_ws_bytes(B * Hh, nb, vol)) return fail(PRISM_ERR_ARG, "%s: workspace too small", who);
   return launched(launch_blocks_to_tiles(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, B * Hh, nb, vol, k_max,
@@ -605,7 +613,7 @@ prism_status prism_blocks_to_tiles(const int32_t* block_valid, const int32_t* se
 }
 
 size_t prism_tiles_mixed_workspace_size(int B, int Hh, int nb) {
-  if (B < 1 || Hh < 1 || nb < 1) return 0;
+  if (B < 1 || Hh < 1 || nb < 1 || !heads_fit(B, Hh, nb)) return 0;
   return tiles_mixed_ws_bytes(B * Hh, nb);
 }
 
@@ -620,7 +628,7 @@ prism_status prism_blocks_to_tiles_mixed(const int32_t* block_valid, const int32
     return fail(PRISM_ERR_ARG, "%s: null pointer", who);
   if (B < 1 || Hh < 1 || nb < 1 || k_max < 1) return fail(PRISM_ERR_ARG, "%s: B, Hh, nb, k_max must be >= 1", who);
   if (max_units < 1 || max_units > 64) return fail(PRISM_ERR_ARG, "%s: max_units must be in [1, 64]", who);
-  if (int64_t(B) * Hh * nb * int64_t(k_max) * max_units > (int64_t(1) << 31))
+  if (int64_t(B) * Hh * nb * int64_t(k_max) * max_units > int64_t(INT32_MAX))
     return fail(PRISM_ERR_SHAPE, "%s: tile lists exceed 2^31 entries", who);
   if (ws_bytes < tiles_mixed_ws_bytes(B * Hh, nb)) return fail(PRISM_ERR_ARG, "%s: workspace too small", who);
   return launched(launch_blocks_to_tiles_mixed(block_valid, sel_idx, sel_cnt, rev_ptr, rev_idx, B * Hh, nb, k_max,

@@ -31,7 +31,7 @@
  *              Statistics, pooled means, scores, LSE and D are always float32.
  *   Sizes      B*Hh heads times the zones, blocks or rows a call handles per head must
  *              stay below 2^31 (the launches' grids and per-launch indices are 32-bit);
- *              larger calls return PRISM_ERR_SHAPE.
+ *              larger calls return PRISM_ERR_SHAPE and the *_workspace_size functions 0.
  */
 #ifndef PRISM_H
 #define PRISM_H

@@ -83,6 +83,33 @@ int main(void) {
          PRISM_ERR_SHAPE);
   expect("tiles_mixed(max_units 65)",
          prism_blocks_to_tiles_mixed(I, I, I, I, I, 1, 1, 16, 8, 65, I, I, I, I, P, (size_t)-1, 0), PRISM_ERR_ARG);
+  /* B*Hh heads times the per-head units past 2^31 - 1: an error (calls) or 0 (sizes), with
+     no int product of B and Hh formed on the way */
+  expect("zone_stats(B*Hh*zones overflow)", prism_zone_stats(P, P, PRISM_BF16, 1 << 16, 1 << 15, 128, &g, F, 0),
+         PRISM_ERR_SHAPE);
+  expect("assign_shapes(B*Hh overflow)", prism_assign_shapes(F, 0x7fffffff, 0x7fffffff, &g, &s, &sp, I, NULL, 0),
+         PRISM_ERR_SHAPE);
+  expect("permute(B*Hh*blocks overflow)",
+         prism_permute(P, (char*)P + 64, PRISM_F32, 1 << 16, 1 << 14, 64, &g, &s, I, 0, NULL, 0), PRISM_ERR_SHAPE);
+  expect("select_pooled(B*Hh*nb overflow)",
+         prism_select_blocks_pooled(F, F, I, 1 << 16, 1 << 8, 1 << 8, 128, 0.1f, &sel, I, I, I, I, NULL, P,
+                                    (size_t)-1, 0), PRISM_ERR_SHAPE);
+  expect("fwd(B*Hh*rows = 2^31)", prism_sparse_attn_fwd(P, P, P, PRISM_BF16, I, I, I, 8, 1 << 15, 1 << 16, 1, 1,
+                                                        128, 0.1f, P, F, P, (size_t)-1, 0), PRISM_ERR_SHAPE);
+  expect("select_ws_size(B*Hh overflow)",
+         (prism_status)(prism_select_workspace_size(0x7fffffff, 0x7fffffff, 16, 128) == 0 ? 1 : 0), 1);
+  expect("select_pooled_ws_size(B*Hh*nb overflow)",
+         (prism_status)(prism_select_pooled_workspace_size(1 << 16, 1 << 16, 16) == 0 ? 1 : 0), 1);
+  expect("bwd_ws_size(nb*vol overflow)",
+         (prism_status)(prism_bwd_workspace_size(1, 1, 1 << 26, 64, 128, PRISM_BF16) == 0 ? 1 : 0), 1);
+  expect("fwd_ws_size(B*Hh overflow)",
+         (prism_status)(prism_fwd_workspace_size(0x7fffffff, 2, 16, 64, 128, PRISM_BF16) == 0 ? 1 : 0), 1);
+  expect("dense_bwd_ws_size(B*Hh*N overflow)",
+         (prism_status)(prism_dense_bwd_workspace_size(1 << 16, 1 << 16, 64, 128, PRISM_BF16) == 0 ? 1 : 0), 1);
+  expect("tiles_ws_size(B*Hh overflow)",
+         (prism_status)(prism_tiles_workspace_size(0x7fffffff, 0x7fffffff, 16, 128) == 0 ? 1 : 0), 1);
+  expect("tiles_mixed_ws_size(B*Hh overflow)",
+         (prism_status)(prism_tiles_mixed_workspace_size(0x7fffffff, 0x7fffffff, 16) == 0 ? 1 : 0), 1);
   expect("bench_mfma(workgroups 0)", prism_bench_mfma_peak(0, 1, (uint64_t*)P, F, 0), PRISM_ERR_ARG);
   expect("bench_stream(bytes not a multiple of 16)", prism_bench_stream_read(P, P, 1000, (uint32_t*)P, 0), PRISM_ERR_ARG);
   expect("bench_stream(null sink)", prism_bench_stream_read(P, P, 1 << 20, NULL, 0), PRISM_ERR_ARG);
