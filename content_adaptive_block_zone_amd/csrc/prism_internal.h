@@ -60,6 +60,27 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
   x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
+// The same for data read exactly once: non-temporal loads, which leave the caches' room
+// to data that is read again
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void load8_once(const bf16_t* p, float (&x)[8]) {
+  const nt_u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = __uint_as_float(u[i] << 16);
+    x[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void load8_once(const float* p, float (&x)[8]) {
+  const nt_f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p));
+  const nt_f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const nt_f32x4*>(p + 4));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[i] = a[i];
+    x[4 + i] = b[i];
+  }
+}
 
 // ----------------------------------------------------------------------------------
 // Caller-provided device lists (valid counts, selection lists, reverse index) are

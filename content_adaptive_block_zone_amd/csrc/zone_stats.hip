@@ -77,7 +77,7 @@ __global__ __launch_bounds__(NT) void k_zone_stats(const T* __restrict__ v, cons
         load8(vr + o, x[j]);
         load8(vr + o + dh, yh[j]);
         load8(vr + o + dt, yt[j]);
-        if constexpr (!FROM_NORM) load8(ar + o, u[j]);
+        if constexpr (!FROM_NORM) load8_once(ar + o, u[j]);  // each A2V row is read once
       }
       if (lw0 == 0) {
 #pragma unroll
