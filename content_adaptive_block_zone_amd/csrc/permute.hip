@@ -78,7 +78,11 @@ __global__ __launch_bounds__(NT) void k_permute(const uint4* __restrict__ x, uin
       const int tok = ((t0 + j / (eh * ew)) * g.H + h0 + (j / ew) % eh) * g.W + w0 + j % ew;
       const size_t trow = (tok_base + tok) * chunks + ch;
       if (inverse) {
-        y[trow] = x[srow];
+        // the token-order result goes back to the caller, not to a later step of the path:
+        // streamed past the caches (non-temporal), so that it leaves no dirty lines there
+        typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
+        const u32x4_nt u = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(x + srow));
+        __builtin_nontemporal_store(u, reinterpret_cast<u32x4_nt*>(y + trow));
       } else {
         const uint4 u = x[trow];
         y[srow] = u;
